@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Throughput of the fused SDPA forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  * prefill: full self-attention, DiT shape B=2, H=38, L=4250, D=64, fp16
+    (the SD3-style workload of the "Metal shaders for memory efficient self
+    attention on large sequences" page);
+  * decode: long-context batched decode, B=8, Hq=32, Hkv=8, D=128,
+    Lk=131072, bf16 K/V, fp32 [B,1,1,Lk] mask whose trailing 10 % is -inf,
+    two-pass split-K.
+Inputs are resident in HBM before the timed region.  Each kernel is timed
+with HIP events recorded on the stream it is launched on (torch's current
+stream, which the binding passes to the library).
+
+Prints ONE JSON line.  ``value`` is the prefill throughput (TFLOP/s, 4*D flops
+per visible (query, key) pair); ``decode`` carries the decode throughput
+(GB/s of K/V/Q/O/mask bytes, each K/V element counted once per (batch, KV
+head)).  ``roofline`` / ``decode.roofline`` compare the dominant kernel of each
+form with MI355X's published peaks.  ``cpu_baseline`` is the fp64 oracle timed
+on a bounded sample of the same workload on the host cores.
+
+Other workloads (for profiling): --workload dit_fp16|dit_fp32|causal_bf16|
+long_decode_bf16|<gqa8 decode name>.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"fp16": 2500.0, "bf16": 2500.0, "fp32": 157.3}   # dense matrix-core peaks
+PEAK_HBM_GBS = 8000.0
+METRIC = "prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM peak), 1×MI355X"
+
+
+def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
+    """(query, key) pairs entering the softmax per (batch, head); bottom-right causal."""
+    if not causal:
+        return Lq * Lk
+    off = Lk - Lq
+    tot = 0
+    for i in range(Lq):
+        tot += max(0, min(Lk, i + off + 1))
+    return tot
+
+
+def prefill_flops(w) -> int:
+    return 4 * w.D * visible_pairs(w.Lq, w.Lk, w.causal) * w.B * w.Hq
+
+
+def decode_bytes(w) -> int:
+    es = 4 if w.dtype == "fp32" else 2
+    kv = 2 * w.B * w.Hkv * w.Lk * w.D * es
+    qo = 2 * w.B * w.Hq * w.D * es
+    mask = 4 * w.B * w.Lk if w.mask else 0
+    return kv + qo + mask
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "scaled_dot_product_prefill_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, fn), "rb") as f:
+            h.update(fn.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel)
+    if not e or e.get("source_hash") != source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline_prefill(w, budget_s: float = 12.0):
+    """fp64 oracle on whole (b, head) slices of the workload until ~budget_s."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from oracle import sdpa_reference
+    from threadpoolctl import threadpool_info
+
+    dt = w.torch_dtype
+    done, flops, t_used = 0, 0, 0.0
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for b, h in pairs:
+        hk = h // (w.Hq // w.Hkv)
+        q = workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, h, w.Lq, w.D, dt)[None, None]
+        k = workloads.slice_normal(w.cfg_id, workloads.TENSOR_K, b, hk, w.Lk, w.D, dt)[None, None]
+        v = workloads.slice_normal(w.cfg_id, workloads.TENSOR_V, b, hk, w.Lk, w.D, dt)[None, None]
+        t0 = time.perf_counter()
+        sdpa_reference(q, k, v, scale=w.scale, causal=w.causal)
+        t_used += time.perf_counter() - t0
+        done += 1
+        flops += 4 * w.D * visible_pairs(w.Lq, w.Lk, w.causal)
+        if t_used >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (batch, head) slices of {w.name}, all {w.Lq} query rows, "
+                      f"fp64 numpy, {t_used:.1f} s"}
+
+
+def cpu_baseline_decode(w, budget_s: float = 8.0):
+    import torch
+
+    import workloads
+    from oracle import sdpa_reference
+    from threadpoolctl import threadpool_info
+
+    dt = w.torch_dtype
+    G = w.Hq // w.Hkv
+    done, nbytes, t_used = 0, 0, 0.0
+    es = 4 if w.dtype == "fp32" else 2
+    units = [(b, hk) for b in range(w.B) for hk in range(w.Hkv)]
+    for b, hk in units:
+        q = torch.stack([workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, hk * G + i, 1, w.D, dt)
+                         for i in range(G)])[None]
+        k = workloads.slice_normal(w.cfg_id, workloads.TENSOR_K, b, hk, w.Lk, w.D, dt)[None, None]
+        v = workloads.slice_normal(w.cfg_id, workloads.TENSOR_V, b, hk, w.Lk, w.D, dt)[None, None]
+        mask = workloads.tail_mask(1, w.Lk) if w.mask else None
+        t0 = time.perf_counter()
+        sdpa_reference(q, k, v, scale=w.scale, mask=mask)
+        t_used += time.perf_counter() - t0
+        done += 1
+        nbytes += 2 * w.Lk * w.D * es + 2 * G * w.D * es + (4 * w.Lk if w.mask else 0)
+        if t_used >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(units)} (batch, KV head) groups of {w.name}, fp64 numpy, {t_used:.1f} s"}
+
+
+class Timed:
+    """Per-call HIP event pairs on the current (launch) stream."""
+
+    def __init__(self, torch, n):
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n)]
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.ev]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="default")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "the multi-GPU sharding of this path is a design note, not a measured run.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import scaled_dot_product_prefill_amd as sdpa
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sdpa.library()
+
+    wl = args.workload
+    pre_w = workloads.DIT_FP16 if wl == "default" else workloads.ALL[wl]
+    run_prefill = wl == "default" or pre_w.Lq > 1
+    dec_w = workloads.LONG_DECODE if wl == "default" else (pre_w if pre_w.Lq == 1 else None)
+    if wl != "default" and pre_w.Lq == 1:
+        run_prefill = False
+
+    print(f"[bench] generating inputs ({wl})", file=sys.stderr, flush=True)
+    P = workloads.make_inputs(pre_w, device=dev) if run_prefill else None
+    Dd = workloads.make_inputs(dec_w, device=dev) if dec_w is not None else None
+    ws = None
+    if Dd is not None:
+        nb = sdpa.decode_workspace_bytes(Dd["q"], Dd["k"], Dd["v"])
+        ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+        dec_out = torch.empty_like(Dd["q"])
+        nsplit = sdpa.decode_num_splits(Dd["q"], Dd["k"], Dd["v"])
+    if P is not None:
+        pre_out = torch.empty_like(P["q"])
+        want_lse = pre_w.lse
+    torch.cuda.synchronize()
+
+    def step(tp=None, td=None, i=0):
+        if P is not None:
+            if tp: tp.ev[i][0].record()
+            sdpa.prefill(P["q"], P["k"], P["v"], scale=pre_w.scale, causal=pre_w.causal,
+                         mask=P["mask"], sinks=P["sinks"], return_lse=want_lse, out=pre_out)
+            if tp: tp.ev[i][1].record()
+        if Dd is not None:
+            if td: td.ev[i][0].record()
+            sdpa.decode(Dd["q"], Dd["k"], Dd["v"], scale=dec_w.scale, mask=Dd["mask"],
+                        sinks=Dd["sinks"], workspace=ws, out=dec_out)
+            if td: td.ev[i][1].record()
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    tp = Timed(torch, args.steps) if P is not None else None
+    td = Timed(torch, args.steps) if Dd is not None else None
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(tp, td, i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "data": "synthetic (seeded N(0,1), see workloads/)"}
+    cfg = {}
+    if P is not None:
+        pm = sorted(tp.ms())
+        avg = sum(pm) / len(pm)
+        fl = prefill_flops(pre_w)
+        tf = fl / (avg * 1e-3) / 1e12
+        peak = PEAK_TFLOPS[pre_w.dtype]
+        res.update(value=round(tf, 2), unit="TFLOP/s", dtype=pre_w.dtype)
+        res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
+                           "frac": round(tf / peak, 4), "traffic": load_traffic("prefill_" + pre_w.name),
+                           "kernel": "prefill_kernel", "avg_ms": round(avg, 5),
+                           "median_ms": round(pm[len(pm) // 2], 5),
+                           "flops_per_launch": fl}
+        cfg["workload"] = pre_w.name
+        cfg.update(prefill={"B": pre_w.B, "Hq": pre_w.Hq, "Hkv": pre_w.Hkv, "Lq": pre_w.Lq,
+                            "Lk": pre_w.Lk, "D": pre_w.D, "dtype": pre_w.dtype,
+                            "causal": pre_w.causal, "lse": pre_w.lse})
+    if Dd is not None:
+        dm = sorted(td.ms())
+        avg = sum(dm) / len(dm)
+        nbytes = decode_bytes(dec_w)
+        gbs = nbytes / (avg * 1e-3) / 1e9
+        dec = {"value": round(gbs, 1), "unit": "GB/s", "dtype": dec_w.dtype, "avg_ms": round(avg, 5),
+               "median_ms": round(dm[len(dm) // 2], 5), "splits": nsplit,
+               "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                            "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": load_traffic("decode_" + dec_w.name),
+                            "kernel": "decode_kernel + merge_kernel", "bytes_per_launch": nbytes}}
+        cfg["workload"] = (cfg.get("workload", "") + " + " if P is not None else "") + dec_w.name
+        cfg["decode"] = {"B": dec_w.B, "Hq": dec_w.Hq, "Hkv": dec_w.Hkv, "Lk": dec_w.Lk, "D": dec_w.D,
+                         "dtype": dec_w.dtype, "mask": dec_w.mask, "sinks": dec_w.sinks}
+        if P is None:
+            res.update(value=dec["value"], unit="GB/s", dtype=dec_w.dtype, roofline=dec["roofline"])
+        res["decode"] = dec
+    res["config"] = cfg
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
+        if P is not None:
+            res["cpu_baseline"] = cpu_baseline_prefill(pre_w)
+            if Dd is not None:
+                res["decode"]["cpu_baseline"] = cpu_baseline_decode(dec_w)
+        else:
+            res["cpu_baseline"] = cpu_baseline_decode(dec_w)
+    res["source_hash"] = source_hash()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

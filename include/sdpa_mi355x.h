@@ -1,0 +1,163 @@
+/*
+ * sdpa_mi355x.h -- C ABI of the MI355X (gfx950) fused scaled-dot-product
+ * attention forward library, libsdpa_mi355x.so.
+ *
+ * The library computes, for every batch b and query head hq,
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * without materialising the Lq x Lk score matrix, in two forms:
+ *
+ *   sdpa_prefill  tiled full / causal self-attention with an online (running
+ *                 max, running sum) softmax -- the forward kernel of the
+ *                 rustytorch "flash_attention.metal" page ("Online softmax
+ *                 update", "Write final output") and the full self-attention
+ *                 kernels of the "Metal shaders for memory efficient self
+ *                 attention on large sequences" page;
+ *   sdpa_decode   single-query "vector" attention (Lq == 1) with a single-pass
+ *                 and a two-pass split-K variant -- the two vector kernels of
+ *                 the "Add D512 support to Metal vector attention" page.
+ *
+ * The optional inputs follow the SDPA graph attributes configured by
+ * build_sdpa_graph on the "mlx 0.30.7 -- backend/cuda/
+ * scaled_dot_product_attention.cpp" page: attention scale, log-sum-exp
+ * statistics output, bottom-right causal mask, additive bias, sink token.
+ *
+ * Semantics (the same for both entry points):
+ *   - query head hq reads KV head hq / (Hq / Hkv)   (Hq % Hkv must be 0);
+ *   - S[i,j] = scale * (q_i . k_j) computed from the dtype inputs with fp32
+ *     products and fp32 accumulation, then + mask[b,hq,i,j] (fp32);
+ *   - causal (bottom-right): key j is visible to query i iff
+ *     j <= i + (Lk - Lq); for Lq == 1 every key is visible;
+ *   - sinks[hq] (fp32, not multiplied by scale) adds exp(sinks[hq]) to the
+ *     softmax denominator and nothing to the numerator;
+ *   - lse[b,hq,i] = natural log of the full softmax denominator (including
+ *     the sink term);
+ *   - a row that sees no key and has no sink gets O = 0 and lse = -inf; a row
+ *     that sees no key but has a sink gets O = 0 and lse = sink.
+ *   - fp32 inputs are computed in full fp32 (no reduced-precision products).
+ *
+ * Memory, ownership, threading:
+ *   - every pointer in sdpa_args is DEVICE memory owned by the caller; the
+ *     library never allocates, frees, retains or synchronises.  Each call
+ *     only enqueues kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns; execution errors surface at the caller's next
+ *     synchronisation.
+ *   - q, k, v, o are 4-D [B, H, L, D] tensors whose last dim (D) is
+ *     contiguous; *_stride[0..2] are ELEMENT strides of the B, H and L dims.
+ *     Base pointers must be 16-byte aligned and every stride * element size
+ *     a multiple of 16 bytes (the input preparation rule of prepare_sdpa_input
+ *     on the mlx 0.30.7 page: unit last-dim stride, aligned pointer).
+ *   - mask (optional, fp32) is indexed mask[b*s0 + hq*s1 + i*s2 + j*s3] with
+ *     mask_stride[0..3] in elements; a stride of 0 broadcasts that dim (a
+ *     [B,1,1,Lk] mask passes strides {Lk, 0, 0, 1}).  4-byte aligned.
+ *   - sinks (optional) is fp32 [Hq], contiguous (the cuDNN path on the mlx
+ *     page converts sinks to float32 in prepare_sdpa_sinks).
+ *   - lse (optional output) is fp32 [B, Hq, Lq], contiguous.
+ *   - o must not overlap q, k, v, mask, sinks or lse.
+ *
+ * Errors: every argument is checked on the host BEFORE anything is enqueued;
+ * on any error nothing is written, the call returns a non-zero sdpa_status and
+ * sdpa_last_error() describes it.  A request no kernel covers returns
+ * SDPA_ERR_UNSUPPORTED -- there is no slower fallback path (the convention of
+ * force_fused on the D512 page: an explicit error instead of a silent
+ * fallback).  All functions are thread-safe; sdpa_last_error() is per thread.
+ */
+#ifndef SDPA_MI355X_H
+#define SDPA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SDPA_MI355X_ABI_VERSION 1
+
+#ifndef SDPA_API
+#define SDPA_API __attribute__((visibility("default")))
+#endif
+
+typedef enum sdpa_dtype {
+  SDPA_F32 = 0,
+  SDPA_F16 = 1,
+  SDPA_BF16 = 2
+} sdpa_dtype;
+
+typedef enum sdpa_status {
+  SDPA_OK = 0,
+  SDPA_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  SDPA_ERR_SHAPE = 2,       /* sizes inconsistent (B, H, L, D < 1, Hq % Hkv, ...)  */
+  SDPA_ERR_UNSUPPORTED = 3, /* valid request that no kernel covers (D, dtype, ...) */
+  SDPA_ERR_ALIGN = 4,       /* pointer / stride alignment or non-unit D stride     */
+  SDPA_ERR_WORKSPACE = 5,   /* decode workspace missing or too small               */
+  SDPA_ERR_ARG = 6,         /* bad scalar (non-finite scale), overlap, bad splits  */
+  SDPA_ERR_HIP = 7          /* the HIP runtime rejected a launch                   */
+} sdpa_status;
+
+typedef struct sdpa_args {
+  int64_t B;        /* batch                                   */
+  int64_t Hq;       /* query heads                             */
+  int64_t Hkv;      /* key/value heads (Hq % Hkv == 0)         */
+  int64_t Lq;       /* queries per head                        */
+  int64_t Lk;       /* keys per head                           */
+  int64_t D;        /* head dim (q, k and v share it)          */
+  int32_t dtype;    /* sdpa_dtype of q, k, v and o             */
+  int32_t causal;   /* 0 or 1, bottom-right aligned            */
+  float scale;      /* multiplies q.k; must be finite          */
+  int32_t reserved; /* must be 0                               */
+  const void *q;    int64_t q_stride[3];   /* [B, Hq,  Lq, D] */
+  const void *k;    int64_t k_stride[3];   /* [B, Hkv, Lk, D] */
+  const void *v;    int64_t v_stride[3];   /* [B, Hkv, Lk, D] */
+  void *o;          int64_t o_stride[3];   /* [B, Hq,  Lq, D] output, dtype */
+  const float *mask; int64_t mask_stride[4]; /* optional [B, Hq, Lq, Lk] fp32 */
+  const float *sinks;                        /* optional [Hq] fp32            */
+  float *lse;                                /* optional [B, Hq, Lq] fp32 out */
+} sdpa_args;
+
+/* Prefill / full self-attention, any Lq >= 1, Lk >= 1.
+ * Supported: D in {64, 128}; dtype F32, F16, BF16.  One kernel launch. */
+SDPA_API int sdpa_prefill(const sdpa_args *args, void *stream);
+
+/* Host-only validation of a prefill request (no GPU work, no HIP calls).
+ * Returns what sdpa_prefill would return before launching. */
+SDPA_API int sdpa_prefill_check(const sdpa_args *args);
+
+/* Single-query decode (Lq == 1; causal has no effect there).
+ * Supported: D in {64, 128, 256, 512}; dtype F32, F16, BF16; Hq / Hkv <= 16.
+ * num_splits = 0 picks the split count automatically; 1 forces the
+ * single-pass kernel; n >= 2 forces the two-pass split-K kernel pair with n
+ * splits of the key range (n <= Lk).  The two-pass form needs a workspace of
+ * sdpa_decode_workspace_bytes() bytes of device memory (16-byte aligned,
+ * caller-owned, contents need not be initialised; it is overwritten). */
+SDPA_API int sdpa_decode(const sdpa_args *args, int num_splits,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of a decode request (no GPU work, no HIP calls). */
+SDPA_API int sdpa_decode_check(const sdpa_args *args, int num_splits,
+                      const void *workspace, size_t workspace_bytes);
+
+/* Number of key-range splits sdpa_decode will use for this request and
+ * num_splits value (0 = automatic); 1 means the single-pass kernel.
+ * Returns 0 when the request is invalid. */
+SDPA_API int sdpa_decode_num_splits(const sdpa_args *args, int num_splits);
+
+/* Workspace bytes sdpa_decode needs for this request and num_splits
+ * (0 when the single-pass kernel is used or the request is invalid). */
+SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_splits);
+
+/* Static description of a status code. */
+SDPA_API const char *sdpa_status_string(int status);
+
+/* Message of the last failing call on this thread ("" if none). */
+SDPA_API const char *sdpa_last_error(void);
+
+/* Library build description (arch, ABI version). */
+SDPA_API const char *sdpa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SDPA_MI355X_H */

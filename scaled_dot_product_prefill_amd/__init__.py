@@ -1,0 +1,233 @@
+"""Python binding of libsdpa_mi355x.so (fused SDPA forward for MI355X / gfx950).
+
+Argument marshalling only: every step of the attention runs in the HIP
+kernels of the library.  PyTorch supplies device memory and the stream.  When
+the library is missing, every entry point raises -- there is no CPU path.
+
+    prefill(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False)
+    decode(q, k, v, scale=None, mask=None, sinks=None, return_lse=False, num_splits=0)
+
+q: [B, Hq, Lq, D], k / v: [B, Hkv, Lk, D] (float32, float16 or bfloat16),
+mask: additive float tensor broadcastable to [B, Hq, Lq, Lk], sinks: [Hq].
+Returns O ([B, Hq, Lq, D], dtype of q) or (O, LSE) with LSE fp32 [B, Hq, Lq].
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_bytes",
+           "SdpaArgs", "library", "library_path", "Status", "SdpaError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_PKG, "lib", "libsdpa_mi355x.so")
+
+F32, F16, BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+
+class Status:
+    OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_WORKSPACE, ERR_ARG, ERR_HIP = range(8)
+
+
+class SdpaError(ValueError):
+    """A request the library rejected (status code in ``.status``)."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"sdpa status {status}: {msg}")
+        self.status = status
+
+
+class SdpaArgs(ctypes.Structure):
+    """Mirror of ``struct sdpa_args`` (include/sdpa_mi355x.h)."""
+    _fields_ = [
+        ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
+        ("Lq", ctypes.c_int64), ("Lk", ctypes.c_int64), ("D", ctypes.c_int64),
+        ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("q", ctypes.c_void_p), ("q_stride", ctypes.c_int64 * 3),
+        ("k", ctypes.c_void_p), ("k_stride", ctypes.c_int64 * 3),
+        ("v", ctypes.c_void_p), ("v_stride", ctypes.c_int64 * 3),
+        ("o", ctypes.c_void_p), ("o_stride", ctypes.c_int64 * 3),
+        ("mask", ctypes.c_void_p), ("mask_stride", ctypes.c_int64 * 4),
+        ("sinks", ctypes.c_void_p),
+        ("lse", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library():
+    """Load the HIP library (raises RuntimeError when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise RuntimeError(
+            f"{library_path} is missing: build it with "
+            "`python -m scaled_dot_product_prefill_amd.build_lib` (there is no CPU fallback)")
+    lib = ctypes.CDLL(library_path)
+    P = ctypes.POINTER(SdpaArgs)
+    lib.sdpa_prefill.argtypes = [P, ctypes.c_void_p]
+    lib.sdpa_prefill.restype = ctypes.c_int
+    lib.sdpa_prefill_check.argtypes = [P]
+    lib.sdpa_prefill_check.restype = ctypes.c_int
+    lib.sdpa_decode.argtypes = [P, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.sdpa_decode.restype = ctypes.c_int
+    lib.sdpa_decode_check.argtypes = [P, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
+    lib.sdpa_decode_check.restype = ctypes.c_int
+    lib.sdpa_decode_num_splits.argtypes = [P, ctypes.c_int]
+    lib.sdpa_decode_num_splits.restype = ctypes.c_int
+    lib.sdpa_decode_workspace_bytes.argtypes = [P, ctypes.c_int]
+    lib.sdpa_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.sdpa_status_string.argtypes = [ctypes.c_int]
+    lib.sdpa_status_string.restype = ctypes.c_char_p
+    lib.sdpa_last_error.argtypes = []
+    lib.sdpa_last_error.restype = ctypes.c_char_p
+    lib.sdpa_version.argtypes = []
+    lib.sdpa_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _raise(status: int):
+    lib = library()
+    msg = lib.sdpa_last_error().decode() or lib.sdpa_status_string(status).decode()
+    if status == Status.ERR_HIP:
+        raise RuntimeError(f"sdpa HIP error: {msg}")
+    raise SdpaError(status, msg)
+
+
+def _prep(x: torch.Tensor, name: str) -> torch.Tensor:
+    """Unit last-dim stride and 16-byte aligned pointer and strides, else a
+    contiguous copy (the rule of prepare_sdpa_input on the mlx 0.30.7 page)."""
+    if x.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, L, D], got {tuple(x.shape)}")
+    es = x.element_size()
+    ok = (x.stride(-1) == 1 and x.data_ptr() % 16 == 0
+          and all((s * es) % 16 == 0 for s in x.stride()[:3]))
+    return x if ok else x.contiguous()
+
+
+def _fill(a: SdpaArgs, name: str, t: Optional[torch.Tensor]):
+    setattr(a, name, t.data_ptr() if t is not None else None)
+    if t is not None:
+        st = getattr(a, name + "_stride")
+        for i in range(3):
+            st[i] = t.stride(i)
+
+
+def _make_args(q, k, v, o, scale, causal, mask, sinks, lse) -> SdpaArgs:
+    B, Hq, Lq, D = q.shape
+    a = SdpaArgs()
+    a.B, a.Hq, a.Lq, a.D = B, Hq, Lq, D
+    a.Hkv, a.Lk = k.shape[1], k.shape[2]
+    a.dtype = _DTYPE_CODE[q.dtype]
+    a.causal = 1 if causal else 0
+    a.scale = float(scale)
+    a.reserved = 0
+    for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _fill(a, n, t)
+    if mask is not None:
+        a.mask = mask.data_ptr()
+        for i in range(4):
+            a.mask_stride[i] = mask.stride(i)
+    a.sinks = sinks.data_ptr() if sinks is not None else None
+    a.lse = lse.data_ptr() if lse is not None else None
+    return a
+
+
+def _common(q, k, v, scale, mask, sinks, Lq_expected=None):
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k and v must share a dtype")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise ValueError("q, k and v must be GPU tensors (there is no CPU path)")
+    q, k, v = _prep(q, "q"), _prep(k, "k"), _prep(v, "v")
+    B, Hq, Lq, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+        raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
+    Lk = k.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if mask is not None:
+        if mask.dtype != torch.float32:
+            mask = mask.to(torch.float32)
+        mask = mask.to(q.device).expand(B, Hq, Lq, Lk)     # broadcast dims get stride 0
+    if sinks is not None:
+        sinks = sinks.to(device=q.device, dtype=torch.float32).reshape(Hq).contiguous()
+    return q, k, v, scale, mask, sinks
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+            causal: bool = False, mask: Optional[torch.Tensor] = None,
+            sinks: Optional[torch.Tensor] = None, return_lse: bool = False,
+            out: Optional[torch.Tensor] = None):
+    """Fused attention forward over a whole query block (prefill / full self-attention)."""
+    lib = library()
+    q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
+    B, Hq, Lq, D = q.shape
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.sdpa_prefill(ctypes.byref(a), ctypes.c_void_p(stream))
+    if st != 0:
+        _raise(st)
+    return (o, lse) if return_lse else o
+
+
+def _decode_args(q, k, v, scale, mask, sinks):
+    q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
+    return q, k, v, scale, mask, sinks
+
+
+def decode_num_splits(q, k, v, *, num_splits: int = 0) -> int:
+    """Splits of the key range sdpa_decode would use (1 = single pass)."""
+    lib = library()
+    return int(lib.sdpa_decode_num_splits(ctypes.byref(_size_args(q, k)), int(num_splits)))
+
+
+def decode_workspace_bytes(q, k, v, *, num_splits: int = 0) -> int:
+    lib = library()
+    return int(lib.sdpa_decode_workspace_bytes(ctypes.byref(_size_args(q, k)), int(num_splits)))
+
+
+def _size_args(q, k) -> SdpaArgs:
+    """Sizes-only argument block for the split / workspace queries."""
+    a = SdpaArgs()
+    a.B, a.Hq, a.Lq, a.D = q.shape
+    a.Hkv, a.Lk = k.shape[1], k.shape[2]
+    a.dtype = _DTYPE_CODE[q.dtype]
+    a.scale = 1.0
+    return a
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+           mask: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None,
+           return_lse: bool = False, num_splits: int = 0,
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+    """Single-query attention (q has Lq == 1).  num_splits: 0 automatic,
+    1 single-pass kernel, n >= 2 two-pass split-K with n key ranges."""
+    lib = library()
+    q, k, v, scale, mask, sinks = _decode_args(q, k, v, scale, mask, sinks)
+    B, Hq, Lq, D = q.shape
+    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    a = _make_args(q, k, v, o, scale, False, mask, sinks, lse)
+    need = int(lib.sdpa_decode_workspace_bytes(ctypes.byref(a), int(num_splits)))
+    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if (workspace is not None and need > 0) else None
+    ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.sdpa_decode(ctypes.byref(a), int(num_splits), ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+    if st != 0:
+        _raise(st)
+    return (o, lse) if return_lse else o

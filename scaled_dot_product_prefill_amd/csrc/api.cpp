@@ -1,0 +1,302 @@
+// Host side of libsdpa_mi355x.so: argument validation, decode split choice,
+// workspace layout and the extern "C" entry points declared in sdpa_mi355x.h.
+//
+// Validation happens entirely before any HIP call, so the *_check entry
+// points (and every error path of the launching entry points) run without a
+// GPU.  Unsupported requests return SDPA_ERR_UNSUPPORTED instead of taking a
+// slower path, the convention of the force_fused check on the "Add D512
+// support to Metal vector attention" page.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "sdpa_internal.hpp"
+#include "sdpa_mi355x.h"
+
+namespace sdpa {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int ok() {
+  g_last_error.clear();
+  return SDPA_OK;
+}
+
+int elem_bytes(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
+
+constexpr int64_t kMaxInt = 2147483647LL;
+
+struct Extent {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi)
+  bool valid = false;
+};
+
+Extent tensor_extent(const void* p, const int64_t* st, int64_t n0, int64_t n1, int64_t n2,
+                     int64_t inner, int es) {
+  Extent e;
+  if (!p) return e;
+  const int64_t last = (n0 - 1) * st[0] + (n1 - 1) * st[1] + (n2 - 1) * st[2] + inner;
+  e.lo = (uintptr_t)p;
+  e.hi = e.lo + (uintptr_t)(last * es);
+  e.valid = true;
+  return e;
+}
+
+bool overlaps(const Extent& a, const Extent& b) {
+  return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi;
+}
+
+// Size and scalar checks (no pointers examined).
+int check_sizes(const sdpa_args* a) {
+  if (!a) return fail(SDPA_ERR_NULL, "args is NULL");
+  if (a->B < 1 || a->Hq < 1 || a->Hkv < 1 || a->Lq < 1 || a->Lk < 1 || a->D < 1)
+    return fail(SDPA_ERR_SHAPE, "B, Hq, Hkv, Lq, Lk, D must all be >= 1 (got %lld %lld %lld %lld %lld %lld)",
+                (long long)a->B, (long long)a->Hq, (long long)a->Hkv, (long long)a->Lq,
+                (long long)a->Lk, (long long)a->D);
+  if (a->Hq % a->Hkv != 0)
+    return fail(SDPA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)a->Hq,
+                (long long)a->Hkv);
+  if (a->Lq > kMaxInt / 2 || a->Lk > kMaxInt / 2 || a->B * a->Hq > kMaxInt / 2)
+    return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the 32-bit index range of the kernels");
+  if (a->dtype != SDPA_F32 && a->dtype != SDPA_F16 && a->dtype != SDPA_BF16)
+    return fail(SDPA_ERR_UNSUPPORTED, "dtype %d is not one of SDPA_F32, SDPA_F16, SDPA_BF16", a->dtype);
+  if (a->causal != 0 && a->causal != 1) return fail(SDPA_ERR_ARG, "causal must be 0 or 1");
+  if (a->reserved != 0) return fail(SDPA_ERR_ARG, "reserved field must be 0");
+  if (!std::isfinite(a->scale)) return fail(SDPA_ERR_ARG, "scale must be finite");
+  return SDPA_OK;
+}
+
+// Checks shared by both launching entry points.
+int check_common(const sdpa_args* a) {
+  int st = check_sizes(a);
+  if (st != SDPA_OK) return st;
+  if (!a->q || !a->k || !a->v || !a->o) return fail(SDPA_ERR_NULL, "q, k, v and o must be non-NULL");
+  const int es = elem_bytes(a->dtype);
+  const void* ptrs[4] = {a->q, a->k, a->v, a->o};
+  const int64_t* strides[4] = {a->q_stride, a->k_stride, a->v_stride, a->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  for (int t = 0; t < 4; ++t) {
+    if ((uintptr_t)ptrs[t] % 16 != 0) return fail(SDPA_ERR_ALIGN, "%s is not 16-byte aligned", names[t]);
+    for (int d = 0; d < 3; ++d) {
+      if (strides[t][d] < 0) return fail(SDPA_ERR_ARG, "%s stride %d is negative", names[t], d);
+      if ((strides[t][d] * es) % 16 != 0)
+        return fail(SDPA_ERR_ALIGN, "%s stride %d (%lld elements) is not a multiple of 16 bytes",
+                    names[t], d, (long long)strides[t][d]);
+    }
+  }
+  if (a->o_stride[2] < a->D) return fail(SDPA_ERR_ARG, "o rows overlap (o_stride[2] < D)");
+  if (a->mask) {
+    if ((uintptr_t)a->mask % 4 != 0) return fail(SDPA_ERR_ALIGN, "mask is not 4-byte aligned");
+    for (int d = 0; d < 4; ++d)
+      if (a->mask_stride[d] < 0) return fail(SDPA_ERR_ARG, "mask stride %d is negative", d);
+  }
+  if (a->sinks && (uintptr_t)a->sinks % 4 != 0) return fail(SDPA_ERR_ALIGN, "sinks is not 4-byte aligned");
+  if (a->lse && (uintptr_t)a->lse % 4 != 0) return fail(SDPA_ERR_ALIGN, "lse is not 4-byte aligned");
+
+  // the output must not overlap any input or the other output
+  const Extent eo = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, a->D, es);
+  const Extent eq = tensor_extent(a->q, a->q_stride, a->B, a->Hq, a->Lq, a->D, es);
+  const Extent ek = tensor_extent(a->k, a->k_stride, a->B, a->Hkv, a->Lk, a->D, es);
+  const Extent ev = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, a->D, es);
+  Extent em;
+  if (a->mask) {
+    const int64_t last = (a->B - 1) * a->mask_stride[0] + (a->Hq - 1) * a->mask_stride[1] +
+                         (a->Lq - 1) * a->mask_stride[2] + (a->Lk - 1) * a->mask_stride[3] + 1;
+    em.lo = (uintptr_t)a->mask;
+    em.hi = em.lo + (uintptr_t)(last * 4);
+    em.valid = true;
+  }
+  Extent es_, el;
+  if (a->sinks) { es_.lo = (uintptr_t)a->sinks; es_.hi = es_.lo + a->Hq * 4; es_.valid = true; }
+  if (a->lse) { el.lo = (uintptr_t)a->lse; el.hi = el.lo + a->B * a->Hq * a->Lq * 4; el.valid = true; }
+  if (overlaps(eo, eq) || overlaps(eo, ek) || overlaps(eo, ev) || overlaps(eo, em) ||
+      overlaps(eo, es_) || overlaps(eo, el))
+    return fail(SDPA_ERR_ARG, "o overlaps an input or lse");
+  if (overlaps(el, eq) || overlaps(el, ek) || overlaps(el, ev) || overlaps(el, em) || overlaps(el, es_))
+    return fail(SDPA_ERR_ARG, "lse overlaps an input");
+  return SDPA_OK;
+}
+
+int check_prefill(const sdpa_args* a) {
+  int st = check_common(a);
+  if (st != SDPA_OK) return st;
+  if (a->D != 64 && a->D != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "prefill supports D in {64, 128}, got %lld", (long long)a->D);
+  const int64_t grid = ((a->Lq + 127) / 128) * a->B * a->Hq;
+  if (grid > kMaxInt) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
+  return SDPA_OK;
+}
+
+struct SplitPlan {
+  int nsplit = 1;
+  int split_len = 0;
+};
+
+// Split of the key range for decode.  Automatic: enough workgroups to give
+// every compute unit several (about 1024 for 256 CUs), each split a whole
+// number of key tiles, never more splits than tiles.
+SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
+  SplitPlan sp;
+  const int64_t Lk = a->Lk;
+  if (num_splits == 1) {
+    sp.nsplit = 1;
+    sp.split_len = (int)Lk;
+    return sp;
+  }
+  int64_t len;
+  if (num_splits >= 2) {
+    len = (Lk + num_splits - 1) / num_splits;
+  } else {
+    const int64_t tk = decode_tile_keys(a->dtype, (int)a->D);
+    const int64_t tiles = (Lk + tk - 1) / tk;
+    const int64_t units = a->B * a->Hkv;
+    int64_t ns = (1024 + units - 1) / units;
+    if (ns > tiles) ns = tiles;
+    if (ns < 1) ns = 1;
+    const int64_t tiles_per = (tiles + ns - 1) / ns;
+    len = tiles_per * tk;
+  }
+  sp.split_len = (int)len;
+  sp.nsplit = (int)((Lk + len - 1) / len);
+  return sp;
+}
+
+size_t workspace_for(const sdpa_args* a, const SplitPlan& sp) {
+  if (sp.nsplit <= 1) return 0;
+  return (size_t)a->B * a->Hq * sp.nsplit * (a->D + 2) * sizeof(float);
+}
+
+int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_bytes, SplitPlan* out) {
+  int st = check_common(a);
+  if (st != SDPA_OK) return st;
+  if (a->Lq != 1)
+    return fail(SDPA_ERR_UNSUPPORTED, "decode needs Lq == 1, got %lld", (long long)a->Lq);
+  if (a->D != 64 && a->D != 128 && a->D != 256 && a->D != 512)
+    return fail(SDPA_ERR_UNSUPPORTED, "decode supports D in {64, 128, 256, 512}, got %lld", (long long)a->D);
+  if (a->Hq / a->Hkv > 16)
+    return fail(SDPA_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16, got %lld", (long long)(a->Hq / a->Hkv));
+  if (num_splits < 0 || num_splits > a->Lk)
+    return fail(SDPA_ERR_ARG, "num_splits must be in [0, Lk], got %d", num_splits);
+  SplitPlan sp = plan_splits(a, num_splits);
+  if ((int64_t)sp.nsplit * a->Hkv * a->B > kMaxInt) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
+  const size_t need = workspace_for(a, sp);
+  if (need > 0) {
+    if (!ws) return fail(SDPA_ERR_WORKSPACE, "two-pass decode needs a workspace of %zu bytes", need);
+    if ((uintptr_t)ws % 16 != 0) return fail(SDPA_ERR_ALIGN, "workspace is not 16-byte aligned");
+    if (ws_bytes < need)
+      return fail(SDPA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  }
+  if (out) *out = sp;
+  return SDPA_OK;
+}
+
+int launch_status(hipError_t e) {
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+AttnParams make_params(const sdpa_args& a) {
+  AttnParams p{};
+  p.q = a.q; p.k = a.k; p.v = a.v; p.o = a.o;
+  for (int d = 0; d < 3; ++d) {
+    p.qs[d] = a.q_stride[d]; p.ks[d] = a.k_stride[d];
+    p.vs[d] = a.v_stride[d]; p.os[d] = a.o_stride[d];
+  }
+  p.mask = a.mask;
+  for (int d = 0; d < 4; ++d) p.ms[d] = a.mask_stride[d];
+  p.sinks = a.sinks;
+  p.lse = a.lse;
+  p.B = (int)a.B; p.Hq = (int)a.Hq; p.Hkv = (int)a.Hkv;
+  p.Lq = (int)a.Lq; p.Lk = (int)a.Lk; p.D = (int)a.D;
+  p.group = (int)(a.Hq / a.Hkv);
+  p.causal_off = (int)(a.Lk - a.Lq);
+  p.scale_log2 = a.scale * 1.4426950408889634f;
+  p.nsplit = 1;
+  p.split_len = (int)a.Lk;
+  return p;
+}
+
+}  // namespace sdpa
+
+extern "C" {
+
+int sdpa_prefill_check(const sdpa_args* args) {
+  int st = sdpa::check_prefill(args);
+  return st == SDPA_OK ? sdpa::ok() : st;
+}
+
+int sdpa_prefill(const sdpa_args* args, void* stream) {
+  int st = sdpa::check_prefill(args);
+  if (st != SDPA_OK) return st;
+  sdpa::AttnParams p = sdpa::make_params(*args);
+  return sdpa::launch_status(sdpa::launch_prefill(p, args->dtype, args->causal != 0, (hipStream_t)stream));
+}
+
+int sdpa_decode_check(const sdpa_args* args, int num_splits, const void* workspace, size_t workspace_bytes) {
+  int st = sdpa::check_decode(args, num_splits, workspace, workspace_bytes, nullptr);
+  return st == SDPA_OK ? sdpa::ok() : st;
+}
+
+int sdpa_decode_num_splits(const sdpa_args* args, int num_splits) {
+  if (sdpa::check_sizes(args) != SDPA_OK) return 0;
+  if (num_splits < 0 || num_splits > args->Lk) return 0;
+  return sdpa::plan_splits(args, num_splits).nsplit;
+}
+
+size_t sdpa_decode_workspace_bytes(const sdpa_args* args, int num_splits) {
+  if (sdpa::check_sizes(args) != SDPA_OK) return 0;
+  if (num_splits < 0 || num_splits > args->Lk) return 0;
+  return sdpa::workspace_for(args, sdpa::plan_splits(args, num_splits));
+}
+
+int sdpa_decode(const sdpa_args* args, int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  sdpa::SplitPlan sp;
+  int st = sdpa::check_decode(args, num_splits, workspace, workspace_bytes, &sp);
+  if (st != SDPA_OK) return st;
+  sdpa::AttnParams p = sdpa::make_params(*args);
+  p.nsplit = sp.nsplit;
+  p.split_len = sp.split_len;
+  if (sp.nsplit > 1) {
+    float* ws = (float*)workspace;
+    p.part_o = ws;
+    p.part_ml = ws + (size_t)args->B * args->Hq * sp.nsplit * args->D;
+  }
+  return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
+}
+
+const char* sdpa_status_string(int status) {
+  switch (status) {
+    case SDPA_OK: return "ok";
+    case SDPA_ERR_NULL: return "required pointer is NULL";
+    case SDPA_ERR_SHAPE: return "inconsistent sizes";
+    case SDPA_ERR_UNSUPPORTED: return "unsupported request (no kernel covers it)";
+    case SDPA_ERR_ALIGN: return "pointer or stride alignment";
+    case SDPA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SDPA_ERR_ARG: return "invalid argument";
+    case SDPA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* sdpa_last_error(void) { return sdpa::g_last_error.c_str(); }
+
+const char* sdpa_version(void) { return "sdpa_mi355x abi 1, gfx950 (CDNA4)"; }
+
+}  // extern "C"

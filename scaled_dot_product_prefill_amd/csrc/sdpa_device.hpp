@@ -1,0 +1,141 @@
+// Device-side building blocks shared by the prefill and decode kernels
+// (gfx950 / CDNA4 only).
+//
+// Matrix-core operand layouts used throughout (wave64, lane l, register r):
+//   v_mfma_f32_32x32x16_{bf16,f16}: A[m][k] m = l%32, k = 8*(l/32)+e (e = 0..7)
+//                                   B[k][n] n = l%32, k = 8*(l/32)+e
+//                                   C[m][n] n = l%32, m = 8*(r/4)+4*(l/32)+r%4 (r = 0..15)
+//   v_mfma_f32_32x32x2_f32:        A m = l%32, k = l/32;  B n = l%32, k = l/32;  C as above
+//   v_mfma_f32_16x16x32_{bf16,f16}: A m = l%16, k = 8*(l/16)+e;  B n = l%16, k = 8*(l/16)+e
+//                                   C n = l%16, m = 4*(l/16)+r (r = 0..3)
+//   v_mfma_f32_16x16x4_f32:        A m = l%16, k = l/16;  B n = l%16, k = l/16;  C as above
+// A reduction index k may be assigned to any element of the contraction as
+// long as A and B agree; the kernels use that freedom to read operands as
+// 16-byte vectors.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sdpa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// element types: storage is raw bits; arithmetic is always fp32
+// ---------------------------------------------------------------------------
+struct TF32 {
+  using storage = float;
+  static constexpr int kBytes = 4;
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static inline float to_f32(storage x) { return x; }
+  __device__ static inline storage from_f32(float x) { return x; }
+};
+struct TF16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+  static constexpr int kVec = 8;
+  __device__ static inline float to_f32(storage x) {
+    return (float)__builtin_bit_cast(_Float16, x);
+  }
+  __device__ static inline storage from_f32(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);  // round to nearest even
+  }
+  // pack two fp32 into one dword (lo in bits 0..15)
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    return (uint32_t)from_f32(lo) | ((uint32_t)from_f32(hi) << 16);
+  }
+};
+struct TBF16 {
+  using storage = uint16_t;
+  static constexpr int kBytes = 2;
+  static constexpr int kVec = 8;
+  __device__ static inline float to_f32(storage x) {
+    return __builtin_bit_cast(float, (uint32_t)x << 16);
+  }
+  __device__ static inline storage from_f32(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+  }
+  __device__ static inline uint32_t pack2(float lo, float hi) {
+    return (uint32_t)from_f32(lo) | ((uint32_t)from_f32(hi) << 16);
+  }
+};
+
+// Scalar reinterpretation.  Arguments are taken by value: a bit-cast applied
+// directly to an element of an ext_vector_type expression does not select the
+// element on this compiler, so vector elements are always copied out first.
+__device__ inline float as_float(uint32_t x) { return __uint_as_float(x); }
+__device__ inline uint32_t as_uint(float x) { return __float_as_uint(x); }
+
+// ---------------------------------------------------------------------------
+// matrix-core wrappers (operands as raw dwords)
+// ---------------------------------------------------------------------------
+__device__ inline f32x16 mma32(TBF16, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x16 mma32(TF16, u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+// fp32: one 16-byte vector holds the operands of four consecutive k-steps
+__device__ inline f32x16 mma32(TF32, u32x4 a, u32x4 b, f32x16 c) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    c = __builtin_amdgcn_mfma_f32_32x32x2f32(as_float(a[t]), as_float(b[t]), c, 0, 0, 0);
+  return c;
+}
+
+__device__ inline f32x4 mma16(TBF16, u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x4 mma16(TF16, u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ inline f32x4 mma16(TF32, u32x4 a, u32x4 b, f32x4 c) {
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(as_float(a[t]), as_float(b[t]), c, 0, 0, 0);
+  return c;
+}
+
+// ---------------------------------------------------------------------------
+// memory helpers
+// ---------------------------------------------------------------------------
+__device__ inline u32x4 ldg16(const void* p) {
+  return __builtin_nontemporal_load((const u32x4*)p);
+}
+__device__ inline u32x4 ldg16_cached(const void* p) { return *(const u32x4*)p; }
+__device__ inline u32x4 lds_read16(const void* p) { return *(const u32x4*)p; }
+__device__ inline void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
+__device__ inline void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
+
+// byte-select of two dwords: result bytes = sel over {b (bytes 0..3), a (bytes 4..7)}
+__device__ inline uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) {
+  return __builtin_amdgcn_perm(a, b, sel);
+}
+// low / high 16-bit halves of (b, a) joined: lo(b) | lo(a) << 16, hi(b) | hi(a) << 16
+__device__ inline uint32_t join_lo(uint32_t a, uint32_t b) { return perm(a, b, 0x05040100u); }
+__device__ inline uint32_t join_hi(uint32_t a, uint32_t b) { return perm(a, b, 0x07060302u); }
+
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// exchange with lane l ^ 32 (the other half of the wave)
+__device__ inline float xor32(float v) { return __shfl_xor(v, 32, 64); }
+__device__ inline float xor16(float v) { return __shfl_xor(v, 16, 64); }
+
+}  // namespace sdpa

@@ -1,0 +1,42 @@
+// Host <-> kernel interface of the library (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sdpa_mi355x.h"
+
+namespace sdpa {
+
+// Kernel parameters, passed by value.  Strides are in elements.
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t qs[3], ks[3], vs[3], os[3];
+  const float* mask;
+  int64_t ms[4];
+  const float* sinks;
+  float* lse;
+  int B, Hq, Hkv, Lq, Lk, D;
+  int group;         // Hq / Hkv
+  int causal_off;    // Lk - Lq (bottom-right alignment)
+  float scale_log2;  // scale * log2(e)
+  // decode only
+  int nsplit;        // number of key-range splits (1 = single pass)
+  int split_len;     // keys per split
+  float* part_o;     // [B*Hq, nsplit, D]  fp32 partial numerators
+  float* part_ml;    // [B*Hq, nsplit, 2]  fp32 (running max in log2 units, sum)
+};
+
+AttnParams make_params(const sdpa_args& a);
+
+// Kernel launchers: return hipSuccess or the launch error.
+hipError_t launch_prefill(const AttnParams& p, int dtype, bool causal, hipStream_t s);
+hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s);
+
+// Decode tiling shared by the host heuristics and the kernels.
+int decode_tile_keys(int dtype, int D);
+
+}  // namespace sdpa

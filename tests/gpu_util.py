@@ -1,0 +1,49 @@
+"""Helpers for the GPU parity tests: move seeded inputs to the device, call the
+HIP library through its binding, compare with the fp64 oracle."""
+import sys
+
+import numpy as np
+import torch
+
+from oracle import allclose_report, sdpa_reference
+
+# elementwise |gpu - ref| <= atol + rtol * |ref|
+TOL = {"fp32": (1e-5, 0.0), "fp16": (2e-3, 1e-2), "bf16": (2e-3, 1e-2)}
+DT_NAME = {torch.float32: "fp32", torch.float16: "fp16", torch.bfloat16: "bf16"}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def to_dev(x):
+    return {k: (v.cuda() if v is not None else None) for k, v in x.items()}
+
+
+def check(got, ref, dtype_name, what, lse=False):
+    atol, rtol = TOL[dtype_name]
+    rep = allclose_report(got, ref, atol, rtol)
+    say(f"  {what}{' lse' if lse else ''}: max_abs={rep['max_abs']:.3e} "
+        f"norm_rel={rep['norm_rel']:.3e} ok={rep['ok']}")
+    assert rep["ok"], f"{what}: {rep}"
+    return rep
+
+
+def compare_full(out, lse, x, scale, dtype_name, what, causal=False):
+    O, L = sdpa_reference(x["q"], x["k"], x["v"], scale=scale, causal=causal,
+                          mask=x["mask"], sinks=x["sinks"])
+    check(out.float().cpu(), O, dtype_name, what)
+    if lse is not None:
+        check(lse.cpu(), L, dtype_name, what, lse=True)
+
+
+def compare_sampled(out, lse, x_cpu, scale, dtype_name, what, heads, rows, causal=False):
+    """Compare selected (b, hq) pairs and query rows against the oracle."""
+    O, L = sdpa_reference(x_cpu["q"], x_cpu["k"], x_cpu["v"], scale=scale, causal=causal,
+                          mask=x_cpu["mask"], sinks=x_cpu["sinks"], rows=rows, heads=heads)
+    got = np.stack([out[b, h, rows].float().cpu().numpy() for b, h in heads])
+    check(got, O, dtype_name, what)
+    if lse is not None:
+        gl = np.stack([lse[b, h, rows].cpu().numpy() for b, h in heads])
+        check(gl, L, dtype_name, what, lse=True)

@@ -1,0 +1,188 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+declared in include/*.h, the ctypes mirror of sdpa_args has the C layout, and
+every validation error is reachable through the host-only *_check entry
+points (no kernel is ever launched here)."""
+import ctypes
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+import scaled_dot_product_prefill_amd as sdpa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER_DIR = os.path.join(ROOT, "include")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sdpa.library_path):
+        from scaled_dot_product_prefill_amd import build_lib
+        build_lib.build()
+    return sdpa.library()
+
+
+def _declared_functions():
+    names = []
+    for fn in os.listdir(HEADER_DIR):
+        if fn.endswith(".h"):
+            text = open(os.path.join(HEADER_DIR, fn)).read()
+            names += re.findall(r"SDPA_API\s+[\w\s\*]+?\b(sdpa_\w+)\s*\(", text)
+    return names
+
+
+def test_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert len(names) >= 9, names
+    out = subprocess.run(["nm", "-D", "--defined-only", sdpa.library_path],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(\w+)$", out, re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    assert b"gfx950" in lib.sdpa_version()
+
+
+def test_struct_layout_matches_c():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "sdpa_mi355x.h"
+#define F(f) printf("%s %zu\n", #f, offsetof(sdpa_args, f));
+int main(void) {
+  printf("sizeof %zu\n", sizeof(sdpa_args));
+  F(B) F(Hq) F(Hkv) F(Lq) F(Lk) F(D) F(dtype) F(causal) F(scale) F(reserved)
+  F(q) F(q_stride) F(k) F(k_stride) F(v) F(v_stride) F(o) F(o_stride)
+  F(mask) F(mask_stride) F(sinks) F(lse)
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "layout.c")
+        exe = os.path.join(td, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", HEADER_DIR, c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(l.split() for l in out.strip().splitlines())
+    assert int(got.pop("sizeof")) == ctypes.sizeof(sdpa.SdpaArgs)
+    for name, off in got.items():
+        assert getattr(sdpa.SdpaArgs, name).offset == int(off), name
+
+
+def _args(**kw):
+    a = sdpa.SdpaArgs()
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.D = 2, 8, 2, 64, 64, 128
+    a.dtype, a.causal, a.scale, a.reserved = sdpa.BF16, 0, 0.125, 0
+    # fake, aligned, non-overlapping host addresses: validation never dereferences them
+    base = 1 << 40
+    for i, n in enumerate(("q", "k", "v", "o")):
+        setattr(a, n, base + i * (1 << 32))
+    for n, L, H in (("q", 64, 8), ("k", 64, 2), ("v", 64, 2), ("o", 64, 8)):
+        st = getattr(a, n + "_stride")
+        st[0], st[1], st[2] = H * L * 128, L * 128, 128
+    for k, v in kw.items():
+        if isinstance(v, tuple):
+            arr = getattr(a, k)
+            for i, x in enumerate(v):
+                arr[i] = x
+        else:
+            setattr(a, k, v)
+    return a
+
+
+def _prefill(lib, **kw):
+    return lib.sdpa_prefill_check(ctypes.byref(_args(**kw)))
+
+
+def _decode(lib, num_splits=0, ws=1 << 44, ws_bytes=1 << 30, **kw):
+    kw.setdefault("Lq", 1)
+    a = _args(**kw)
+    for n in ("q_stride", "o_stride"):
+        st = getattr(a, n)
+        st[0], st[1], st[2] = 8 * 128, 128, 128
+    return lib.sdpa_decode_check(ctypes.byref(a), num_splits, ws, ws_bytes)
+
+
+S = sdpa.Status
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib) == S.OK
+    assert lib.sdpa_prefill_check(None) == S.ERR_NULL
+    assert _prefill(lib, q=None) == S.ERR_NULL
+    assert _prefill(lib, Lq=0) == S.ERR_SHAPE
+    assert _prefill(lib, Hq=7) == S.ERR_SHAPE                 # not a multiple of Hkv
+    assert _prefill(lib, D=96) == S.ERR_UNSUPPORTED
+    assert _prefill(lib, dtype=7) == S.ERR_UNSUPPORTED
+    assert _prefill(lib, q=(1 << 40) + 8) == S.ERR_ALIGN
+    assert _prefill(lib, k_stride=(2 * 64 * 128, 64 * 128, 100)) == S.ERR_ALIGN
+    assert _prefill(lib, scale=float("nan")) == S.ERR_ARG
+    assert _prefill(lib, scale=float("inf")) == S.ERR_ARG
+    assert _prefill(lib, causal=2) == S.ERR_ARG
+    assert _prefill(lib, reserved=1) == S.ERR_ARG
+    assert _prefill(lib, o=(1 << 40) + 4096) == S.ERR_ARG     # o overlaps q
+    assert _prefill(lib, mask=(1 << 45) + 2) == S.ERR_ALIGN
+    assert _prefill(lib, mask=1 << 45, mask_stride=(0, 0, -1, 1)) == S.ERR_ARG
+    assert _prefill(lib, lse=(1 << 40) + 16) == S.ERR_ARG     # lse overlaps q
+    assert _prefill(lib, D=64, causal=1, Lq=100, Lk=7) == S.OK
+    msg = lib.sdpa_last_error()
+    assert msg == b""
+    _prefill(lib, D=96)
+    assert b"D in {64, 128}" in lib.sdpa_last_error()
+
+
+def test_decode_validation(lib):
+    assert _decode(lib) == S.OK
+    assert _decode(lib, Lq=2) == S.ERR_UNSUPPORTED
+    assert _decode(lib, D=96) == S.ERR_UNSUPPORTED
+    assert _decode(lib, Hq=34) == S.ERR_UNSUPPORTED           # group of 17
+    assert _decode(lib, num_splits=-1) == S.ERR_ARG
+    assert _decode(lib, num_splits=65) == S.ERR_ARG           # more splits than keys
+    assert _decode(lib, num_splits=4, ws=None) == S.ERR_WORKSPACE
+    assert _decode(lib, num_splits=4, ws_bytes=16) == S.ERR_WORKSPACE
+    assert _decode(lib, num_splits=4, ws=(1 << 44) + 4) == S.ERR_ALIGN
+    assert _decode(lib, num_splits=1, ws=None, ws_bytes=0) == S.OK   # single pass needs none
+    for st in range(8):
+        assert lib.sdpa_status_string(st)
+
+
+def _sizes(B, Hq, Hkv, Lk, D, dtype):
+    a = sdpa.SdpaArgs()
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.D, a.dtype, a.scale = B, Hq, Hkv, 1, Lk, D, dtype, 1.0
+    return a
+
+
+def test_split_plan(lib):
+    # long-context batch: B*Hkv = 64 units -> 16 splits of 8192 keys
+    a = _sizes(8, 32, 8, 131072, 128, sdpa.BF16)
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 16
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 0) == 8 * 32 * 16 * 130 * 4
+    # GQA-8 D=512, B=1, Lk=1024: one 32-key tile per split
+    a = _sizes(1, 32, 4, 1024, 512, sdpa.F16)
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 32
+    # forced counts and single pass
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 1) == 1
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 1) == 0
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 7) == 7
+    a = _sizes(1, 8, 1, 10, 128, sdpa.F32)
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 6) == 5   # ceil(10/6)=2 keys -> 5 splits
+    # every split count covers the key range exactly once
+    for Lk in (1, 31, 32, 33, 1000, 131072):
+        for ns in (0, 2, 3, 17):
+            if ns > Lk:
+                continue
+            a = _sizes(1, 4, 1, Lk, 128, sdpa.BF16)
+            n = lib.sdpa_decode_num_splits(ctypes.byref(a), ns)
+            assert n >= 1
+            if ns >= 2:
+                ln = -(-Lk // ns)
+                assert n == -(-Lk // ln) and (n - 1) * ln < Lk <= n * ln
+
+
+def test_python_binding_has_no_cpu_path():
+    import torch
+    x = torch.zeros(1, 1, 4, 64)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        sdpa.prefill(x, x, x)

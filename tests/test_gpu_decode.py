@@ -1,0 +1,121 @@
+"""GPU parity of the decode kernels (sdpa_decode through the C ABI: single-pass,
+and two-pass split-K + merge) against the fp64 oracle: the whole GQA-8 D=512
+grid (Lk 1k/8k/32k, B 1/2, fp16/bf16/fp32, with and without sinks), the
+long-context masked batch at full size, and edge cases (fully masked splits,
+all keys masked, KV-cache slices, every head dim and group size)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_prefill_amd as sdpa
+import workloads
+from tests.gpu_util import check, compare_full, say, to_dev
+from workloads import random_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _decode(d, scale, num_splits):
+    out, l = sdpa.decode(d["q"], d["k"], d["v"], scale=scale, mask=d["mask"], sinks=d["sinks"],
+                         return_lse=True, num_splits=num_splits)
+    torch.cuda.synchronize()
+    return out, l
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("w", workloads.GQA_DECODE, ids=lambda w: w.name)
+def test_gqa8_d512_grid(w):
+    say("decode", w)
+    x = workloads.make_inputs(w)
+    d = to_dev(x)
+    ns = sdpa.decode_num_splits(d["q"], d["k"], d["v"])
+    for num_splits in (0, 1):
+        out, l = _decode(d, w.scale, num_splits)
+        compare_full(out, l, x, w.scale, w.dtype, f"{w.name} splits={num_splits}->"
+                     f"{ns if num_splits == 0 else 1}")
+
+
+@pytest.mark.timeout(900)
+def test_long_context_masked_full_size():
+    w = workloads.LONG_DECODE
+    say("decode full size", w)
+    x = workloads.make_inputs(w)
+    d = to_dev(x)
+    ns = sdpa.decode_num_splits(d["q"], d["k"], d["v"])
+    say(f"  auto splits: {ns}")
+    out, l = _decode(d, w.scale, 0)
+    compare_full(out, l, x, w.scale, w.dtype, f"{w.name} auto")
+    # 64 splits of 2048 keys: the last 6 splits see only -inf keys
+    out2, l2 = _decode(d, w.scale, 64)
+    compare_full(out2, l2, x, w.scale, w.dtype, f"{w.name} 64 splits")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
+@pytest.mark.parametrize("G", [1, 4, 16])
+def test_head_dims_and_groups(dtype, D, G):
+    Hkv = 2
+    x = random_case(3000 + D + G, 2, Hkv * G, Hkv, 1, 777, D, dtype, sinks=(G == 4))
+    d = to_dev(x)
+    sc = 1 / math.sqrt(D)
+    for ns in (0, 1, 5):
+        out, l = _decode(d, sc, ns)
+        compare_full(out, l, x, sc, dtype, f"D{D} G{G} splits={ns}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_fully_masked_splits_and_rows(dtype):
+    B, Hq, Hkv, Lk, D = 2, 8, 2, 1000, 128
+    x = random_case(3100, B, Hq, Hkv, 1, Lk, D, dtype, mask=True, mask_shape=(B, 1, 1, Lk))
+    x["mask"][..., 600:] = -math.inf                  # trailing splits fully masked
+    x["mask"][1] = -math.inf                          # batch 1 sees no key at all
+    d = to_dev(x)
+    sc = 1 / math.sqrt(D)
+    for ns in (1, 4, 10, 0):
+        out, l = _decode(d, sc, ns)
+        assert torch.all(out[1] == 0) and torch.all(torch.isneginf(l[1]))
+        compare_full(out, l, x, sc, dtype, f"masked splits={ns}")
+    # with sinks the empty batch gets O = 0 and LSE = sink
+    x["sinks"] = torch.linspace(-2, 2, Hq)
+    d = to_dev(x)
+    for ns in (1, 7):
+        out, l = _decode(d, sc, ns)
+        compare_full(out, l, x, sc, dtype, f"masked+sinks splits={ns}")
+
+
+def test_kv_cache_slice():
+    # K / V are the first Lk rows of a larger cache (row stride Lk_max * D per head)
+    B, Hq, Hkv, Lmax, Lk, D = 2, 16, 2, 4096, 3000, 128
+    x = random_case(3200, B, Hq, Hkv, 1, Lmax, D, "bf16")
+    d = to_dev(x)
+    k, v = d["k"][:, :, :Lk], d["v"][:, :, :Lk]
+    assert not k.is_contiguous()
+    out, l = sdpa.decode(d["q"], k, v, return_lse=True)
+    torch.cuda.synchronize()
+    xs = dict(x, k=x["k"][:, :, :Lk], v=x["v"][:, :, :Lk])
+    compare_full(out, l, xs, 1 / math.sqrt(D), "bf16", "kv-cache slice")
+
+
+def test_single_pass_matches_two_pass_and_prefill():
+    x = to_dev(random_case(3300, 1, 32, 4, 1, 4096, 128, "fp16", sinks=True))
+    a = sdpa.decode(x["q"], x["k"], x["v"], sinks=x["sinks"], num_splits=1)
+    b = sdpa.decode(x["q"], x["k"], x["v"], sinks=x["sinks"], num_splits=16)
+    c = sdpa.prefill(x["q"], x["k"], x["v"], sinks=x["sinks"])
+    torch.cuda.synchronize()
+    for name, y in (("two-pass", b), ("prefill", c)):
+        err = (a.float() - y.float()).abs().max().item()
+        say(f"  single-pass vs {name}: {err:.3e}")
+        assert err <= 2e-3
+
+
+def test_decode_errors():
+    x = to_dev(random_case(3400, 1, 4, 2, 2, 64, 128, "fp16"))
+    with pytest.raises(sdpa.SdpaError) as e:
+        sdpa.decode(x["q"], x["k"], x["v"])                # Lq = 2
+    assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
+    x = to_dev(random_case(3401, 1, 34, 2, 1, 64, 128, "fp16"))
+    with pytest.raises(sdpa.SdpaError) as e:
+        sdpa.decode(x["q"], x["k"], x["v"])                # group of 17 > 16
+    assert e.value.status == sdpa.Status.ERR_UNSUPPORTED

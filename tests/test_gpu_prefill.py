@@ -1,0 +1,170 @@
+"""GPU parity of the prefill kernel (sdpa_prefill through the C ABI) against the
+fp64 oracle: the tiny, DiT and causal workloads at full size (sampled rows),
+a grid of small cases spanning several tiles with ragged tails, and the
+edge cases of the method (empty rows, fully masked rows, sinks, GQA,
+non-contiguous layouts, one key)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_prefill_amd as sdpa
+import workloads
+from tests.gpu_util import check, compare_full, compare_sampled, say, to_dev
+from workloads import random_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, dtype_name, causal=False, scale=None, lse=True):
+    d = to_dev(x)
+    D = x["q"].shape[-1]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    out, l = sdpa.prefill(d["q"], d["k"], d["v"], scale=scale, causal=causal, mask=d["mask"],
+                          sinks=d["sinks"], return_lse=True)
+    torch.cuda.synchronize()
+    return out, (l if lse else None), scale
+
+
+def test_tiny_fp32_full():
+    w = workloads.TINY
+    say("tiny fp32", w)
+    x = workloads.make_inputs(w)
+    out, l, sc = _run(x, w.dtype)
+    compare_full(out, l, x, sc, w.dtype, w.name)
+
+
+# (B, Hq, Hkv, Lq, Lk, causal, mask, sinks)
+GRID = [
+    (1, 2, 2, 200, 333, False, False, False),   # ragged non-causal
+    (2, 4, 2, 300, 300, True, False, False),    # causal Lq == Lk, GQA
+    (1, 2, 1, 100, 357, True, False, True),     # bottom-right causal Lq < Lk, sinks
+    (1, 2, 2, 260, 130, True, False, False),    # Lq > Lk: leading rows see nothing
+    (1, 3, 1, 129, 257, False, True, True),     # mask with -inf entries and sinks
+    (2, 2, 2, 64, 64, True, True, False),       # causal + mask together
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", range(len(GRID)))
+def test_prefill_grid(dtype, D, case):
+    B, Hq, Hkv, Lq, Lk, causal, mask, sinks = GRID[case]
+    say(f"prefill grid {dtype} D={D} case={GRID[case]}")
+    x = random_case(1000 + 10 * case + D, B, Hq, Hkv, Lq, Lk, D, dtype, mask=mask, sinks=sinks,
+                    sink_scale=2.0, mask_neg_inf_frac=0.1)
+    out, l, sc = _run(x, dtype, causal=causal)
+    compare_full(out, l, x, sc, dtype, f"grid{case}-{dtype}-D{D}", causal=causal)
+
+
+def _full_size(w, heads, rows):
+    say("full size", w)
+    x = workloads.make_inputs(w)
+    out, l, sc = _run(x, w.dtype, causal=w.causal)
+    compare_sampled(out, l, x, sc, w.dtype, w.name, heads, rows, causal=w.causal)
+
+
+@pytest.mark.timeout(600)
+def test_dit_fp16_full_size_sampled():
+    w = workloads.DIT_FP16
+    rows = [0, 1, 127, 128, 2000, 4095, 4096, 4224, 4249]
+    _full_size(w, [(0, 0), (0, 37), (1, 19), (1, 37)], rows)
+
+
+@pytest.mark.timeout(600)
+def test_dit_fp32_full_size_sampled():
+    w = workloads.DIT_FP32
+    rows = [0, 5, 1000, 4127, 4128, 4249]
+    _full_size(w, [(0, 1), (1, 36)], rows)
+
+
+@pytest.mark.timeout(600)
+def test_causal_bf16_full_size_sampled():
+    w = workloads.CAUSAL
+    rows = [0, 1, 2, 63, 64, 127, 128, 1000, 2047, 2048, 3071, 4094, 4095]
+    _full_size(w, [(0, 0), (0, 13), (0, 31)], rows)
+
+
+# ---------------------------------------------------------------------------
+# edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_one_key_and_one_query(dtype):
+    x = random_case(2001, 1, 2, 2, 1, 1, 64, dtype, sinks=True)
+    out, l, sc = _run(x, dtype)
+    compare_full(out, l, x, sc, dtype, "Lq=Lk=1")
+    x = random_case(2002, 1, 2, 1, 70, 1, 128, dtype)
+    out, l, sc = _run(x, dtype, causal=True)          # Lq > Lk: only the last row sees the key
+    compare_full(out, l, x, sc, dtype, "Lk=1 causal", causal=True)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16"])
+def test_fully_masked_rows(dtype):
+    x = random_case(2003, 1, 2, 2, 130, 90, 64, dtype, mask=True)
+    x["mask"][:, :, 5] = -math.inf                    # row 5 sees nothing
+    x["mask"][:, :, 100:] = -math.inf                 # rows 100.. see nothing
+    out, l, sc = _run(x, dtype)
+    assert torch.all(out[:, :, 5] == 0) and torch.all(out[:, :, 100:] == 0)
+    assert torch.all(torch.isneginf(l[:, :, 5]))
+    compare_full(out, l, x, sc, dtype, "masked rows")
+    # with sinks: O = 0 and LSE = sink on the empty rows
+    x["sinks"] = torch.tensor([0.5, -1.25])
+    out, l, sc = _run(x, dtype)
+    compare_full(out, l, x, sc, dtype, "masked rows + sinks")
+
+
+def test_large_sinks_and_scale():
+    x = random_case(2004, 2, 4, 2, 150, 200, 128, "bf16", sinks=True, sink_scale=10.0)
+    out, l, sc = _run(x, "bf16", causal=True, scale=0.3)
+    compare_full(out, l, x, sc, "bf16", "10x sinks", causal=True)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16"])
+def test_dominant_logit_and_identical_keys(dtype):
+    x = random_case(2005, 1, 1, 1, 40, 300, 64, dtype)
+    k = x["k"].float()
+    k[0, 0, 77] = 4.0 * x["q"][0, 0, 3].float()       # key 77 dominates query 3
+    k[0, 0, 200:] = k[0, 0, 200]                      # identical tail keys
+    x["k"] = k.to(x["q"].dtype)
+    out, l, sc = _run(x, dtype)
+    compare_full(out, l, x, sc, dtype, "dominant/identical")
+
+
+def test_non_contiguous_layouts():
+    # q, k, v, o stored as [B, L, H, D] and viewed as [B, H, L, D]
+    B, H, L, D = 2, 4, 150, 128
+    g = torch.Generator().manual_seed(7)
+    mk = lambda: torch.randn(B, L, H, D, generator=g).to(torch.bfloat16)
+    qs, ks, vs = mk(), mk(), mk()
+    x = {"q": qs.transpose(1, 2), "k": ks.transpose(1, 2), "v": vs.transpose(1, 2),
+         "mask": None, "sinks": None}
+    dq, dk, dv = (t.cuda().transpose(1, 2) for t in (qs, ks, vs))
+    o_store = torch.empty(B, L, H, D, dtype=torch.bfloat16, device="cuda")
+    out = sdpa.prefill(dq, dk, dv, causal=True, out=o_store.transpose(1, 2))
+    torch.cuda.synchronize()
+    compare_full(o_store.transpose(1, 2), None, x, 1 / math.sqrt(D), "bf16", "strided", causal=True)
+
+
+def test_deterministic():
+    x = to_dev(random_case(2006, 2, 4, 4, 333, 333, 128, "fp16"))
+    a = sdpa.prefill(x["q"], x["k"], x["v"], causal=True)
+    b = sdpa.prefill(x["q"], x["k"], x["v"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_gqa_equals_repeated_kv():
+    x = to_dev(random_case(2007, 1, 8, 2, 200, 260, 64, "bf16"))
+    a = sdpa.prefill(x["q"], x["k"], x["v"], causal=True)
+    b = sdpa.prefill(x["q"], x["k"].repeat_interleave(4, 1), x["v"].repeat_interleave(4, 1), causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_rejects_unsupported():
+    x = to_dev(random_case(2008, 1, 2, 2, 8, 8, 96, "fp16"))
+    with pytest.raises(sdpa.SdpaError) as e:
+        sdpa.prefill(x["q"], x["k"], x["v"])
+    assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
