@@ -20,6 +20,8 @@
 //                                      across the waves, partials summed in LDS)
 //     O^T (dims x heads) += V^T . P^T  (each wave owns a quarter of the dims)
 // K / V tiles stream HBM -> registers (next tile prefetched) -> LDS.
+#include <type_traits>
+
 #include "sdpa_device.hpp"
 #include "sdpa_internal.hpp"
 
@@ -251,13 +253,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
     } else {
 #pragma unroll
       for (int pp = 0; pp < C::NBLK / 2; ++pp) {
-        u32x4 pb = {T::pack2(sc[2 * pp][0], sc[2 * pp][1]), T::pack2(sc[2 * pp][2], sc[2 * pp][3]),
-                    T::pack2(sc[2 * pp + 1][0], sc[2 * pp + 1][1]),
-                    T::pack2(sc[2 * pp + 1][2], sc[2 * pp + 1][3])};
+        if constexpr (std::is_same<T, TBF16>::value) {
+          // bf16 P carries 8 significant bits: feed P = hi + lo (the matrix
+          // cores have ample headroom in this bandwidth-bound kernel)
+          u32x4 hi, lo;
 #pragma unroll
-        for (int i = 0; i < C::NOB; ++i) {
-          const int row = 16 * (wave * C::NOB + i) + n;
-          acc[i] = mma16(T{}, lds_read16(Vt + row * C::VP + (32 * pp + 8 * g4) * 2), pb, acc[i]);
+          for (int e = 0; e < 4; ++e) {
+            uint32_t h, l;
+            T::split2(sc[2 * pp + (e >> 1)][2 * (e & 1)], sc[2 * pp + (e >> 1)][2 * (e & 1) + 1], h, l);
+            hi[e] = h;
+            lo[e] = l;
+          }
+#pragma unroll
+          for (int i = 0; i < C::NOB; ++i) {
+            const int row = 16 * (wave * C::NOB + i) + n;
+            const u32x4 va = lds_read16(Vt + row * C::VP + (32 * pp + 8 * g4) * 2);
+            acc[i] = mma16(T{}, va, hi, acc[i]);
+            acc[i] = mma16(T{}, va, lo, acc[i]);
+          }
+        } else {
+          u32x4 pb = {T::pack2(sc[2 * pp][0], sc[2 * pp][1]), T::pack2(sc[2 * pp][2], sc[2 * pp][3]),
+                      T::pack2(sc[2 * pp + 1][0], sc[2 * pp + 1][1]),
+                      T::pack2(sc[2 * pp + 1][2], sc[2 * pp + 1][3])};
+#pragma unroll
+          for (int i = 0; i < C::NOB; ++i) {
+            const int row = 16 * (wave * C::NOB + i) + n;
+            acc[i] = mma16(T{}, lds_read16(Vt + row * C::VP + (32 * pp + 8 * g4) * 2), pb, acc[i]);
+          }
         }
       }
     }

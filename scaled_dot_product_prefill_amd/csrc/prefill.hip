@@ -19,6 +19,8 @@
 // query (lane % 32) for 16 keys of each 32-key block: the row max and row sum
 // are in-lane reductions plus one exchange with lane ^ 32, and the lane's
 // probabilities are directly the B operand of the P.V product.
+#include <type_traits>
+
 #include "sdpa_device.hpp"
 #include "sdpa_internal.hpp"
 
@@ -117,6 +119,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   if (CAUSAL) kend = min(kend, i0 + kBM + p.causal_off);
   const int ntiles = kend > 0 ? (kend + C::BN - 1) / C::BN : 0;
   const int wave_last_key = CAUSAL ? iw + 31 + p.causal_off : p.Lk - 1;
+  // bf16 probabilities carry 8 significant bits; rows that average few keys
+  // would show that rounding directly in O, so such workgroups feed P.V with
+  // P = hi + lo (two bf16 products).  Many-key rows average it away.
+  const bool split_p = std::is_same<T, TBF16>::value && (MASK || kend <= 1024);
 
   f32x16 acc[C::NMB];
 #pragma unroll
@@ -263,11 +269,30 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
       } else {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
+          const uint8_t* vcol = Vt + l32 * C::VP + (32 * kb + 16 * u + 8 * g) * 2;
+          if constexpr (std::is_same<T, TBF16>::value) {
+            if (split_p) {
+              u32x4 hi, lo;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                uint32_t h, l;
+                T::split2(sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1], h, l);
+                hi[e] = h;
+                lo[e] = l;
+              }
+#pragma unroll
+              for (int mb = 0; mb < C::NMB; ++mb) {
+                const u32x4 va = lds_read16(vcol + 32 * mb * C::VP);
+                acc[mb] = mma32(T{}, va, hi, acc[mb]);
+                acc[mb] = mma32(T{}, va, lo, acc[mb]);
+              }
+              continue;
+            }
+          }
           u32x4 pb = {T::pack2(sc[kb][8 * u + 0], sc[kb][8 * u + 1]),
                       T::pack2(sc[kb][8 * u + 2], sc[kb][8 * u + 3]),
                       T::pack2(sc[kb][8 * u + 4], sc[kb][8 * u + 5]),
                       T::pack2(sc[kb][8 * u + 6], sc[kb][8 * u + 7])};
-          const uint8_t* vcol = Vt + l32 * C::VP + (32 * kb + 16 * u + 8 * g) * 2;
 #pragma unroll
           for (int mb = 0; mb < C::NMB; ++mb)
             acc[mb] = mma32(T{}, lds_read16(vcol + 32 * mb * C::VP), pb, acc[mb]);

@@ -70,6 +70,13 @@ struct TBF16 {
   __device__ static inline uint32_t pack2(float lo, float hi) {
     return (uint32_t)from_f32(lo) | ((uint32_t)from_f32(hi) << 16);
   }
+  // p = hi + lo with hi = bf16(p) and lo = bf16(p - hi): a matrix product with
+  // both halves carries p to ~16 significant bits instead of 8.
+  __device__ static inline void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+    const storage ha = from_f32(a), hb = from_f32(b);
+    hi = (uint32_t)ha | ((uint32_t)hb << 16);
+    lo = pack2(a - to_f32(ha), b - to_f32(hb));
+  }
 };
 
 // Scalar reinterpretation.  Arguments are taken by value: a bit-cast applied
