@@ -70,8 +70,10 @@ __device__ constexpr int vt_group_slot(int kg) {
   return F32 ? kg : ((kg & ~3) | ((kg & 1) << 1) | ((kg & 2) >> 1));
 }
 
+// fp32 inputs: fp32 matrix cores (32x32x2), V transposed into LDS by the
+// loading threads.
 template <class T, int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) {
   using C = PrefillCfg<T, D>;
   using S = typename T::storage;
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::K_BYTES + C::V_BYTES];
@@ -333,18 +335,308 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnParams p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// 16-bit inputs (fp16 / bf16)
+// ---------------------------------------------------------------------------
+template <int D>
+struct Cfg16 {
+  static constexpr int BN = 64;                 // keys per tile
+  static constexpr int NKB = BN / 32;           // 32-key blocks per tile
+  static constexpr int NCH = D / 8;             // 16-byte chunks per row
+  static constexpr int KP = D * 2 + 16;         // K row pitch (bytes)
+  static constexpr int VP = D * 2 + 64;         // V row pitch (bytes): 4 rows tile 256 B
+  static constexpr int STAGE = BN * KP + BN * VP;
+  static constexpr int NQ = D / 16;             // 16-byte Q vectors per lane
+  static constexpr int IT = BN * NCH / kThreads;  // K (and V) chunks per thread
+  static constexpr int NMB = D / 32;            // 32-row blocks of O^T
+  static_assert(IT >= 1 && BN * NCH % kThreads == 0, "tile split");
+};
+
+// Per wave and tile (BN = 64 keys, 32 queries):
+//   S^T = K . Q^T        (NKB x NQ 32x32x16 matrix-core ops, K from LDS)
+//   online softmax       (in-lane over 32 keys, one exchange with lane ^ 32)
+//   O^T += V^T . P^T     (V^T read with ds_read_b64_tr_b16 from row-major V)
+// Interior tiles (every key visible, no mask) take a path with no per-element
+// visibility test; the scale is folded into the exponent, exp2(s*c - m).
+// The running max only rescales O and l when it grows for some lane.
+template <class T, int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
+  using C = Cfg16<D>;
+  using S = uint16_t;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const int nqt = (p.Lq + kBM - 1) / kBM;
+  const int bh_count = p.B * p.Hq;
+  const int qt = nqt - 1 - (int)(blockIdx.x / bh_count);  // heaviest causal tiles first
+  const int bh = blockIdx.x % bh_count;
+  const int b = bh / p.Hq;
+  const int hq = bh % p.Hq;
+  const int hk = hq / p.group;
+
+  const int i0 = qt * kBM;
+  const int iw = i0 + 32 * wave;
+  const int my_i = iw + l32;
+
+  // exponent scale c = |scale| log2(e); a negative scale is moved into Q
+  const float c = fabsf(p.scale_log2);
+  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+
+  u32x4 qreg[C::NQ];
+  {
+    const bool ok = my_i < p.Lq;
+    const S* row = (const S*)p.q + b * p.qs[0] + hq * p.qs[1] + (int64_t)(ok ? my_i : 0) * p.qs[2];
+#pragma unroll
+    for (int s = 0; s < C::NQ; ++s) {
+      u32x4 v = ldg16_cached(row + (2 * s + g) * 8);
+      v ^= qflip;
+      qreg[s] = ok ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  int kend = p.Lk;
+  if (CAUSAL) kend = min(kend, i0 + kBM + p.causal_off);
+  const int ntiles = kend > 0 ? (kend + C::BN - 1) / C::BN : 0;
+  const int wave_last_key = CAUSAL ? iw + 31 + p.causal_off : p.Lk - 1;
+  // bf16 probabilities carry 8 significant bits; rows that average few keys
+  // would show that rounding directly in O, so such workgroups feed P.V with
+  // P = hi + lo (two bf16 products).  Many-key rows average it away.
+  const bool split_p = std::is_same<T, TBF16>::value && (MASK || kend <= 1024);
+
+  f32x16 acc[C::NMB];
+#pragma unroll
+  for (int mb = 0; mb < C::NMB; ++mb) acc[mb] = f32x16{};
+  float m_run = kNegInf;  // running max of the scaled scores (log2 units)
+  float l_run = 0.f;      // running sum over this lane's half of the keys
+
+  // ---- K / V tile loads: buffer resources clip the key range (loads past
+  //      the last key return zeros); per-thread byte offsets are fixed ----
+  const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
+  const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
+  uint32_t koff[C::IT], voff[C::IT], lds_off[C::IT];
+#pragma unroll
+  for (int it = 0; it < C::IT; ++it) {
+    const int u = tid + kThreads * it;
+    const int key = u / C::NCH, ch = u % C::NCH;
+    koff[it] = (uint32_t)(key * p.ks[2] * 2 + ch * 16);
+    voff[it] = (uint32_t)(key * p.vs[2] * 2 + ch * 16);
+    lds_off[it] = key * C::KP + ch * 16;
+  }
+  auto valid_bytes = [&](int j0, int64_t stride) -> uint32_t {
+    const int64_t n = (int64_t)(p.Lk - j0 - 1) * stride * 2 + D * 2;
+    return n > 0xffffffffLL ? 0xffffffffu : (uint32_t)n;
+  };
+  u32x4 kpre[C::IT], vpre[C::IT];
+  auto prefetch = [&](int j0) {
+    const auto rk = make_rsrc(kbase + (int64_t)j0 * p.ks[2], valid_bytes(j0, p.ks[2]));
+    const auto rv = make_rsrc(vbase + (int64_t)j0 * p.vs[2], valid_bytes(j0, p.vs[2]));
+#pragma unroll
+    for (int it = 0; it < C::IT; ++it) {
+      kpre[it] = buf_load16(rk, koff[it]);
+      vpre[it] = buf_load16(rv, voff[it]);
+    }
+  };
+  auto store = [&](uint8_t* st) {
+#pragma unroll
+    for (int it = 0; it < C::IT; ++it) {
+      lds_write16(st + lds_off[it], kpre[it]);
+      // V rows use the V pitch: the same (key, chunk) position
+      const int u = tid + kThreads * it;
+      lds_write16(st + C::BN * C::KP + (u / C::NCH) * C::VP + (u % C::NCH) * 16, vpre[it]);
+    }
+  };
+
+  // lane part of the transposed V read: row 4g + r/4, columns 16*dh + 4*(r%4)
+  const int r16 = lane & 15;
+  const int dh = (lane >> 4) & 1;
+  const uint32_t vtr_lane = (4 * g + (r16 >> 2)) * C::VP + (16 * dh + 4 * (r16 & 3)) * 2;
+
+  auto compute = [&](const uint8_t* st, int j0, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    const uint8_t* Ks = st;
+    const uint8_t* Vs = st + C::BN * C::KP;
+    f32x16 sc[C::NKB];
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+      sc[kb] = f32x16{};
+      const uint8_t* krow = Ks + (32 * kb + l32) * C::KP + g * 16;
+#pragma unroll
+      for (int s = 0; s < C::NQ; ++s) sc[kb] = mma32(T{}, lds_read16(krow + s * 32), qreg[s], sc[kb]);
+    }
+    float m_use;
+    if constexpr (!EDGE) {
+      // every key visible: max over raw scores, scale applied once per row
+      float mx = sc[0][0];
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+      mx = fmaxf(mx, xor32(mx)) * c;
+      const float m_new = fmaxf(m_run, mx);
+      if (__any(m_new > m_run)) {
+        const float corr = fast_exp2(m_run - m_new);
+        l_run *= corr;
+#pragma unroll
+        for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+        m_run = m_new;
+      }
+      m_use = m_run;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(fmaf(sc[kb][r], c, -m_use));
+          sc[kb][r] = pr;
+          l_run += pr;
+        }
+    } else {
+      float mx = kNegInf;
+      const int ii = my_i < p.Lq ? my_i : p.Lq - 1;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          float x = sc[kb][r] * c;
+          if (MASK) {
+            const int jj = j < p.Lk ? j : p.Lk - 1;
+            x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]];
+          }
+          const bool vis = (j < p.Lk) && (!CAUSAL || j <= my_i + p.causal_off);
+          x = vis ? x : kNegInf;
+          sc[kb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, xor32(mx));
+      const float m_new = fmaxf(m_run, mx);
+      if (__any(m_new > m_run)) {
+        const float corr = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+        l_run *= corr;
+#pragma unroll
+        for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+        m_run = m_new;
+      }
+      m_use = m_run == kNegInf ? 0.f : m_run;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pr = fast_exp2(sc[kb][r] - m_use);
+          sc[kb][r] = pr;
+          l_run += pr;
+        }
+    }
+    // ---- O^T += V^T . P^T; k-step u of block kb covers keys 32kb + 16u + [0, 16):
+    //      B element e <-> key 16u + 8(e/4) + 4g + e%4 (the accumulator rows)
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        u32x4 hi, lo;
+        bool two = false;
+        if constexpr (std::is_same<T, TBF16>::value) {
+          if (split_p) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              uint32_t h, l;
+              T::split2(sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1], h, l);
+              hi[e] = h;
+              lo[e] = l;
+            }
+            two = true;
+          }
+        }
+        if (!two) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) hi[e] = cvt_pk(T{}, sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1]);
+        }
+        const uint8_t* vb = Vs + vtr_lane + (32 * kb + 16 * u) * C::VP;
+#pragma unroll
+        for (int mb = 0; mb < C::NMB; ++mb) {
+          const u32x2 a0 = lds_read_tr16(vb + 64 * mb);
+          const u32x2 a1 = lds_read_tr16(vb + 8 * C::VP + 64 * mb);
+          const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
+          acc[mb] = mma32(T{}, va, hi, acc[mb]);
+          if (two) acc[mb] = mma32(T{}, va, lo, acc[mb]);
+        }
+      }
+    }
+  };
+
+  if (ntiles > 0) {
+    prefetch(0);
+    store(smem);
+  }
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = t * C::BN;
+    uint8_t* cur = smem + (t & 1) * C::STAGE;
+    if (t + 1 < ntiles) prefetch(j0 + C::BN);
+    if (j0 <= wave_last_key) {
+      const bool edge = MASK || (j0 + C::BN > p.Lk) || (CAUSAL && j0 + C::BN - 1 > iw + p.causal_off);
+      if (edge) compute(cur, j0, std::true_type{});
+      else compute(cur, j0, std::false_type{});
+    }
+    if (t + 1 < ntiles) store(smem + ((t + 1) & 1) * C::STAGE);
+    __syncthreads();
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + xor32(l_run);
+  float M = m_run, Ltot = l_tot;
+  if (p.sinks) {
+    const float sk = p.sinks[hq] * kLog2e;
+    M = fmaxf(m_run, sk);
+    if (M != kNegInf) Ltot = l_tot * fast_exp2(m_run - M) + fast_exp2(sk - M);
+  }
+  float scale_o = 0.f, lse = kNegInf;
+  if (M != kNegInf && Ltot > 0.f) {
+    scale_o = (p.sinks ? fast_exp2(m_run - M) : 1.f) / Ltot;
+    lse = (M + fast_log2(Ltot)) * kLn2;
+  }
+  if (my_i < p.Lq) {
+    S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)my_i * p.os[2];
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        // rows 8*q4 + 4g + (0..3) of block mb: four consecutive head-dim elements
+        const u32x2 w = {cvt_pk(T{}, acc[mb][4 * q4] * scale_o, acc[mb][4 * q4 + 1] * scale_o),
+                         cvt_pk(T{}, acc[mb][4 * q4 + 2] * scale_o, acc[mb][4 * q4 + 3] * scale_o)};
+        *(u32x2*)(orow + 32 * mb + 8 * q4 + 4 * g) = w;
+      }
+    if (p.lse && g == 0) p.lse[((int64_t)b * p.Hq + hq) * p.Lq + my_i] = lse;
+  }
+}
+
 template <class T, int D>
 hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
   const int nqt = (p.Lq + kBM - 1) / kBM;
   const dim3 grid((unsigned)(nqt * p.B * p.Hq));
   const dim3 block(kThreads);
   const bool mask = p.mask != nullptr;
-  if (causal) {
-    if (mask) hipLaunchKernelGGL((prefill_kernel<T, D, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((prefill_kernel<T, D, true, false>), grid, block, 0, s, p);
+  if constexpr (std::is_same<T, TF32>::value) {
+    if (causal) {
+      if (mask) hipLaunchKernelGGL((prefill_f32_kernel<T, D, true, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill_f32_kernel<T, D, true, false>), grid, block, 0, s, p);
+    } else {
+      if (mask) hipLaunchKernelGGL((prefill_f32_kernel<T, D, false, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill_f32_kernel<T, D, false, false>), grid, block, 0, s, p);
+    }
   } else {
-    if (mask) hipLaunchKernelGGL((prefill_kernel<T, D, false, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((prefill_kernel<T, D, false, false>), grid, block, 0, s, p);
+    if (causal) {
+      if (mask) hipLaunchKernelGGL((prefill16_kernel<T, D, true, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill16_kernel<T, D, true, false>), grid, block, 0, s, p);
+    } else {
+      if (mask) hipLaunchKernelGGL((prefill16_kernel<T, D, false, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill16_kernel<T, D, false, false>), grid, block, 0, s, p);
+    }
   }
   return hipGetLastError();
 }

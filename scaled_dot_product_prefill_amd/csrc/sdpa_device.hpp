@@ -119,6 +119,18 @@ __device__ inline f32x4 mma16(TF32, u32x4 a, u32x4 b, f32x4 c) {
   return c;
 }
 
+// Two fp32 values -> one dword of two 16-bit values (round to nearest even;
+// v_cvt_pk_{bf16,f16}_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t cvt_pk(TBF16, float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
+}
+__device__ inline uint32_t cvt_pk(TF16, float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+}
+
 // ---------------------------------------------------------------------------
 // memory helpers
 // ---------------------------------------------------------------------------
@@ -126,6 +138,26 @@ __device__ inline u32x4 ldg16(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
 __device__ inline u32x4 ldg16_cached(const void* p) { return *(const u32x4*)p; }
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane r names 4 consecutive
+// 16-bit values (a "row"); lane r receives element (r % 4) of the rows named by
+// lanes r/4, 4 + r/4, 8 + r/4, 12 + r/4.  With lane r pointing at
+// X[k0 + r/4][c0 + 4*(r%4)] of a row-major 16-bit matrix X, lane r receives
+// X[k0 + e][c0 + r] for e = 0..3: a 4 x 16 block read transposed.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x2 lds_read_tr16(const void* p) {
+  // address-space cast (not an integer cast): generic LDS address -> LDS offset
+  auto lp = (__attribute__((address_space(3))) s16x4*)(const_cast<void*>(p));
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(lp));
+}
 __device__ inline u32x4 lds_read16(const void* p) { return *(const u32x4*)p; }
 __device__ inline void lds_write16(void* p, u32x4 v) { *(u32x4*)p = v; }
 __device__ inline void lds_write8(void* p, u32x2 v) { *(u32x2*)p = v; }
