@@ -350,8 +350,16 @@ struct Cfg16 {
   static constexpr int NQ = D / 16;             // 16-byte Q vectors per lane
   static constexpr int IT = BN * NCH / kThreads;  // K (and V) chunks per thread
   static constexpr int NMB = D / 32;            // 32-row blocks of O^T
+  // D = 64: the per-row sum of P runs on the matrix cores as one more
+  // 32-row block whose V^T rows are all ones (the VALU is the scarcer unit)
+  static constexpr bool SUM_MFMA = (D == 64);
   static_assert(IT >= 1 && BN * NCH % kThreads == 0, "tile split");
 };
+
+// The running max is only moved (and O, l rescaled) when a row's tile max
+// exceeds it by more than this many log2 units; probabilities then stay
+// below 2^8, and O = sum(p v) / sum(p) is unchanged by which max is used.
+constexpr float kRescaleSlack = 8.f;
 
 // Per wave and tile (BN = 64 keys, 32 queries):
 //   S^T = K . Q^T        (NKB x NQ 32x32x16 matrix-core ops, K from LDS)
@@ -412,8 +420,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
   f32x16 acc[C::NMB];
 #pragma unroll
   for (int mb = 0; mb < C::NMB; ++mb) acc[mb] = f32x16{};
-  float m_run = kNegInf;  // running max of the scaled scores (log2 units)
+  f32x16 lacc = f32x16{};  // row sums from the matrix cores (SUM_MFMA)
+  float m_run = kNegInf;  // reference max of the scaled scores (log2 units)
   float l_run = 0.f;      // running sum over this lane's half of the keys
+  constexpr uint32_t kOnes = std::is_same<T, TBF16>::value ? 0x3F803F80u : 0x3C003C00u;
+  const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
+  auto rescale = [&](float corr) {
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+    if constexpr (C::SUM_MFMA) lacc *= corr;
+    else l_run *= corr;
+  };
 
   // ---- K / V tile loads: buffer resources clip the key range (loads past
   //      the last key return zeros); per-thread byte offsets are fixed ----
@@ -477,13 +494,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = fmaxf(mx, xor32(mx)) * c;
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        const float corr = fast_exp2(m_run - m_new);
-        l_run *= corr;
-#pragma unroll
-        for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+      mx = max_xor32(mx) * c;
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        rescale(fast_exp2(m_run - m_new));
         m_run = m_new;
       }
       m_use = m_run;
@@ -493,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
         for (int r = 0; r < 16; ++r) {
           const float pr = fast_exp2(fmaf(sc[kb][r], c, -m_use));
           sc[kb][r] = pr;
-          l_run += pr;
+          if constexpr (!C::SUM_MFMA) l_run += pr;
         }
     } else {
       float mx = kNegInf;
@@ -513,13 +527,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
           sc[kb][r] = x;
           mx = fmaxf(mx, x);
         }
-      mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      if (__any(m_new > m_run)) {
-        const float corr = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
-        l_run *= corr;
-#pragma unroll
-        for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+      mx = max_xor32(mx);
+      if (__any(mx > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mx);
+        // rows that still see nothing (both -inf) keep corr = 1
+        rescale(m_new > m_run ? fast_exp2(m_run - m_new) : 1.f);
         m_run = m_new;
       }
       m_use = m_run == kNegInf ? 0.f : m_run;
@@ -529,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
         for (int r = 0; r < 16; ++r) {
           const float pr = fast_exp2(sc[kb][r] - m_use);
           sc[kb][r] = pr;
-          l_run += pr;
+          if constexpr (!C::SUM_MFMA) l_run += pr;
         }
     }
     // ---- O^T += V^T . P^T; k-step u of block kb covers keys 32kb + 16u + [0, 16):
@@ -565,30 +577,47 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
           acc[mb] = mma32(T{}, va, hi, acc[mb]);
           if (two) acc[mb] = mma32(T{}, va, lo, acc[mb]);
         }
+        if constexpr (C::SUM_MFMA) {
+          lacc = mma32(T{}, ones, hi, lacc);
+          if (two) lacc = mma32(T{}, ones, lo, lacc);
+        }
       }
     }
   };
 
+  // Tiles [0, n_int) are interior for every wave of the workgroup (all keys
+  // visible to all 128 rows, no mask); they run a loop with a single path.
+  // The remaining tiles (causal diagonal, key tail, or every tile when a mask
+  // is given) run the masking path.
+  int n_int = 0;
+  if (!MASK) {
+    int last_full = p.Lk;                                   // keys [0, last_full) are in range
+    if (CAUSAL) last_full = min(last_full, i0 + 1 + p.causal_off);  // visible to row i0
+    n_int = last_full > 0 ? min(ntiles, last_full / C::BN) : 0;
+  }
   if (ntiles > 0) {
     prefetch(0);
     store(smem);
   }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  int t = 0;
+  for (; t < n_int; ++t) {
     const int j0 = t * C::BN;
-    uint8_t* cur = smem + (t & 1) * C::STAGE;
     if (t + 1 < ntiles) prefetch(j0 + C::BN);
-    if (j0 <= wave_last_key) {
-      const bool edge = MASK || (j0 + C::BN > p.Lk) || (CAUSAL && j0 + C::BN - 1 > iw + p.causal_off);
-      if (edge) compute(cur, j0, std::true_type{});
-      else compute(cur, j0, std::false_type{});
-    }
+    compute(smem + (t & 1) * C::STAGE, j0, std::false_type{});
+    if (t + 1 < ntiles) store(smem + ((t + 1) & 1) * C::STAGE);
+    __syncthreads();
+  }
+  for (; t < ntiles; ++t) {
+    const int j0 = t * C::BN;
+    if (t + 1 < ntiles) prefetch(j0 + C::BN);
+    if (j0 <= wave_last_key) compute(smem + (t & 1) * C::STAGE, j0, std::true_type{});
     if (t + 1 < ntiles) store(smem + ((t + 1) & 1) * C::STAGE);
     __syncthreads();
   }
 
   // ---- epilogue ----
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = C::SUM_MFMA ? lacc[0] : sum_xor32(l_run);
   float M = m_run, Ltot = l_tot;
   if (p.sinks) {
     const float sk = p.sinks[hq] * kLog2e;

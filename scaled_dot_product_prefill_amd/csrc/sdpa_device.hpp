@@ -173,6 +173,17 @@ __device__ inline uint32_t join_hi(uint32_t a, uint32_t b) { return perm(a, b, 0
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Combine each lane with lane l ^ 32 (v_permlane32_swap: the two halves of
+// the wave trade places, no LDS round trip).
+__device__ inline float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_uint(v), as_uint(v), false, false);
+  return fmaxf(as_float(r[0]), as_float(r[1]));
+}
+__device__ inline float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_uint(v), as_uint(v), false, false);
+  return as_float(r[0]) + as_float(r[1]);
+}
+
 // exchange with lane l ^ 32 (the other half of the wave)
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32, 64); }
 __device__ inline float xor16(float v) { return __shfl_xor(v, 16, 64); }
