@@ -187,6 +187,17 @@ def main():
     sdpa.library()
 
     wl = args.workload
+    if wl == "copy_1gib":
+        # calibration for the HBM byte counters: one device copy of 1 GiB
+        # (reads 1 GiB, writes 1 GiB) per step
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": "copy_1gib", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "steps": args.steps + args.warmup}))
+        return
     pre_w = workloads.DIT_FP16 if wl == "default" else workloads.ALL[wl]
     run_prefill = wl == "default" or pre_w.Lq > 1
     dec_w = workloads.LONG_DECODE if wl == "default" else (pre_w if pre_w.Lq == 1 else None)

@@ -333,42 +333,73 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
   }
 }
 
-// Merge pass: one workgroup per (batch, query head); thread d handles
-// elements d, d + 128, ...
+// Merge pass.  Workgroup (b, hq, 64-element slice of the head dim): the
+// reference max M and the total L are reduced over the splits by all 256
+// threads, then thread (split group sg, element quad dq) sums its splits'
+// weighted partial O for four head-dim elements and the 16 split groups are
+// combined in LDS.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeCols = 64;  // head-dim elements per workgroup
+
 template <class T, int D>
-__global__ __launch_bounds__(128) void merge_kernel(AttnParams p) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   using S = typename T::storage;
-  const int64_t bh = blockIdx.x;
+  constexpr int NDQ = (D < kMergeCols ? D : kMergeCols) / 4;  // float4 columns per workgroup
+  constexpr int NSG = kMergeThreads / NDQ;                      // split groups
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ f32x4 part[NSG][NDQ];
+  const int tid = threadIdx.x;
+  const int nslice = D / (NDQ * 4);
+  const int64_t bh = blockIdx.x / nslice;
+  const int d0 = (blockIdx.x % nslice) * NDQ * 4;
   const int hq = (int)(bh % p.Hq);
   const int b = (int)(bh / p.Hq);
   const float* pml = p.part_ml + bh * p.nsplit * 2;
   const float* po = p.part_o + bh * p.nsplit * D;
-  float M = kNegInf;
-  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, pml[2 * s]);
   const float sk = p.sinks ? p.sinks[hq] * kLog2e : kNegInf;
+
+  // M = max(max_s m_s, sink)
+  float M = kNegInf;
+  for (int s = tid; s < p.nsplit; s += kMergeThreads) M = fmaxf(M, pml[2 * s]);
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   M = fmaxf(M, sk);
+  __syncthreads();
+  // L = sum_s l_s 2^(m_s - M) + 2^(sink - M); splits with m_s = -inf weigh 0
   float L = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < p.nsplit; ++s) {
+  if (M != kNegInf)
+    for (int s = tid; s < p.nsplit; s += kMergeThreads) {
       const float ms = pml[2 * s];
       if (ms != kNegInf) L += pml[2 * s + 1] * fast_exp2(ms - M);
     }
-    if (p.sinks) L += fast_exp2(sk - M);
-  }
+  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+  if ((tid & 63) == 0) red[tid >> 6] = L;
+  __syncthreads();
+  L = red[0] + red[1] + red[2] + red[3];
+  if (p.sinks && M != kNegInf) L += fast_exp2(sk - M);
   const bool live = M != kNegInf && L > 0.f;
-  const float inv = live ? 1.f / L : 0.f;
-  S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1];
-  for (int d = threadIdx.x; d < D; d += 128) {
-    float o = 0.f;
-    if (live) {
-      for (int s = 0; s < p.nsplit; ++s) {
-        const float ms = pml[2 * s];
-        if (ms != kNegInf) o += po[(int64_t)s * D + d] * fast_exp2(ms - M);
-      }
+
+  // weighted partial numerators
+  const int dq = tid % NDQ, sg = tid / NDQ;
+  f32x4 o = f32x4{};
+  if (live)
+    for (int s = sg; s < p.nsplit; s += NSG) {
+      const float ms = pml[2 * s];
+      if (ms != kNegInf) o += fast_exp2(ms - M) * *(const f32x4*)(po + (int64_t)s * D + d0 + 4 * dq);
     }
-    orow[d] = T::from_f32(o * inv);
+  part[sg][dq] = o;
+  __syncthreads();
+  if (sg == 0) {
+    for (int g = 1; g < NSG; ++g) o += part[g][dq];
+    const float inv = live ? 1.f / L : 0.f;
+    S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + d0 + 4 * dq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) orow[e] = T::from_f32(o[e] * inv);
+    if (p.lse && blockIdx.x % nslice == 0 && dq == 0)
+      p.lse[bh] = live ? (M + fast_log2(L)) * kLn2 : kNegInf;
   }
-  if (p.lse && threadIdx.x == 0) p.lse[bh] = live ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
 template <class T, int D>
@@ -381,7 +412,9 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
     else hipLaunchKernelGGL((decode_kernel<T, D, false, true>), grid, block, 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)p.B * p.Hq)), dim3(128), 0, s, p);
+    const int nslice = D / (D < kMergeCols ? D : kMergeCols);
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)p.B * p.Hq * nslice)),
+                       dim3(kMergeThreads), 0, s, p);
   } else {
     if (mask) hipLaunchKernelGGL((decode_kernel<T, D, true, false>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((decode_kernel<T, D, false, false>), grid, block, 0, s, p);

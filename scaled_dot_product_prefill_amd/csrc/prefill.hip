@@ -89,9 +89,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
   // heaviest (last) query tiles first: with the causal mask their key range
   // is the longest
   const int nqt = (p.Lq + kBM - 1) / kBM;
-  const int bh_count = p.B * p.Hq;
-  const int qt = nqt - 1 - (int)(blockIdx.x / bh_count);
-  const int bh = blockIdx.x % bh_count;
+  int qt, bh;
+  prefill_tile((int)blockIdx.x, (int)gridDim.x, nqt, p.B * p.Hq, CAUSAL, qt, bh);
   const int b = bh / p.Hq;
   const int hq = bh % p.Hq;
   const int hk = hq / p.group;
@@ -381,9 +380,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
   const int g = lane >> 5;
 
   const int nqt = (p.Lq + kBM - 1) / kBM;
-  const int bh_count = p.B * p.Hq;
-  const int qt = nqt - 1 - (int)(blockIdx.x / bh_count);  // heaviest causal tiles first
-  const int bh = blockIdx.x % bh_count;
+  int qt, bh;
+  prefill_tile((int)blockIdx.x, (int)gridDim.x, nqt, p.B * p.Hq, CAUSAL, qt, bh);
   const int b = bh / p.Hq;
   const int hq = bh % p.Hq;
   const int hk = hq / p.group;

@@ -170,6 +170,38 @@ __device__ inline uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) {
 __device__ inline uint32_t join_lo(uint32_t a, uint32_t b) { return perm(a, b, 0x05040100u); }
 __device__ inline uint32_t join_hi(uint32_t a, uint32_t b) { return perm(a, b, 0x07060302u); }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (block i -> XCD i % 8),
+// each with its own L2.  Map block i to work item w so that every XCD walks a
+// contiguous range of the work list (a bijection on [0, n)).
+constexpr int kNumXcd = 8;
+__device__ inline int xcd_work_index(int i, int n) {
+  const int x = i % kNumXcd, local = i / kNumXcd;
+  const int q = n / kNumXcd, r = n % kNumXcd;
+  return x < r ? x * (q + 1) + local : r * (q + 1) + (x - r) * q + local;
+}
+
+// Prefill workgroup -> (query tile, batch*head).  Causal: tiles differ in
+// work, so the heaviest (last) query tiles go first; when the head count is a
+// multiple of 8, head h lives on XCD h % 8 (its K / V stay in one L2) and each
+// XCD runs its heads' tiles heaviest first.  Non-causal: tiles are equal, each
+// XCD walks whole heads in turn.
+__device__ inline void prefill_tile(int i, int n, int nqt, int nbh, bool causal, int& qt, int& bh) {
+  if (causal) {
+    if (nbh % kNumXcd == 0) {
+      const int per = nbh / kNumXcd, local = i / kNumXcd;
+      qt = nqt - 1 - local / per;
+      bh = i % kNumXcd + kNumXcd * (local % per);
+    } else {
+      qt = nqt - 1 - i / nbh;
+      bh = i % nbh;
+    }
+  } else {
+    const int w = xcd_work_index(i, n);
+    qt = w % nqt;
+    bh = w / nqt;
+  }
+}
+
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
