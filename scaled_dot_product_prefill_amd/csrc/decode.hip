@@ -37,23 +37,38 @@ struct DecodeCfg {
   static constexpr int VEC = T::kVec;
   static constexpr int NCH = D / VEC;                  // 16-byte chunks per row
   static constexpr bool F32 = (ES == 4);
-  static constexpr int TK = F32 ? (D >= 256 ? 16 : 4096 / D) : (D >= 256 ? 32 : 8192 / D);
+#ifndef SDPA_DECODE_TILE_BYTES
+#define SDPA_DECODE_TILE_BYTES 32768  // K + V bytes per key tile (D <= 128)
+#endif
+#ifndef SDPA_DECODE_MAX_STAGE_BYTES
+#define SDPA_DECODE_MAX_STAGE_BYTES 81920  // double-buffer LDS when 2 stages fit in this
+#endif
+  static constexpr int TK = F32 ? (D >= 256 ? 16 : SDPA_DECODE_TILE_BYTES / (8 * D))
+                                : (D >= 256 ? 32 : SDPA_DECODE_TILE_BYTES / (4 * D));
   static constexpr int NBLK = TK / 16;                 // 16-key blocks per tile
   static constexpr int KP = D * ES + 16;               // K row pitch (bytes)
-  static constexpr int VP = TK * ES + 16;              // V^T row pitch (bytes)
+  // 16-bit: V row-major, read transposed (ds_read_b64_tr_b16); a pitch of
+  // 32 (mod 256) bytes spreads the 16 rows one read touches over the banks.
+  // fp32: V^T written transposed by the loading threads.
+  static constexpr int VP = F32 ? TK * ES + 16 : D * 2 + 32;
   static constexpr int K_BYTES = TK * KP;
-  static constexpr int V_BYTES = D * VP;
-  static constexpr int NS = D * ES / 64;               // 16-byte Q vectors per head row / 4
-  static constexpr int QSPLIT = NS < kWaves ? NS : kWaves;  // waves sharing Q.K^T
+  static constexpr int V_BYTES = F32 ? D * VP : TK * VP;
+  static constexpr int NS = D * ES / 64;               // Q vectors per head row / 4
+  // fp32 splits the Q.K^T contraction over the waves (a full fp32 Q row
+  // would not fit the registers) and sums the partial scores in LDS; 16-bit
+  // waves each form the whole S^T tile.
+  static constexpr int QSPLIT = F32 ? (NS < kWaves ? NS : kWaves) : 1;
   static constexpr int NSW = NS / QSPLIT;              // Q vectors per wave
-  static constexpr int X_BYTES = QSPLIT * NBLK * 64 * 16;  // partial-score exchange
+  static constexpr int X_BYTES = F32 ? QSPLIT * NBLK * 64 * 16 : 0;
   static constexpr int NOB = D / 16 / kWaves;          // 16-row blocks of O^T per wave
   static constexpr int K_IT = TK * NCH / kThreads;
-  static constexpr int V_IT = (TK / 4) * NCH / kThreads;
+  static constexpr int V_IT = F32 ? (TK / 4) * NCH / kThreads : TK * NCH / kThreads;
+  static constexpr int STAGE = K_BYTES + V_BYTES;
+  static constexpr int STAGES = 2 * STAGE <= SDPA_DECODE_MAX_STAGE_BYTES ? 2 : 1;
   static_assert(NS % QSPLIT == 0, "Q split");
   static_assert(NOB >= 1, "O split");
   static_assert(K_IT >= 1 && TK * NCH % kThreads == 0, "K tile split");
-  static_assert(V_IT >= 1 && (TK / 4) * NCH % kThreads == 0, "V tile split");
+  static_assert(V_IT >= 1, "V tile split");
   static_assert(F32 ? TK % 16 == 0 : TK % 32 == 0, "tile keys");
 };
 
@@ -62,36 +77,25 @@ __device__ constexpr int vt_row(int c, int e) { return c + NCH * e; }
 template <int NCH, int VEC>
 __device__ constexpr int vt_row_to_d(int rho) { return VEC * (rho % NCH) + rho / NCH; }
 
-// Slot of key group kg (4 keys) inside a 32-key block of a V^T row.  16-bit:
-// lane group g4 of the P.V product supplies keys {16a + 4*g4 + c} (a: which
-// 16-key score block, c = 0..3) as its 8 contiguous k-slots 8*g4 + 4a + c.
-// fp32: natural order.
-template <bool F32>
-__device__ constexpr int vt_group_slot(int kg) {
-  return F32 ? kg : ((kg & ~7) | (2 * (kg & 3) + ((kg >> 2) & 1)));
-}
-
 template <class T, int D, bool MASK, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   using C = DecodeCfg<T, D>;
   using S = typename T::storage;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[C::K_BYTES + C::V_BYTES + C::X_BYTES];
-  uint8_t* Ks = smem;
-  uint8_t* Vt = smem + C::K_BYTES;
-  f32x4* Sx = (f32x4*)(smem + C::K_BYTES + C::V_BYTES);
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::STAGES * C::STAGE + (C::X_BYTES ? C::X_BYTES : 16)];
+  f32x4* Sx = (f32x4*)(smem + C::STAGES * C::STAGE);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int n = lane & 15;   // head column of the 16x16 tiles
+  const int n = lane & 15;   // head column of the 16x16 tiles (also the K row of the A operand)
   const int g4 = lane >> 4;  // lane group
 
   const int split = blockIdx.x % p.nsplit;
   const int bk = blockIdx.x / p.nsplit;
   const int hk = bk % p.Hkv;
   const int b = bk / p.Hkv;
-  const int hq = hk * p.group + n;  // query head of this lane's column
   const bool head_ok = n < p.group;
+  const int hq = hk * p.group + (head_ok ? n : 0);  // query head of this lane's column
 
   const int kbeg = split * p.split_len;
   const int kend = min(p.Lk, kbeg + p.split_len);
@@ -100,11 +104,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
   const S* kp = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
   const S* vp = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
 
-  // ---- Q^T operand: this wave's share of the head dim; vector s = chunk 4*(s0+s) + g4
+  // ---- Q^T operand (B of S^T = K . Q^T): vector s holds chunk 4*(s0+s) + g4
   u32x4 qreg[C::NSW];
   {
     const int s0 = wave < C::QSPLIT ? wave * C::NSW : 0;
-    const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)(head_ok ? hq : hk * p.group) * p.qs[1];
+    const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1];
 #pragma unroll
     for (int s = 0; s < C::NSW; ++s) {
       u32x4 v = ldg16_cached(row + (4 * (s0 + s) + g4) * C::VEC);
@@ -112,151 +116,169 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
     }
   }
 
+  // mask row of this lane's head: four consecutive keys per 16-key block
+  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] : nullptr;
+  const bool mask_vec = MASK && p.ms[3] == 1 && (((uintptr_t)mrow) & 15) == 0;
+
   f32x4 acc[C::NOB];
 #pragma unroll
   for (int i = 0; i < C::NOB; ++i) acc[i] = f32x4{};
   float m_run = kNegInf;
   float l_run = 0.f;
 
+  // ---- tile loads (buffer resources zero-fill keys at or past kend)
+  auto valid_bytes = [&](int j0, int64_t stride) -> uint32_t {
+    const int64_t nb = (int64_t)(kend - j0 - 1) * stride * C::ES + D * C::ES;
+    return nb > 0xffffffffLL ? 0xffffffffu : (uint32_t)nb;
+  };
   u32x4 kpre[C::K_IT];
-  u32x4 vpre[C::V_IT][4];
+  u32x4 vpre[C::V_IT][C::F32 ? 4 : 1];
   auto prefetch = [&](int j0) {
+    const auto rk = make_rsrc(kp + (int64_t)j0 * p.ks[2], valid_bytes(j0, p.ks[2]));
+    const auto rv = make_rsrc(vp + (int64_t)j0 * p.vs[2], valid_bytes(j0, p.vs[2]));
 #pragma unroll
     for (int it = 0; it < C::K_IT; ++it) {
       const int u = tid + kThreads * it;
-      const int key = u / C::NCH, c = u % C::NCH;
-      const int j = j0 + key;
-      kpre[it] = j < kend ? ldg16(kp + (int64_t)j * p.ks[2] + c * C::VEC) : u32x4{0, 0, 0, 0};
+      kpre[it] = buf_load16(rk, (uint32_t)((u / C::NCH) * p.ks[2] * C::ES + (u % C::NCH) * 16));
     }
 #pragma unroll
     for (int it = 0; it < C::V_IT; ++it) {
       const int u = tid + kThreads * it;
-      const int kg = u / C::NCH, c = u % C::NCH;
+      if constexpr (C::F32) {
+        const int kg = u / C::NCH, c = u % C::NCH;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 4 * kg + r;
-        vpre[it][r] = j < kend ? ldg16(vp + (int64_t)j * p.vs[2] + c * C::VEC) : u32x4{0, 0, 0, 0};
+        for (int r = 0; r < 4; ++r)
+          vpre[it][r] = buf_load16(rv, (uint32_t)((4 * kg + r) * p.vs[2] * C::ES + c * 16));
+      } else {
+        vpre[it][0] = buf_load16(rv, (uint32_t)((u / C::NCH) * p.vs[2] * C::ES + (u % C::NCH) * 16));
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](uint8_t* st) {
+    uint8_t* Ks = st;
+    uint8_t* Vs = st + C::K_BYTES;
 #pragma unroll
     for (int it = 0; it < C::K_IT; ++it) {
       const int u = tid + kThreads * it;
-      const int key = u / C::NCH, c = u % C::NCH;
-      lds_write16(Ks + key * C::KP + c * 16, kpre[it]);
+      lds_write16(Ks + (u / C::NCH) * C::KP + (u % C::NCH) * 16, kpre[it]);
     }
 #pragma unroll
     for (int it = 0; it < C::V_IT; ++it) {
       const int u = tid + kThreads * it;
-      const int kg = u / C::NCH, c = u % C::NCH;
-      const int slot4 = vt_group_slot<C::F32>(kg);
       if constexpr (C::F32) {
+        const int kg = u / C::NCH, c = u % C::NCH;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           u32x4 w = {vpre[it][0][e], vpre[it][1][e], vpre[it][2][e], vpre[it][3][e]};
-          lds_write16(Vt + vt_row<C::NCH>(c, e) * C::VP + slot4 * 16, w);
+          lds_write16(Vs + vt_row<C::NCH>(c, e) * C::VP + kg * 16, w);
         }
       } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int dw = e >> 1;
-          uint32_t lo, hi;
-          if (e & 1) {
-            lo = join_hi(vpre[it][1][dw], vpre[it][0][dw]);
-            hi = join_hi(vpre[it][3][dw], vpre[it][2][dw]);
-          } else {
-            lo = join_lo(vpre[it][1][dw], vpre[it][0][dw]);
-            hi = join_lo(vpre[it][3][dw], vpre[it][2][dw]);
-          }
-          lds_write8(Vt + vt_row<C::NCH>(c, e) * C::VP + slot4 * 8, u32x2{lo, hi});
-        }
+        lds_write16(Vs + (u / C::NCH) * C::VP + (u % C::NCH) * 16, vpre[it][0]);
       }
     }
   };
 
-  if (ntiles > 0) prefetch(kbeg);
+  // lane part of the transposed V read (16-bit): key row 4*g4 + r/4, head-dim
+  // columns 4*(r%4) of the 16-column block
+  const uint32_t vtr_lane = (4 * g4 + (n >> 2)) * C::VP + 4 * (n & 3) * 2;
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = kbeg + t * C::TK;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) prefetch(j0 + C::TK);
-
-    // ---- partial S^T over this wave's share of the head dim ----
-    if (wave < C::QSPLIT) {
+  auto compute = [&](const uint8_t* st, int j0) {
+    const uint8_t* Ks = st;
+    const uint8_t* Vs = st + C::K_BYTES;
+    // ---- S^T = K . Q^T (16-bit: every wave; fp32: split over the waves)
+    f32x4 sc[C::NBLK];
+    if constexpr (!C::F32) {
 #pragma unroll
       for (int blk = 0; blk < C::NBLK; ++blk) {
         f32x4 s = f32x4{};
-        const uint8_t* krow = Ks + (16 * blk + n) * C::KP + (4 * wave * C::NSW + g4) * 16;
+        const uint8_t* krow = Ks + (16 * blk + n) * C::KP + g4 * 16;
 #pragma unroll
         for (int ss = 0; ss < C::NSW; ++ss) s = mma16(T{}, lds_read16(krow + ss * 64), qreg[ss], s);
-        Sx[(wave * C::NBLK + blk) * 64 + lane] = s;
+        sc[blk] = s;
+      }
+    } else {
+      if (wave < C::QSPLIT) {
+#pragma unroll
+        for (int blk = 0; blk < C::NBLK; ++blk) {
+          f32x4 s = f32x4{};
+          const uint8_t* krow = Ks + (16 * blk + n) * C::KP + (4 * wave * C::NSW + g4) * 16;
+#pragma unroll
+          for (int ss = 0; ss < C::NSW; ++ss) s = mma16(T{}, lds_read16(krow + ss * 64), qreg[ss], s);
+          Sx[(wave * C::NBLK + blk) * 64 + lane] = s;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int blk = 0; blk < C::NBLK; ++blk) {
+        f32x4 s = Sx[blk * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < C::QSPLIT; ++w) s += Sx[(w * C::NBLK + blk) * 64 + lane];
+        sc[blk] = s;
       }
     }
-    __syncthreads();
-
-    // ---- full scores, scale, mask, tail, running max (identical in all waves)
-    f32x4 sc[C::NBLK];
+    // ---- scale, mask, key tail, running max (identical in all waves)
     float mx = kNegInf;
 #pragma unroll
     for (int blk = 0; blk < C::NBLK; ++blk) {
-      f32x4 s = Sx[blk * 64 + lane];
+      const int jb = j0 + 16 * blk + 4 * g4;
+      f32x4 mk = f32x4{};
+      if (MASK) {
+        if (mask_vec) {
+          const auto rm = make_rsrc(mrow + jb, (uint32_t)max(0, kend - jb) * 4);
+          mk = __builtin_bit_cast(f32x4, buf_load16(rm, 0));
+        } else {
 #pragma unroll
-      for (int w = 1; w < C::QSPLIT; ++w) s += Sx[(w * C::NBLK + blk) * 64 + lane];
+          for (int r = 0; r < 4; ++r) mk[r] = p.mask[(mrow - p.mask) + (int64_t)min(jb + r, kend - 1) * p.ms[3]];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int j = j0 + 16 * blk + 4 * g4 + r;
-        float x = s[r] * p.scale_log2;
-        if (MASK) {
-          const int jj = j < kend ? j : kend - 1;
-          const int hh = head_ok ? hq : hk * p.group;
-          x += kLog2e * p.mask[b * p.ms[0] + hh * p.ms[1] + (int64_t)jj * p.ms[3]];
-        }
-        x = j < kend ? x : kNegInf;
+        float x = sc[blk][r] * p.scale_log2;
+        if (MASK) x += kLog2e * mk[r];
+        x = jb + r < kend ? x : kNegInf;
         sc[blk][r] = x;
         mx = fmaxf(mx, x);
       }
     }
     mx = fmaxf(mx, xor16(mx));
-    mx = fmaxf(mx, xor32(mx));
+    mx = max_xor32(mx);
     const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == kNegInf ? 0.f : m_new;
-    const float corr = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    l_run *= corr;
+    if (__any(m_new > m_run)) {
+      const float corr = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= corr;
 #pragma unroll
-    for (int i = 0; i < C::NOB; ++i) acc[i] *= corr;
+      for (int i = 0; i < C::NOB; ++i) acc[i] *= corr;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
 #pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) {
+    for (int blk = 0; blk < C::NBLK; ++blk)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float pr = fast_exp2(sc[blk][r] - m_use);
         sc[blk][r] = pr;
         l_run += pr;
       }
-    }
 
-    // ---- O^T += V^T . P^T on this wave's rows ----
+    // ---- O^T += V^T . P^T on this wave's rows
     if constexpr (C::F32) {
 #pragma unroll
       for (int blk = 0; blk < C::NBLK; ++blk) {
-        u32x4 pb = {as_uint(sc[blk][0]), as_uint(sc[blk][1]),
-                    as_uint(sc[blk][2]), as_uint(sc[blk][3])};
+        const u32x4 pb = {as_uint(sc[blk][0]), as_uint(sc[blk][1]), as_uint(sc[blk][2]), as_uint(sc[blk][3])};
 #pragma unroll
         for (int i = 0; i < C::NOB; ++i) {
           const int row = 16 * (wave * C::NOB + i) + n;
-          acc[i] = mma16(T{}, lds_read16(Vt + row * C::VP + (16 * blk + 4 * g4) * 4), pb, acc[i]);
+          acc[i] = mma16(T{}, lds_read16(Vs + row * C::VP + (16 * blk + 4 * g4) * 4), pb, acc[i]);
         }
       }
     } else {
+      // k-slot 8*g4 + 4a + c <-> key 16a + 4*g4 + c of the 32-key pair pp
 #pragma unroll
       for (int pp = 0; pp < C::NBLK / 2; ++pp) {
+        u32x4 hi, lo;
         if constexpr (std::is_same<T, TBF16>::value) {
           // bf16 P carries 8 significant bits: feed P = hi + lo (the matrix
           // cores have ample headroom in this bandwidth-bound kernel)
-          u32x4 hi, lo;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             uint32_t h, l;
@@ -264,42 +286,64 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
             hi[e] = h;
             lo[e] = l;
           }
-#pragma unroll
-          for (int i = 0; i < C::NOB; ++i) {
-            const int row = 16 * (wave * C::NOB + i) + n;
-            const u32x4 va = lds_read16(Vt + row * C::VP + (32 * pp + 8 * g4) * 2);
-            acc[i] = mma16(T{}, va, hi, acc[i]);
-            acc[i] = mma16(T{}, va, lo, acc[i]);
-          }
         } else {
-          u32x4 pb = {T::pack2(sc[2 * pp][0], sc[2 * pp][1]), T::pack2(sc[2 * pp][2], sc[2 * pp][3]),
-                      T::pack2(sc[2 * pp + 1][0], sc[2 * pp + 1][1]),
-                      T::pack2(sc[2 * pp + 1][2], sc[2 * pp + 1][3])};
 #pragma unroll
-          for (int i = 0; i < C::NOB; ++i) {
-            const int row = 16 * (wave * C::NOB + i) + n;
-            acc[i] = mma16(T{}, lds_read16(Vt + row * C::VP + (32 * pp + 8 * g4) * 2), pb, acc[i]);
-          }
+          for (int e = 0; e < 4; ++e)
+            hi[e] = cvt_pk(T{}, sc[2 * pp + (e >> 1)][2 * (e & 1)], sc[2 * pp + (e >> 1)][2 * (e & 1) + 1]);
+        }
+        const uint8_t* vb = Vs + vtr_lane + 32 * pp * C::VP;
+#pragma unroll
+        for (int i = 0; i < C::NOB; ++i) {
+          const int d0 = 16 * (wave * C::NOB + i);
+          const u32x2 a0 = lds_read_tr16(vb + d0 * 2);
+          const u32x2 a1 = lds_read_tr16(vb + 16 * C::VP + d0 * 2);
+          const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
+          acc[i] = mma16(T{}, va, hi, acc[i]);
+          if constexpr (std::is_same<T, TBF16>::value) acc[i] = mma16(T{}, va, lo, acc[i]);
         }
       }
+    }
+  };
+
+  if (ntiles > 0) {
+    prefetch(kbeg);
+    if constexpr (C::STAGES == 2) store_tile(smem);
+  }
+  if constexpr (C::STAGES == 2) {
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const int j0 = kbeg + t * C::TK;
+      if (t + 1 < ntiles) prefetch(j0 + C::TK);
+      compute(smem + (t & 1) * C::STAGE, j0);
+      if (t + 1 < ntiles) store_tile(smem + ((t + 1) & 1) * C::STAGE);
+      __syncthreads();
+    }
+  } else {
+    for (int t = 0; t < ntiles; ++t) {
+      const int j0 = kbeg + t * C::TK;
+      __syncthreads();
+      store_tile(smem);
+      __syncthreads();
+      if (t + 1 < ntiles) prefetch(j0 + C::TK);
+      compute(smem, j0);
     }
   }
 
   // ---- epilogue ----
   float l_tot = l_run + xor16(l_run);
-  l_tot += xor32(l_tot);
+  l_tot = sum_xor32(l_tot);
   const int64_t bh = (int64_t)b * p.Hq + hq;
+  auto out_d = [&](int i, int r) {
+    const int rho = 16 * (wave * C::NOB + i) + 4 * g4 + r;
+    return C::F32 ? vt_row_to_d<C::NCH, C::VEC>(rho) : rho;
+  };
   if constexpr (SPLIT) {
     if (head_ok) {
       float* po = p.part_o + (bh * p.nsplit + split) * D;
 #pragma unroll
-      for (int i = 0; i < C::NOB; ++i) {
+      for (int i = 0; i < C::NOB; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rho = 16 * (wave * C::NOB + i) + 4 * g4 + r;
-          po[vt_row_to_d<C::NCH, C::VEC>(rho)] = acc[i][r];
-        }
-      }
+        for (int r = 0; r < 4; ++r) po[out_d(i, r)] = acc[i][r];
       if (wave == 0 && g4 == 0) {
         float* pml = p.part_ml + (bh * p.nsplit + split) * 2;
         pml[0] = m_run;
@@ -309,7 +353,273 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
   } else {
     float M = m_run, Ltot = l_tot;
     if (p.sinks) {
-      const float sk = p.sinks[head_ok ? hq : 0] * kLog2e;
+      const float sk = p.sinks[hq] * kLog2e;
+      M = fmaxf(m_run, sk);
+      if (M != kNegInf) Ltot = l_tot * fast_exp2(m_run - M) + fast_exp2(sk - M);
+    }
+    float so = 0.f, lse = kNegInf;
+    if (M != kNegInf && Ltot > 0.f) {
+      so = (p.sinks ? fast_exp2(m_run - M) : 1.f) / Ltot;
+      lse = (M + fast_log2(Ltot)) * kLn2;
+    }
+    if (head_ok) {
+      S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1];
+#pragma unroll
+      for (int i = 0; i < C::NOB; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) orow[out_d(i, r)] = T::from_f32(acc[i][r] * so);
+      if (p.lse && wave == 0 && g4 == 0) p.lse[bh] = lse;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit decode: K / V stream HBM -> LDS by direct (VGPR-free) buffer loads
+// into a ring of NST tile stages; a wave waits only for its own loads of the
+// tile it is about to use, so NST - 2 further tiles stay in flight while one
+// is consumed.  Rows are stored unpadded (the direct loads fill 1 KiB lines)
+// with 16-byte chunks XOR-swizzled by row, which keeps both the Q.K^T operand
+// reads (16 rows, one chunk) and the transposed V reads (16 rows, two chunks)
+// free of bank conflicts.
+// ---------------------------------------------------------------------------
+#ifndef SDPA_DECODE16_TK128
+#define SDPA_DECODE16_TK128 64  // keys per tile at D <= 128
+#endif
+#ifndef SDPA_DECODE16_STAGES
+#define SDPA_DECODE16_STAGES 2  // ring stages at D <= 128
+#endif
+#ifndef SDPA_DECODE16_STAGES_LARGE
+#define SDPA_DECODE16_STAGES_LARGE 2  // ring stages at D >= 256 (32 KiB stages)
+#endif
+template <int D>
+struct Dec16 {
+  static constexpr int RB = D * 2;                 // row bytes
+  static constexpr int NCH = D / 8;                // 16-byte chunks per row
+  static constexpr int TK = D >= 512 ? 16 : (D >= 256 ? 32 : SDPA_DECODE16_TK128 * 128 / D);
+  static constexpr int TILE = TK * RB;             // bytes of the K (or V) tile
+  static constexpr int NST = D >= 256 ? SDPA_DECODE16_STAGES_LARGE : SDPA_DECODE16_STAGES;
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int LINES = TILE / 1024;        // 1 KiB load lines per K (or V) tile
+  static constexpr int LPW = 2 * LINES / kWaves;   // load instructions per wave per tile
+  static constexpr int NBLK = TK / 16;
+  static constexpr int NQ = D / 32;                // Q vectors per lane
+  static constexpr int NOB = D / 16 / kWaves;      // O^T row blocks per wave
+  static_assert(LINES % kWaves == 0 && LINES >= kWaves, "tile lines");
+  static_assert(NST >= 2 && (NST - 2) * LPW < 64, "ring depth");
+};
+
+// chunk swizzle of a row (both K and V): low chunk bits ^= f(row)
+template <int NCH>
+__device__ constexpr int chunk_swz(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & (NCH - 1)); }
+
+template <class T, int D, bool MASK, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
+  using C = Dec16<D>;
+  using S = uint16_t;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NST * C::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 15;
+  const int g4 = lane >> 4;
+
+  const int split = blockIdx.x % p.nsplit;
+  const int bk = blockIdx.x / p.nsplit;
+  const int hk = bk % p.Hkv;
+  const int b = bk / p.Hkv;
+  const bool head_ok = n < p.group;
+  const int hq = hk * p.group + (head_ok ? n : 0);
+
+  const int kbeg = split * p.split_len;
+  const int kend = min(p.Lk, kbeg + p.split_len);
+  const int ntiles = kend > kbeg ? (kend - kbeg + C::TK - 1) / C::TK : 0;
+
+  const S* kp = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
+  const S* vp = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
+
+  // Q^T operand: vector s = chunk 4s + g4 of the head row
+  u32x4 qreg[C::NQ];
+  {
+    const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1];
+#pragma unroll
+    for (int s = 0; s < C::NQ; ++s) {
+      const u32x4 v = ldg16_cached(row + (4 * s + g4) * 8);
+      qreg[s] = head_ok ? v : u32x4{0, 0, 0, 0};
+    }
+  }
+  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] : nullptr;
+
+  // ---- per-lane direct-load offsets (fixed across tiles): wave w issues
+  //      lines w, w + 4, ...; lines [0, LINES) are K, the rest V
+  uint32_t voff[C::LPW];
+#pragma unroll
+  for (int i = 0; i < C::LPW; ++i) {
+    const int ln = (wave + kWaves * i) % C::LINES;
+    const int pos = ln * 64 + lane;                 // 16-byte slot within the tile
+    const int row = pos / C::NCH, pch = pos % C::NCH;
+    const int lch = pch ^ chunk_swz<C::NCH>(row);
+    const int64_t stride = (wave + kWaves * i) < C::LINES ? p.ks[2] : p.vs[2];
+    voff[i] = (uint32_t)(row * stride * 2 + lch * 16);
+  }
+  auto valid_bytes = [&](int j0, int64_t stride) -> uint32_t {
+    const int64_t nb = (int64_t)(kend - j0 - 1) * stride * 2 + D * 2;
+    return nb > 0xffffffffLL ? 0xffffffffu : (uint32_t)nb;
+  };
+  auto issue = [&](int t) {
+    if (t >= ntiles) return;
+    const int j0 = kbeg + t * C::TK;
+    const auto rk = make_rsrc(kp + (int64_t)j0 * p.ks[2], valid_bytes(j0, p.ks[2]));
+    const auto rv = make_rsrc(vp + (int64_t)j0 * p.vs[2], valid_bytes(j0, p.vs[2]));
+    uint8_t* st = ring + (t % C::NST) * C::STAGE;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) {
+      const int gl = wave + kWaves * i;
+      if (i < C::LINES / kWaves) buf_load16_lds(rk, st + gl * 1024, voff[i]);
+      else buf_load16_lds(rv, st + C::TILE + (gl - C::LINES) * 1024, voff[i]);
+    }
+  };
+
+  // ---- per-lane LDS read offsets
+  const int swk = chunk_swz<C::NCH>(n);                     // K rows 16 blk + n
+  const int vrow = 4 * g4 + (n >> 2);                       // V rows 16 blk + vrow
+  const int swv = chunk_swz<C::NCH>(vrow);
+  const uint32_t vlane = vrow * C::RB + (n & 1) * 8;
+
+  f32x4 acc[C::NOB];
+#pragma unroll
+  for (int i = 0; i < C::NOB; ++i) acc[i] = f32x4{};
+  float m_run = kNegInf, l_run = 0.f;
+
+  // mask values for tile t, loaded one tile ahead
+  auto load_mask = [&](int t, f32x4* mk) {
+#pragma unroll
+    for (int blk = 0; blk < C::NBLK; ++blk) {
+      const int jb = kbeg + t * C::TK + 16 * blk + 4 * g4;
+      const float* mp = mrow + (int64_t)jb * p.ms[3];
+      if (p.ms[3] == 1 && jb + 3 < kend && (((uintptr_t)mp) & 15) == 0) {
+        mk[blk] = *(const f32x4*)mp;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mk[blk][r] = mrow[(int64_t)max(kbeg, min(jb + r, kend - 1)) * p.ms[3]];
+      }
+    }
+  };
+  f32x4 mk_next[C::NBLK];
+  if (MASK && ntiles > 0) load_mask(0, mk_next);
+
+#pragma unroll
+  for (int t = 0; t < C::NST - 1; ++t) issue(t);
+
+  for (int t = 0; t < ntiles; ++t) {
+    // this wave's loads of tile t have landed once at most `rem` later tiles remain
+    const int rem = min(C::NST - 2, ntiles - 1 - t);
+    if constexpr (C::NST >= 4) { if (rem >= 2) wait_vmcnt<2 * C::LPW>(); }
+    if constexpr (C::NST >= 3) { if (rem == 1) wait_vmcnt<C::LPW>(); }
+    if (rem <= 0) wait_vmcnt<0>();
+    lds_barrier();  // ... and every wave's; tile t - 1 is no longer read
+    const int j0 = kbeg + t * C::TK;
+    // this tile's mask values were loaded in the previous iteration; the next
+    // tile's are issued before the direct loads, so waiting for them never
+    // waits for those
+    f32x4 mk[C::NBLK];
+    if (MASK) {
+#pragma unroll
+      for (int blk = 0; blk < C::NBLK; ++blk) mk[blk] = mk_next[blk];
+      if (t + 1 < ntiles) load_mask(t + 1, mk_next);
+    }
+    issue(t + C::NST - 1);
+
+    const uint8_t* Ks = ring + (t % C::NST) * C::STAGE;
+    const uint8_t* Vs = Ks + C::TILE;
+    // ---- S^T = K . Q^T
+    f32x4 sc[C::NBLK];
+#pragma unroll
+    for (int blk = 0; blk < C::NBLK; ++blk) {
+      f32x4 s = f32x4{};
+      const uint8_t* krow = Ks + (16 * blk + n) * C::RB;
+#pragma unroll
+      for (int ss = 0; ss < C::NQ; ++ss)
+        s = mma16(T{}, lds_read16(krow + ((4 * ss + g4) ^ swk) * 16), qreg[ss], s);
+      sc[blk] = s;
+    }
+    // ---- scale, mask, key tail, running max
+    float mx = kNegInf;
+#pragma unroll
+    for (int blk = 0; blk < C::NBLK; ++blk) {
+      const int jb = j0 + 16 * blk + 4 * g4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float x = sc[blk][r] * p.scale_log2;
+        if (MASK) x += kLog2e * mk[blk][r];
+        x = jb + r < kend ? x : kNegInf;
+        sc[blk][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, xor16(mx));
+    mx = max_xor32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__any(m_new > m_run)) {
+      const float corr = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+      l_run *= corr;
+#pragma unroll
+      for (int i = 0; i < C::NOB; ++i) acc[i] *= corr;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    // ---- O^T += V^T . P^T, 16 keys per step (k-slot 4 g4 + e <-> key 4 g4 + e)
+#pragma unroll
+    for (int blk = 0; blk < C::NBLK; ++blk) {
+      float pr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pr[r] = fast_exp2(sc[blk][r] - m_use);
+        l_run += pr[r];
+      }
+      u32x2 hi, lo;
+      if constexpr (std::is_same<T, TBF16>::value) {
+        // bf16 P carries 8 significant bits: P = hi + lo (the matrix cores
+        // have ample headroom in this bandwidth-bound kernel)
+        uint32_t h0, l0, h1, l1;
+        T::split2(pr[0], pr[1], h0, l0);
+        T::split2(pr[2], pr[3], h1, l1);
+        hi = u32x2{h0, h1};
+        lo = u32x2{l0, l1};
+      } else {
+        hi = u32x2{cvt_pk(T{}, pr[0], pr[1]), cvt_pk(T{}, pr[2], pr[3])};
+      }
+      const uint8_t* vb = Vs + 16 * blk * C::RB + vlane;
+#pragma unroll
+      for (int i = 0; i < C::NOB; ++i) {
+        const int lch = 2 * (wave * C::NOB + i) + ((n >> 1) & 1);  // chunk of columns d0 + 4(n%4)
+        const u32x2 va = lds_read_tr16(vb + ((lch ^ swv) * 16));
+        acc[i] = mma16k16(T{}, va, hi, acc[i]);
+        if constexpr (std::is_same<T, TBF16>::value) acc[i] = mma16k16(T{}, va, lo, acc[i]);
+      }
+    }
+  }
+
+  // ---- epilogue (identical in every wave; each writes its rows of O)
+  float l_tot = l_run + xor16(l_run);
+  l_tot = sum_xor32(l_tot);
+  const int64_t bh = (int64_t)b * p.Hq + hq;
+  if constexpr (SPLIT) {
+    if (head_ok) {
+      float* po = p.part_o + (bh * p.nsplit + split) * D;
+#pragma unroll
+      for (int i = 0; i < C::NOB; ++i)
+        *(f32x4*)(po + 16 * (wave * C::NOB + i) + 4 * g4) = acc[i];
+      if (wave == 0 && g4 == 0) {
+        float* pml = p.part_ml + (bh * p.nsplit + split) * 2;
+        pml[0] = m_run;
+        pml[1] = l_tot;
+      }
+    }
+  } else {
+    float M = m_run, Ltot = l_tot;
+    if (p.sinks) {
+      const float sk = p.sinks[hq] * kLog2e;
       M = fmaxf(m_run, sk);
       if (M != kNegInf) Ltot = l_tot * fast_exp2(m_run - M) + fast_exp2(sk - M);
     }
@@ -322,11 +632,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_kernel(AttnParams p) {
       S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1];
 #pragma unroll
       for (int i = 0; i < C::NOB; ++i) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int rho = 16 * (wave * C::NOB + i) + 4 * g4 + r;
-          orow[vt_row_to_d<C::NCH, C::VEC>(rho)] = T::from_f32(acc[i][r] * so);
-        }
+        const f32x4 o = acc[i] * so;
+        *(u32x2*)(orow + 16 * (wave * C::NOB + i) + 4 * g4) =
+            u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
       }
       if (p.lse && wave == 0 && g4 == 0) p.lse[bh] = lse;
     }
@@ -407,17 +715,28 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)p.nsplit * p.Hkv * p.B));
   const dim3 block(kThreads);
   const bool mask = p.mask != nullptr;
+  constexpr bool F32 = std::is_same<T, TF32>::value;
   if (p.nsplit > 1) {
-    if (mask) hipLaunchKernelGGL((decode_kernel<T, D, true, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, false, true>), grid, block, 0, s, p);
+    if constexpr (F32) {
+      if (mask) hipLaunchKernelGGL((decode_f32_kernel<T, D, true, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode_f32_kernel<T, D, false, true>), grid, block, 0, s, p);
+    } else {
+      if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode16_kernel<T, D, false, true>), grid, block, 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nslice = D / (D < kMergeCols ? D : kMergeCols);
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)p.B * p.Hq * nslice)),
                        dim3(kMergeThreads), 0, s, p);
   } else {
-    if (mask) hipLaunchKernelGGL((decode_kernel<T, D, true, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<T, D, false, false>), grid, block, 0, s, p);
+    if constexpr (F32) {
+      if (mask) hipLaunchKernelGGL((decode_f32_kernel<T, D, true, false>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode_f32_kernel<T, D, false, false>), grid, block, 0, s, p);
+    } else {
+      if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, false>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode16_kernel<T, D, false, false>), grid, block, 0, s, p);
+    }
   }
   return hipGetLastError();
 }
@@ -435,8 +754,13 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
 }  // namespace
 
 int decode_tile_keys(int dtype, int D) {
-  const bool f32 = dtype == SDPA_F32;
-  return f32 ? (D >= 256 ? 16 : 4096 / D) : (D >= 256 ? 32 : 8192 / D);
+  if (dtype == SDPA_F32) return D >= 256 ? 16 : SDPA_DECODE_TILE_BYTES / (8 * D);
+  switch (D) {
+    case 64: return Dec16<64>::TK;
+    case 128: return Dec16<128>::TK;
+    case 256: return Dec16<256>::TK;
+    default: return Dec16<512>::TK;
+  }
 }
 
 hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s) {

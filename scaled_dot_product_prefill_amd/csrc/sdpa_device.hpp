@@ -104,6 +104,16 @@ __device__ inline f32x16 mma32(TF32, u32x4 a, u32x4 b, f32x16 c) {
   return c;
 }
 
+// 16x16x16: A m = l%16, k = 4*(l/16)+e; B n = l%16, k = 4*(l/16)+e (e = 0..3)
+__device__ inline f32x4 mma16k16(TBF16, u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, a),
+                                                   __builtin_bit_cast(bf16x4, b), c, 0, 0, 0);
+}
+__device__ inline f32x4 mma16k16(TF16, u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                               __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
 __device__ inline f32x4 mma16(TBF16, u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -145,6 +155,27 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t by
 }
 __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+}
+
+// Direct HBM -> LDS load: lane l's 16 bytes at voff land at lds + 16*l (lds is
+// wave-uniform, written to M0).  Completion is tracked by vmcnt only.
+__device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)(lds), 16, (int)voff, 0, 0, 0);
+}
+
+// Workgroup barrier without the implied memory fence of __syncthreads: the
+// fence would wait for every outstanding load (vmcnt(0)), including direct
+// LDS loads of later tiles.  Callers wait for what they need explicitly.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane r names 4 consecutive
