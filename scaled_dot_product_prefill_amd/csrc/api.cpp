@@ -40,6 +40,7 @@ int ok() {
 int elem_bytes(int dtype) { return dtype == SDPA_F32 ? 4 : 2; }
 
 constexpr int64_t kMaxInt = 2147483647LL;
+constexpr int64_t kMaxRowBytes = 1LL << 23;  // 8 MiB: 256 rows stay below 2^31 bytes
 
 struct Extent {
   uintptr_t lo = 0, hi = 0;  // [lo, hi)
@@ -100,6 +101,9 @@ int check_common(const sdpa_args* a) {
     }
   }
   if (a->o_stride[2] < a->D) return fail(SDPA_ERR_ARG, "o rows overlap (o_stride[2] < D)");
+  // key/value tiles are addressed with 32-bit byte offsets from the tile's first row
+  if (a->k_stride[2] * es > kMaxRowBytes || a->v_stride[2] * es > kMaxRowBytes)
+    return fail(SDPA_ERR_UNSUPPORTED, "k/v row stride above %lld bytes", (long long)kMaxRowBytes);
   if (a->mask) {
     if ((uintptr_t)a->mask % 4 != 0) return fail(SDPA_ERR_ALIGN, "mask is not 4-byte aligned");
     for (int d = 0; d < 4; ++d)

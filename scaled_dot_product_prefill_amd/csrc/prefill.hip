@@ -342,40 +342,103 @@ template <int D>
 struct Cfg16 {
   static constexpr int BN = 64;                 // keys per tile
   static constexpr int NKB = BN / 32;           // 32-key blocks per tile
+  static constexpr int RB = D * 2;              // row bytes (unpadded)
   static constexpr int NCH = D / 8;             // 16-byte chunks per row
-  static constexpr int KP = D * 2 + 16;         // K row pitch (bytes)
-  static constexpr int VP = D * 2 + 64;         // V row pitch (bytes): 4 rows tile 256 B
-  static constexpr int STAGE = BN * KP + BN * VP;
+  static constexpr int TILE = BN * RB;          // bytes of one K (or V) tile
+  static constexpr int LINES = TILE / 1024;     // 1 KiB direct-load lines per tile
+  static constexpr int LPW = LINES / kWaves;    // lines per wave per tile (K or V)
   static constexpr int NQ = D / 16;             // 16-byte Q vectors per lane
-  static constexpr int IT = BN * NCH / kThreads;  // K (and V) chunks per thread
   static constexpr int NMB = D / 32;            // 32-row blocks of O^T
   // D = 64: the per-row sum of P runs on the matrix cores as one more
   // 32-row block whose V^T rows are all ones (the VALU is the scarcer unit)
   static constexpr bool SUM_MFMA = (D == 64);
-  static_assert(IT >= 1 && BN * NCH % kThreads == 0, "tile split");
+  static_assert(LINES % kWaves == 0, "tile lines");
+  static_assert((256 / NCH) % 16 == 0, "swizzle period");
 };
 
-// The running max is only moved (and O, l rescaled) when a row's tile max
+// The reference max is only moved (and O, l rescaled) when a row's tile max
 // exceeds it by more than this many log2 units; probabilities then stay
 // below 2^8, and O = sum(p v) / sum(p) is unchanged by which max is used.
 constexpr float kRescaleSlack = 8.f;
 
-// Per wave and tile (BN = 64 keys, 32 queries):
-//   S^T = K . Q^T        (NKB x NQ 32x32x16 matrix-core ops, K from LDS)
-//   online softmax       (in-lane over 32 keys, one exchange with lane ^ 32)
-//   O^T += V^T . P^T     (V^T read with ds_read_b64_tr_b16 from row-major V)
-// Interior tiles (every key visible, no mask) take a path with no per-element
-// visibility test; the scale is folded into the exponent, exp2(s*c - m).
-// The running max only rescales O and l when it grows for some lane.
+// 16-byte chunk swizzles of the unpadded LDS rows (low chunk bits ^= f(row)):
+// K: the Q.K^T operand read touches 16 consecutive rows in one chunk;
+// V: a transposed read touches 8 rows x 4 consecutive chunks.
+template <int NCH>
+__device__ constexpr int swz_k(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & 7); }
+template <int NCH>
+__device__ constexpr int swz_v(int row) { return NCH >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
+
+// Row sum of two packed 16-bit probabilities, accumulated in fp32.
+__device__ inline float dot2_ones(TF16, uint32_t pk, float acc) {
+  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pk), __builtin_bit_cast(h2, 0x3C003C00u), acc, false);
+}
+__device__ inline float dot2_ones(TBF16, uint32_t pk, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                         acc, false);
+}
+
+#ifndef SDPA_PF_SCHED
+#define SDPA_PF_SCHED 0
+#endif
+// Instruction order of one steady-state tile, per matrix-core op: S(t+1) ops
+// each take a few exponentials and VALU ops of P(t) (the first key half), the
+// first half of the P(t).V(t) ops the exponentials of the second key half,
+// the second half the row max of S(t+1); LDS operand reads run a few ahead.
+// Neither unit waits for a long run of the other.
+template <int D>
+__device__ __forceinline__ void sched_steady() {
+#if SDPA_PF_SCHED
+  constexpr int nQK = 2 * (D / 16);
+  constexpr int nPV = 4 * (D / 32) + (D == 64 ? 4 : 0);
+  constexpr int nPVa = nPV / 2, nPVb = nPV - nPVa;
+  constexpr int kT = 0x400, kV = 0x002, kM = 0x008, kD = 0x100;
+  constexpr int tq = D == 64 ? 2 : 1, vq = D == 64 ? 4 : 3;
+  constexpr int ta = D == 64 ? 3 : 2, va = D == 64 ? 4 : 3;
+  constexpr int vb = D == 64 ? 4 : 3;
+  __builtin_amdgcn_sched_group_barrier(kD, 4, 0);
+#pragma unroll
+  for (int i = 0; i < nQK; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kM, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kT, tq, 0);
+    __builtin_amdgcn_sched_group_barrier(kV, vq, 0);
+    __builtin_amdgcn_sched_group_barrier(kD, 1, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < nPVa; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kM, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kT, ta, 0);
+    __builtin_amdgcn_sched_group_barrier(kV, va, 0);
+    __builtin_amdgcn_sched_group_barrier(kD, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < nPVb; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kM, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kV, vb, 0);
+    __builtin_amdgcn_sched_group_barrier(kD, 2, 0);
+  }
+#endif
+}
+
+// Per wave (32 queries) and tile (64 keys), software-pipelined:
+//   S(t+1) = K(t+1) . Q^T  on the matrix cores  ||  P(t) = exp2(S(t) c - m)  on the VALU
+//   O^T   += V(t)^T . P(t)^T on the matrix cores  ||  row max of S(t+1) on the VALU
+// K and V tiles arrive by direct buffer -> LDS loads into two-stage rings, one
+// tile ahead, with one fence-free barrier per tile.  V^T is read with
+// ds_read_b64_tr_b16.  Interior tiles (every key visible to the whole
+// workgroup, no mask) skip per-element masking.
 template <class T, int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
+__device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   using C = Cfg16<D>;
   using S = uint16_t;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
+  uint8_t* const Kring = smem;               // stages 0, 1
+  uint8_t* const Vring = smem + 2 * C::TILE;  // stages 0, 1
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -393,7 +456,6 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
   // exponent scale c = |scale| log2(e); a negative scale is moved into Q
   const float c = fabsf(p.scale_log2);
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-
   u32x4 qreg[C::NQ];
   {
     const bool ok = my_i < p.Lq;
@@ -409,107 +471,92 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
   int kend = p.Lk;
   if (CAUSAL) kend = min(kend, i0 + kBM + p.causal_off);
   const int ntiles = kend > 0 ? (kend + C::BN - 1) / C::BN : 0;
-  const int wave_last_key = CAUSAL ? iw + 31 + p.causal_off : p.Lk - 1;
+  // tiles [0, n_int) have every key visible to every row of the workgroup
+  int n_int = 0;
+  if (!MASK) {
+    int full = p.Lk;
+    if (CAUSAL) full = min(full, i0 + 1 + p.causal_off);
+    n_int = full > 0 ? min(ntiles, full / C::BN) : 0;
+  }
   // bf16 probabilities carry 8 significant bits; rows that average few keys
   // would show that rounding directly in O, so such workgroups feed P.V with
   // P = hi + lo (two bf16 products).  Many-key rows average it away.
   const bool split_p = std::is_same<T, TBF16>::value && (MASK || kend <= 1024);
 
+  // ---- direct buffer -> LDS loads.  Wave w fills lines w, w + 4, ... of a
+  // tile; line i of a wave sits 256 / NCH rows below line 0 and both swizzles
+  // repeat every 16 rows: one per-lane offset plus a uniform step.
+  const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
+  const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
+  uint32_t koff, voff;
+  {
+    const int pos = wave * 64 + lane;  // 16-byte slot of line 0
+    const int row = pos / C::NCH, pch = pos % C::NCH;
+    koff = (uint32_t)(row * p.ks[2] * 2 + (pch ^ swz_k<C::NCH>(row)) * 16);
+    voff = (uint32_t)(row * p.vs[2] * 2 + (pch ^ swz_v<C::NCH>(row)) * 16);
+  }
+  const uint32_t krow = (uint32_t)(p.ks[2] * 2), vrow = (uint32_t)(p.vs[2] * 2);
+  const uint32_t kstep = (256 / C::NCH) * krow, vstep = (256 / C::NCH) * vrow;
+  // bytes of a tile that hold keys < Lk (rows past Lk read as zero)
+  auto tile_bytes = [&](int j0, uint32_t rowb) -> uint32_t {
+    const int rows = p.Lk - j0;
+    return rows >= C::BN ? 0xffffffffu : (uint32_t)(rows - 1) * rowb + C::RB;
+  };
+  auto issue = [&](const S* base, int64_t rs, uint32_t rowb, uint32_t off, uint32_t step, uint8_t* st,
+                   int t) {
+    const int j0 = t * C::BN;
+    const S* tb = base + (int64_t)j0 * rs;
+    const uint32_t nb = tile_bytes(j0, rowb);
+    const uint32_t la = lds_addr(st) + wave * 1024;
+#pragma unroll
+    for (int i = 0; i < C::LPW; ++i) dma16(tb, nb, la + kWaves * i * 1024, off, i * step);
+  };
+  auto issue_k = [&](int t, uint8_t* st) { issue(kbase, p.ks[2], krow, koff, kstep, st, t); };
+  auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, voff, vstep, st, t); };
+
+  // ---- per-lane LDS read offsets
+  const uint32_t k_lane = l32 * C::RB;                 // + (32 kb) rows
+  const int k_swz = swz_k<C::NCH>(l32);
+  const int r16 = lane & 15, dh = (lane >> 4) & 1;
+  const int v_row = 4 * g + (r16 >> 2);                // + (32 kb + 16 u + 8 a) rows
+  const int v_swz = swz_v<C::NCH>(v_row);
+  const uint32_t v_lane = v_row * C::RB + (r16 & 1) * 8;
+  const int v_ch = 2 * dh + ((r16 >> 1) & 1);          // + 4 mb
+
   f32x16 acc[C::NMB];
 #pragma unroll
   for (int mb = 0; mb < C::NMB; ++mb) acc[mb] = f32x16{};
   f32x16 lacc = f32x16{};  // row sums from the matrix cores (SUM_MFMA)
-  float m_run = kNegInf;  // reference max of the scaled scores (log2 units)
-  float l_run = 0.f;      // running sum over this lane's half of the keys
+  float m_run = kNegInf;   // reference max of the scaled scores (log2 units)
+  float l_run = 0.f;       // running sum over this lane's half of the keys
   constexpr uint32_t kOnes = std::is_same<T, TBF16>::value ? 0x3F803F80u : 0x3C003C00u;
   const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
-  auto rescale = [&](float corr) {
-#pragma unroll
-    for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
-    if constexpr (C::SUM_MFMA) lacc *= corr;
-    else l_run *= corr;
-  };
 
-  // ---- K / V tile loads: buffer resources clip the key range (loads past
-  //      the last key return zeros); per-thread byte offsets are fixed ----
-  const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
-  const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
-  uint32_t koff[C::IT], voff[C::IT], lds_off[C::IT];
-#pragma unroll
-  for (int it = 0; it < C::IT; ++it) {
-    const int u = tid + kThreads * it;
-    const int key = u / C::NCH, ch = u % C::NCH;
-    koff[it] = (uint32_t)(key * p.ks[2] * 2 + ch * 16);
-    voff[it] = (uint32_t)(key * p.vs[2] * 2 + ch * 16);
-    lds_off[it] = key * C::KP + ch * 16;
-  }
-  auto valid_bytes = [&](int j0, int64_t stride) -> uint32_t {
-    const int64_t n = (int64_t)(p.Lk - j0 - 1) * stride * 2 + D * 2;
-    return n > 0xffffffffLL ? 0xffffffffu : (uint32_t)n;
-  };
-  u32x4 kpre[C::IT], vpre[C::IT];
-  auto prefetch = [&](int j0) {
-    const auto rk = make_rsrc(kbase + (int64_t)j0 * p.ks[2], valid_bytes(j0, p.ks[2]));
-    const auto rv = make_rsrc(vbase + (int64_t)j0 * p.vs[2], valid_bytes(j0, p.vs[2]));
-#pragma unroll
-    for (int it = 0; it < C::IT; ++it) {
-      kpre[it] = buf_load16(rk, koff[it]);
-      vpre[it] = buf_load16(rv, voff[it]);
-    }
-  };
-  auto store = [&](uint8_t* st) {
-#pragma unroll
-    for (int it = 0; it < C::IT; ++it) {
-      lds_write16(st + lds_off[it], kpre[it]);
-      // V rows use the V pitch: the same (key, chunk) position
-      const int u = tid + kThreads * it;
-      lds_write16(st + C::BN * C::KP + (u / C::NCH) * C::VP + (u % C::NCH) * 16, vpre[it]);
-    }
-  };
-
-  // lane part of the transposed V read: row 4g + r/4, columns 16*dh + 4*(r%4)
-  const int r16 = lane & 15;
-  const int dh = (lane >> 4) & 1;
-  const uint32_t vtr_lane = (4 * g + (r16 >> 2)) * C::VP + (16 * dh + 4 * (r16 & 3)) * 2;
-
-  auto compute = [&](const uint8_t* st, int j0, auto edge_tag) {
-    constexpr bool EDGE = decltype(edge_tag)::value;
-    const uint8_t* Ks = st;
-    const uint8_t* Vs = st + C::BN * C::KP;
-    f32x16 sc[C::NKB];
+  auto qk = [&](const uint8_t* Kst, f32x16* sc) {
+    const uint8_t* Ks = Kst + k_lane;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
       sc[kb] = f32x16{};
-      const uint8_t* krow = Ks + (32 * kb + l32) * C::KP + g * 16;
 #pragma unroll
-      for (int s = 0; s < C::NQ; ++s) sc[kb] = mma32(T{}, lds_read16(krow + s * 32), qreg[s], sc[kb]);
+      for (int s = 0; s < C::NQ; ++s)
+        sc[kb] = mma32(T{}, lds_read16(Ks + 32 * kb * C::RB + (((2 * s + g) ^ k_swz) * 16)), qreg[s], sc[kb]);
     }
-    float m_use;
+  };
+  // row max of tile t (scaled log2 units), masking first on edge tiles
+  auto tile_max = [&](int t, f32x16* sc, auto edge_tag) -> float {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    float mx;
     if constexpr (!EDGE) {
-      // every key visible: max over raw scores, scale applied once per row
-      float mx = sc[0][0];
+      mx = sc[0][0];
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
       mx = max_xor32(mx) * c;
-      if (__any(mx > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        rescale(fast_exp2(m_run - m_new));
-        m_run = m_new;
-      }
-      m_use = m_run;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(fmaf(sc[kb][r], c, -m_use));
-          sc[kb][r] = pr;
-          if constexpr (!C::SUM_MFMA) l_run += pr;
-        }
     } else {
-      float mx = kNegInf;
+      const int j0 = t * C::BN;
       const int ii = my_i < p.Lq ? my_i : p.Lq - 1;
+      mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
@@ -526,93 +573,136 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
           mx = fmaxf(mx, x);
         }
       mx = max_xor32(mx);
-      if (__any(mx > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mx);
-        // rows that still see nothing (both -inf) keep corr = 1
-        rescale(m_new > m_run ? fast_exp2(m_run - m_new) : 1.f);
-        m_run = m_new;
-      }
-      m_use = m_run == kNegInf ? 0.f : m_run;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float pr = fast_exp2(sc[kb][r] - m_use);
-          sc[kb][r] = pr;
-          if constexpr (!C::SUM_MFMA) l_run += pr;
-        }
     }
-    // ---- O^T += V^T . P^T; k-step u of block kb covers keys 32kb + 16u + [0, 16):
-    //      B element e <-> key 16u + 8(e/4) + 4g + e%4 (the accumulator rows)
+    return mx;
+  };
+  // move the reference max when some row's tile max exceeds it by the slack
+  auto update_max = [&](float mx) {
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float corr = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+      if constexpr (C::SUM_MFMA) lacc *= corr;
+      else l_run *= corr;
+      m_run = m_new;
+    }
+  };
+  // P = exp2(S c - m) (interior) or exp2(S - m) (edge, already scaled), packed
+  // as the B operands of P.V: k-step u of block kb <-> accumulator rows 8u..8u+7.
+  // Without the split the row sum adds the packed (rounded) probabilities,
+  // the values P.V multiplies.
+  auto probs = [&](f32x16* sc, u32x4 (&hi)[C::NKB][2], u32x4 (&lo)[C::NKB][2], auto edge_tag,
+                   bool split) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
+    constexpr bool BF = std::is_same<T, TBF16>::value;
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 hi, lo;
-        bool two = false;
-        if constexpr (std::is_same<T, TBF16>::value) {
-          if (split_p) {
+      for (int r = 0; r < 16; ++r)
+        sc[kb][r] = EDGE ? fast_exp2(sc[kb][r] - m_use) : fast_exp2(fmaf(sc[kb][r], c, -m_use));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              uint32_t h, l;
-              T::split2(sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1], h, l);
-              hi[e] = h;
-              lo[e] = l;
-            }
-            two = true;
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = sc[kb][8 * u + 2 * e], p1 = sc[kb][8 * u + 2 * e + 1];
+          if (BF && split) {
+            uint32_t h, l;
+            TBF16::split2(p0, p1, h, l);
+            hi[kb][u][e] = h;
+            lo[kb][u][e] = l;
+            if constexpr (!C::SUM_MFMA) l_run += p0 + p1;
+          } else {
+            hi[kb][u][e] = cvt_pk(T{}, p0, p1);
+            if constexpr (!C::SUM_MFMA) l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
           }
         }
-        if (!two) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hi[e] = cvt_pk(T{}, sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1]);
-        }
-        const uint8_t* vb = Vs + vtr_lane + (32 * kb + 16 * u) * C::VP;
-#pragma unroll
-        for (int mb = 0; mb < C::NMB; ++mb) {
-          const u32x2 a0 = lds_read_tr16(vb + 64 * mb);
-          const u32x2 a1 = lds_read_tr16(vb + 8 * C::VP + 64 * mb);
-          const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
-          acc[mb] = mma32(T{}, va, hi, acc[mb]);
-          if (two) acc[mb] = mma32(T{}, va, lo, acc[mb]);
-        }
-        if constexpr (C::SUM_MFMA) {
-          lacc = mma32(T{}, ones, hi, lacc);
-          if (two) lacc = mma32(T{}, ones, lo, lacc);
-        }
-      }
     }
   };
+  auto pv = [&](const uint8_t* Vst, u32x4 (&hi)[C::NKB][2], u32x4 (&lo)[C::NKB][2], bool split) {
+    constexpr bool BF = std::is_same<T, TBF16>::value;
+    const uint8_t* Vs = Vst + v_lane;
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const uint8_t* vb = Vs + (32 * kb + 16 * u) * C::RB;
+#pragma unroll
+        for (int mb = 0; mb < C::NMB; ++mb) {
+          const uint32_t ch = ((4 * mb + v_ch) ^ v_swz) * 16;
+          const u32x2 a0 = lds_read_tr16(vb + ch);
+          const u32x2 a1 = lds_read_tr16(vb + 8 * C::RB + ch);
+          const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
+          acc[mb] = mma32(T{}, va, hi[kb][u], acc[mb]);
+          if (BF && split) acc[mb] = mma32(T{}, va, lo[kb][u], acc[mb]);
+        }
+        if constexpr (C::SUM_MFMA) {
+          lacc = mma32(T{}, ones, hi[kb][u], lacc);
+          if (BF && split) lacc = mma32(T{}, ones, lo[kb][u], lacc);
+        }
+      }
+  };
 
-  // Tiles [0, n_int) are interior for every wave of the workgroup (all keys
-  // visible to all 128 rows, no mask); they run a loop with a single path.
-  // The remaining tiles (causal diagonal, key tail, or every tile when a mask
-  // is given) run the masking path.
-  int n_int = 0;
-  if (!MASK) {
-    int last_full = p.Lk;                                   // keys [0, last_full) are in range
-    if (CAUSAL) last_full = min(last_full, i0 + 1 + p.causal_off);  // visible to row i0
-    n_int = last_full > 0 ? min(ntiles, last_full / C::BN) : 0;
-  }
+  // ---- pipeline.  Tile t lives in stage t & 1 of both rings.  Iteration t
+  // waits for K(t+1) and V(t) (issued one iteration earlier), then refills the
+  // stages that K(t) and V(t-1) occupied, whose last reads precede the barrier.
+  f32x16 sa[C::NKB], sb[C::NKB];
   if (ntiles > 0) {
-    prefetch(0);
-    store(smem);
+    issue_k(0, Kring);
+    if (ntiles > 1) issue_k(1, Kring + C::TILE);
+    issue_v(0, Vring);
+    wait_vmcnt<0>();
+    lds_barrier();
+    qk(Kring, sa);
+    update_max(0 < n_int ? tile_max(0, sa, std::false_type{}) : tile_max(0, sa, std::true_type{}));
   }
-  __syncthreads();
+  // steady state (tiles t, t+1 interior, tile t+2 exists, single bf16 P): no
+  // branch between the barrier and the max update, stage offsets fixed by
+  // the parity of t, so matrix-core and VALU work of the two tiles interleave
+  auto steady = [&](int t, auto par_tag, f32x16* cur, f32x16* nxt) {
+    constexpr int PAR = decltype(par_tag)::value;
+    wait_vmcnt<0>();
+    lds_barrier();
+    issue_v(t + 1, Vring + (PAR ^ 1) * C::TILE);
+    issue_k(t + 2, Kring + PAR * C::TILE);
+    u32x4 hi[C::NKB][2], lo[C::NKB][2];
+    qk(Kring + (PAR ^ 1) * C::TILE, nxt);          // matrix cores ...
+    probs(cur, hi, lo, std::false_type{}, false);  // ... while the VALU exponentiates
+    pv(Vring + PAR * C::TILE, hi, lo, false);
+    const float mx = tile_max(t + 1, nxt, std::false_type{});
+    sched_steady<D>();
+    update_max(mx);
+  };
+  auto general = [&](int t, auto edge_tag) {
+    const int par = t & 1;
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
+    if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
+    u32x4 hi[C::NKB][2], lo[C::NKB][2];
+    probs(sa, hi, lo, edge_tag, split_p);
+    pv(Vring + par * C::TILE, hi, lo, split_p);
+    if (t + 1 < ntiles) {
+      qk(Kring + (par ^ 1) * C::TILE, sa);
+      update_max(t + 1 < n_int ? tile_max(t + 1, sa, std::false_type{})
+                               : tile_max(t + 1, sa, std::true_type{}));
+    }
+  };
   int t = 0;
-  for (; t < n_int; ++t) {
-    const int j0 = t * C::BN;
-    if (t + 1 < ntiles) prefetch(j0 + C::BN);
-    compute(smem + (t & 1) * C::STAGE, j0, std::false_type{});
-    if (t + 1 < ntiles) store(smem + ((t + 1) & 1) * C::STAGE);
-    __syncthreads();
+  const int n_steady = split_p ? 0 : max(0, min(n_int - 1, ntiles - 2));
+  for (; t + 1 < n_steady; t += 2) {
+    steady(t, std::integral_constant<int, 0>{}, sa, sb);
+    steady(t + 1, std::integral_constant<int, 1>{}, sb, sa);
   }
-  for (; t < ntiles; ++t) {
-    const int j0 = t * C::BN;
-    if (t + 1 < ntiles) prefetch(j0 + C::BN);
-    if (j0 <= wave_last_key) compute(smem + (t & 1) * C::STAGE, j0, std::true_type{});
-    if (t + 1 < ntiles) store(smem + ((t + 1) & 1) * C::STAGE);
-    __syncthreads();
+  if (t < n_steady) {
+    steady(t, std::integral_constant<int, 0>{}, sa, sb);
+#pragma unroll
+    for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
+    ++t;
   }
+  for (; t < n_int; ++t) general(t, std::false_type{});
+  for (; t < ntiles; ++t) general(t, std::true_type{});
 
   // ---- epilogue ----
   const float l_tot = C::SUM_MFMA ? lacc[0] : sum_xor32(l_run);
@@ -642,6 +732,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
   }
 }
 
+// Two workgroups per CU; the masked variants keep a second score tile plus
+// the mask gathers live across the pipeline and get the whole register file.
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
+  prefill16_body<T, D, CAUSAL, false>(p);
+}
+template <class T, int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void prefill16_mask_kernel(AttnParams p) {
+  prefill16_body<T, D, CAUSAL, true>(p);
+}
+
 template <class T, int D>
 hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
   const int nqt = (p.Lq + kBM - 1) / kBM;
@@ -658,11 +759,11 @@ hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
     }
   } else {
     if (causal) {
-      if (mask) hipLaunchKernelGGL((prefill16_kernel<T, D, true, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((prefill16_kernel<T, D, true, false>), grid, block, 0, s, p);
+      if (mask) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill16_kernel<T, D, true>), grid, block, 0, s, p);
     } else {
-      if (mask) hipLaunchKernelGGL((prefill16_kernel<T, D, false, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((prefill16_kernel<T, D, false, false>), grid, block, 0, s, p);
+      if (mask) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, false>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill16_kernel<T, D, false>), grid, block, 0, s, p);
     }
   }
   return hipGetLastError();

@@ -159,9 +159,33 @@ __device__ inline u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
 
 // Direct HBM -> LDS load: lane l's 16 bytes at voff land at lds + 16*l (lds is
 // wave-uniform, written to M0).  Completion is tracked by vmcnt only.
-__device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+__device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff,
+                                      uint32_t soff = 0) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(
-      r, (__attribute__((address_space(3))) void*)(lds), 16, (int)voff, 0, 0, 0);
+      r, (__attribute__((address_space(3))) void*)(lds), 16, (int)voff, (int)soff, 0, 0);
+}
+
+// The same direct load, issued so that the compiler does not track it: its
+// wait-count pass otherwise cannot tell that a later LDS read of a different
+// ring stage is independent of the load and waits for every load in flight
+// (vmcnt(0)) before that read, which serialises the prefetch.  Callers order
+// it themselves: wait_vmcnt<> then lds_barrier() before reading the stage.
+// The descriptor is built by hand (base, stride 0, num_records, the same
+// format word as make_rsrc); M0 holds the wave-uniform LDS destination, set
+// at least one wait state before the load.
+__device__ inline void dma16(const void* base, uint32_t bytes, uint32_t lds_addr, uint32_t voff,
+                             uint32_t soff) {
+  const uint64_t a = (uint64_t)base;
+  const u32x4 rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, %2 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr));
+}
+// LDS byte address of a pointer into shared memory
+__device__ inline uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
 }
 
 // Workgroup barrier without the implied memory fence of __syncthreads: the
