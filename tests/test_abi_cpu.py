@@ -159,9 +159,9 @@ def test_split_plan(lib):
     a = _sizes(8, 32, 8, 131072, 128, sdpa.BF16)
     assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 16
     assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 0) == 8 * 32 * 16 * 130 * 4
-    # GQA-8 D=512, B=1, Lk=1024: one 32-key tile per split
+    # GQA-8 D=512, B=1, Lk=1024: one 16-key tile per split
     a = _sizes(1, 32, 4, 1024, 512, sdpa.F16)
-    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 32
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
     # forced counts and single pass
     assert lib.sdpa_decode_num_splits(ctypes.byref(a), 1) == 1
     assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 1) == 0
