@@ -420,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g4 = lane >> 4;
 
@@ -469,14 +469,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   auto issue = [&](int t) {
     if (t >= ntiles) return;
     const int j0 = kbeg + t * C::TK;
-    const auto rk = make_rsrc(kp + (int64_t)j0 * p.ks[2], valid_bytes(j0, p.ks[2]));
-    const auto rv = make_rsrc(vp + (int64_t)j0 * p.vs[2], valid_bytes(j0, p.vs[2]));
-    uint8_t* st = ring + (t % C::NST) * C::STAGE;
+    const S* tk = kp + (int64_t)j0 * p.ks[2];
+    const S* tv = vp + (int64_t)j0 * p.vs[2];
+    const uint32_t nk = valid_bytes(j0, p.ks[2]), nv = valid_bytes(j0, p.vs[2]);
+    const uint32_t st = lds_addr(ring) + (t % C::NST) * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
       const int gl = wave + kWaves * i;
-      if (i < C::LINES / kWaves) buf_load16_lds(rk, st + gl * 1024, voff[i]);
-      else buf_load16_lds(rv, st + C::TILE + (gl - C::LINES) * 1024, voff[i]);
+      if (i < C::LINES / kWaves) dma16(tk, nk, st + gl * 1024, voff[i], 0);
+      else dma16(tv, nv, st + C::TILE + (gl - C::LINES) * 1024, voff[i], 0);
     }
   };
 

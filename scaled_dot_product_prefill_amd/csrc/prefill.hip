@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
 // ---------------------------------------------------------------------------
 // 16-bit inputs (fp16 / bf16)
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int NW>
 struct Cfg16 {
   static constexpr int BN = 64;                 // keys per tile
   static constexpr int NKB = BN / 32;           // 32-key blocks per tile
@@ -346,14 +346,15 @@ struct Cfg16 {
   static constexpr int NCH = D / 8;             // 16-byte chunks per row
   static constexpr int TILE = BN * RB;          // bytes of one K (or V) tile
   static constexpr int LINES = TILE / 1024;     // 1 KiB direct-load lines per tile
-  static constexpr int LPW = LINES / kWaves;    // lines per wave per tile (K or V)
+  static constexpr int LPW = LINES / NW;        // lines per wave per tile (K or V)
+  static constexpr int STEP_ROWS = NW * 64 / NCH;  // rows between a wave's lines
   static constexpr int NQ = D / 16;             // 16-byte Q vectors per lane
   static constexpr int NMB = D / 32;            // 32-row blocks of O^T
   // D = 64: the per-row sum of P runs on the matrix cores as one more
   // 32-row block whose V^T rows are all ones (the VALU is the scarcer unit)
   static constexpr bool SUM_MFMA = (D == 64);
-  static_assert(LINES % kWaves == 0, "tile lines");
-  static_assert((256 / NCH) % 16 == 0, "swizzle period");
+  static_assert(LINES % NW == 0, "tile lines");
+  static_assert(STEP_ROWS % 16 == 0, "swizzle period");
 };
 
 // The reference max is only moved (and O, l rescaled) when a row's tile max
@@ -379,47 +380,12 @@ __device__ inline float dot2_ones(TBF16, uint32_t pk, float acc) {
                                          acc, false);
 }
 
-#ifndef SDPA_PF_SCHED
-#define SDPA_PF_SCHED 0
+#ifndef SDPA_PF_WIN
+#define SDPA_PF_WIN 4
 #endif
-// Instruction order of one steady-state tile, per matrix-core op: S(t+1) ops
-// each take a few exponentials and VALU ops of P(t) (the first key half), the
-// first half of the P(t).V(t) ops the exponentials of the second key half,
-// the second half the row max of S(t+1); LDS operand reads run a few ahead.
-// Neither unit waits for a long run of the other.
-template <int D>
-__device__ __forceinline__ void sched_steady() {
-#if SDPA_PF_SCHED
-  constexpr int nQK = 2 * (D / 16);
-  constexpr int nPV = 4 * (D / 32) + (D == 64 ? 4 : 0);
-  constexpr int nPVa = nPV / 2, nPVb = nPV - nPVa;
-  constexpr int kT = 0x400, kV = 0x002, kM = 0x008, kD = 0x100;
-  constexpr int tq = D == 64 ? 2 : 1, vq = D == 64 ? 4 : 3;
-  constexpr int ta = D == 64 ? 3 : 2, va = D == 64 ? 4 : 3;
-  constexpr int vb = D == 64 ? 4 : 3;
-  __builtin_amdgcn_sched_group_barrier(kD, 4, 0);
-#pragma unroll
-  for (int i = 0; i < nQK; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kM, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kT, tq, 0);
-    __builtin_amdgcn_sched_group_barrier(kV, vq, 0);
-    __builtin_amdgcn_sched_group_barrier(kD, 1, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < nPVa; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kM, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kT, ta, 0);
-    __builtin_amdgcn_sched_group_barrier(kV, va, 0);
-    __builtin_amdgcn_sched_group_barrier(kD, 2, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < nPVb; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kM, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kV, vb, 0);
-    __builtin_amdgcn_sched_group_barrier(kD, 2, 0);
-  }
+#ifndef SDPA_PF_LEAD
+#define SDPA_PF_LEAD 2
 #endif
-}
 
 // Per wave (32 queries) and tile (64 keys), software-pipelined:
 //   S(t+1) = K(t+1) . Q^T  on the matrix cores  ||  P(t) = exp2(S(t) c - m)  on the VALU
@@ -428,9 +394,10 @@ __device__ __forceinline__ void sched_steady() {
 // tile ahead, with one fence-free barrier per tile.  V^T is read with
 // ds_read_b64_tr_b16.  Interior tiles (every key visible to the whole
 // workgroup, no mask) skip per-element masking.
-template <class T, int D, bool CAUSAL, bool MASK>
+template <class T, int D, bool CAUSAL, bool MASK, int NW>
 __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
-  using C = Cfg16<D>;
+  using C = Cfg16<D, NW>;
+  constexpr int BM = 32 * NW;  // query rows per workgroup
   using S = uint16_t;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * C::TILE];
   uint8_t* const Kring = smem;               // stages 0, 1
@@ -442,14 +409,14 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const int nqt = (p.Lq + kBM - 1) / kBM;
+  const int nqt = (p.Lq + BM - 1) / BM;
   int qt, bh;
   prefill_tile((int)blockIdx.x, (int)gridDim.x, nqt, p.B * p.Hq, CAUSAL, qt, bh);
   const int b = bh / p.Hq;
   const int hq = bh % p.Hq;
   const int hk = hq / p.group;
 
-  const int i0 = qt * kBM;
+  const int i0 = qt * BM;
   const int iw = i0 + 32 * wave;
   const int my_i = iw + l32;
 
@@ -469,7 +436,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   }
 
   int kend = p.Lk;
-  if (CAUSAL) kend = min(kend, i0 + kBM + p.causal_off);
+  if (CAUSAL) kend = min(kend, i0 + BM + p.causal_off);
   const int ntiles = kend > 0 ? (kend + C::BN - 1) / C::BN : 0;
   // tiles [0, n_int) have every key visible to every row of the workgroup
   int n_int = 0;
@@ -483,9 +450,9 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // P = hi + lo (two bf16 products).  Many-key rows average it away.
   const bool split_p = std::is_same<T, TBF16>::value && (MASK || kend <= 1024);
 
-  // ---- direct buffer -> LDS loads.  Wave w fills lines w, w + 4, ... of a
-  // tile; line i of a wave sits 256 / NCH rows below line 0 and both swizzles
-  // repeat every 16 rows: one per-lane offset plus a uniform step.
+  // ---- direct buffer -> LDS loads.  Wave w fills lines w, w + NW, ... of a
+  // tile; line i of a wave sits i * STEP_ROWS rows below line 0 and both
+  // swizzles repeat every 16 rows: one per-lane offset plus a uniform step.
   const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
   const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
   uint32_t koff, voff;
@@ -496,7 +463,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     voff = (uint32_t)(row * p.vs[2] * 2 + (pch ^ swz_v<C::NCH>(row)) * 16);
   }
   const uint32_t krow = (uint32_t)(p.ks[2] * 2), vrow = (uint32_t)(p.vs[2] * 2);
-  const uint32_t kstep = (256 / C::NCH) * krow, vstep = (256 / C::NCH) * vrow;
+  const uint32_t kstep = C::STEP_ROWS * krow, vstep = C::STEP_ROWS * vrow;
   // bytes of a tile that hold keys < Lk (rows past Lk read as zero)
   auto tile_bytes = [&](int j0, uint32_t rowb) -> uint32_t {
     const int rows = p.Lk - j0;
@@ -509,7 +476,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     const uint32_t nb = tile_bytes(j0, rowb);
     const uint32_t la = lds_addr(st) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < C::LPW; ++i) dma16(tb, nb, la + kWaves * i * 1024, off, i * step);
+    for (int i = 0; i < C::LPW; ++i) dma16(tb, nb, la + NW * i * 1024, off, i * step);
   };
   auto issue_k = [&](int t, uint8_t* st) { issue(kbase, p.ks[2], krow, koff, kstep, st, t); };
   auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, voff, vstep, st, t); };
@@ -644,6 +611,97 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       }
   };
 
+  // One steady-state tile as a fixed sequence of slots.  Slot i holds
+  //   - the LDS operand read of matrix-core op i + W (W ops of lead time),
+  //   - matrix-core op i: ops [0, NQK) form S(t+1) = K(t+1).Q^T (kb-major),
+  //     the rest O^T += V(t)^T.P(t)^T in (kb, u) groups of NMB (+1 row-sum op),
+  //   - its share of the VALU work: "EC" items (two probabilities of P(t),
+  //     exponentials, packing, row sum) before the P.V ops that consume them,
+  //     then "X" items (row max of S(t+1), two scores each) once S(t+1) exists.
+  // A full scheduling fence closes every slot.  A wave whose matrix ops are
+  // spaced by a few VALU ops lets both units run at once; a run of
+  // back-to-back matrix ops stalls the VALU of the other wave on the SIMD.
+  auto steady_slots = [&](const uint8_t* Kst, const uint8_t* Vst, f32x16* cur, f32x16* nxt) -> float {
+    constexpr int NQK = C::NKB * C::NQ;
+    constexpr int GOPS = C::NMB + (C::SUM_MFMA ? 1 : 0);
+    constexpr int NOPS = NQK + C::NKB * 2 * GOPS;
+    constexpr int W = SDPA_PF_WIN;
+    constexpr int NEC = C::NKB * 8;            // EC items: (kb, u, e)
+    constexpr int NX = C::NKB * 8;             // X items: (kb, pair of rows)
+    constexpr int EC_END = NOPS - (D == 64 ? 6 : 8);  // EC items occupy slots [0, EC_END)
+    constexpr int X_BEG = EC_END;                     // X items occupy [X_BEG, NOPS)
+    static_assert(EC_END >= NQK + 2, "X items need S(t+1) complete");
+    u32x4 opnd[NOPS];
+    u32x4 hi[C::NKB][2];
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float mx = kNegInf;
+    auto load_op = [&](int i) {
+      if (i < NQK) {
+        const int kb = i / C::NQ, s = i % C::NQ;
+        opnd[i] = lds_read16(Kst + k_lane + 32 * kb * C::RB + (((2 * s + g) ^ k_swz) * 16));
+      } else {
+        const int j = i - NQK, grp = j / GOPS, w = j % GOPS;
+        const int kb = grp / 2, u = grp % 2;
+        if (w < C::NMB) {
+          const uint8_t* vb = Vst + v_lane + (32 * kb + 16 * u) * C::RB + ((4 * w + v_ch) ^ v_swz) * 16;
+          const u32x2 a0 = lds_read_tr16(vb);
+          const u32x2 a1 = lds_read_tr16(vb + 8 * C::RB);
+          opnd[i] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+        }
+      }
+    };
+    auto do_op = [&](int i) {
+      if (i < NQK) {
+        const int kb = i / C::NQ, s = i % C::NQ;
+        nxt[kb] = mma32(T{}, opnd[i], qreg[s], s == 0 ? f32x16{} : nxt[kb]);
+      } else {
+        const int j = i - NQK, grp = j / GOPS, w = j % GOPS;
+        const int kb = grp / 2, u = grp % 2;
+        if (w < C::NMB) acc[w] = mma32(T{}, opnd[i], hi[kb][u], acc[w]);
+        else lacc = mma32(T{}, ones, hi[kb][u], lacc);
+      }
+    };
+    auto ec_item = [&](int it) {
+      const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
+      const float p0 = fast_exp2(fmaf(cur[kb][8 * u + 2 * e], c, -m_use));
+      const float p1 = fast_exp2(fmaf(cur[kb][8 * u + 2 * e + 1], c, -m_use));
+      hi[kb][u][e] = cvt_pk(T{}, p0, p1);
+      if constexpr (!C::SUM_MFMA) l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
+    };
+    // v_max3 written out: fmaxf on matrix-core results would first quieten
+    // each operand (two extra VALU ops), and volatile keeps it in its slot
+    auto x_item = [&](int it) {
+      const int kb = it / 8, r = 2 * (it % 8);
+      asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(nxt[kb][r]), "v"(nxt[kb][r + 1]));
+    };
+    // item ranges of slot i: LEAD EC items run before the first matrix op,
+    // while the first operand reads are in flight; the other EC items spread
+    // evenly over [0, EC_END), X items over [X_BEG, NOPS)
+    constexpr int LEAD = SDPA_PF_LEAD;
+    auto ec_begin = [](int i) {
+      return i >= EC_END ? NEC : LEAD + (i * (NEC - LEAD) + EC_END - 1) / EC_END;
+    };
+    auto x_begin = [](int i) {
+      return i <= X_BEG ? 0 : (i >= NOPS ? NX : ((i - X_BEG) * NX + (NOPS - X_BEG) - 1) / (NOPS - X_BEG));
+    };
+#pragma unroll
+    for (int i = 0; i < W && i < NOPS; ++i) load_op(i);
+#pragma unroll
+    for (int it = 0; it < LEAD; ++it) ec_item(it);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NOPS; ++i) {
+      if (i + W < NOPS) load_op(i + W);
+      do_op(i);
+#pragma unroll
+      for (int it = ec_begin(i); it < ec_begin(i + 1); ++it) ec_item(it);
+#pragma unroll
+      for (int it = x_begin(i); it < x_begin(i + 1); ++it) x_item(it);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return max_xor32(mx) * c;
+  };
+
   // ---- pipeline.  Tile t lives in stage t & 1 of both rings.  Iteration t
   // waits for K(t+1) and V(t) (issued one iteration earlier), then refills the
   // stages that K(t) and V(t-1) occupied, whose last reads precede the barrier.
@@ -666,13 +724,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     lds_barrier();
     issue_v(t + 1, Vring + (PAR ^ 1) * C::TILE);
     issue_k(t + 2, Kring + PAR * C::TILE);
-    u32x4 hi[C::NKB][2], lo[C::NKB][2];
-    qk(Kring + (PAR ^ 1) * C::TILE, nxt);          // matrix cores ...
-    probs(cur, hi, lo, std::false_type{}, false);  // ... while the VALU exponentiates
-    pv(Vring + PAR * C::TILE, hi, lo, false);
-    const float mx = tile_max(t + 1, nxt, std::false_type{});
-    sched_steady<D>();
-    update_max(mx);
+    update_max(steady_slots(Kring + (PAR ^ 1) * C::TILE, Vring + PAR * C::TILE, cur, nxt));
   };
   auto general = [&](int t, auto edge_tag) {
     const int par = t & 1;
@@ -732,24 +784,25 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   }
 }
 
-// Two workgroups per CU; the masked variants keep a second score tile plus
-// the mask gathers live across the pipeline and get the whole register file.
-template <class T, int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill16_kernel(AttnParams p) {
-  prefill16_body<T, D, CAUSAL, false>(p);
+// Two waves per SIMD (NW-wave workgroups, 8 / NW of them per CU).  The
+// masked variants keep a second score tile plus the mask gathers live across
+// the pipeline and get the whole register file.
+template <class T, int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void prefill16_kernel(AttnParams p) {
+  prefill16_body<T, D, CAUSAL, false, NW>(p);
 }
 template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void prefill16_mask_kernel(AttnParams p) {
-  prefill16_body<T, D, CAUSAL, true>(p);
+  prefill16_body<T, D, CAUSAL, true, kWaves>(p);
 }
 
 template <class T, int D>
 hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
-  const int nqt = (p.Lq + kBM - 1) / kBM;
-  const dim3 grid((unsigned)(nqt * p.B * p.Hq));
-  const dim3 block(kThreads);
   const bool mask = p.mask != nullptr;
   if constexpr (std::is_same<T, TF32>::value) {
+    const int nqt = (p.Lq + kBM - 1) / kBM;
+    const dim3 grid((unsigned)(nqt * p.B * p.Hq));
+    const dim3 block(kThreads);
     if (causal) {
       if (mask) hipLaunchKernelGGL((prefill_f32_kernel<T, D, true, true>), grid, block, 0, s, p);
       else hipLaunchKernelGGL((prefill_f32_kernel<T, D, true, false>), grid, block, 0, s, p);
@@ -758,12 +811,17 @@ hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
       else hipLaunchKernelGGL((prefill_f32_kernel<T, D, false, false>), grid, block, 0, s, p);
     }
   } else {
-    if (causal) {
-      if (mask) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((prefill16_kernel<T, D, true>), grid, block, 0, s, p);
+    // 4-wave workgroups of 128 query rows.  (2-wave workgroups for D = 64 shrink
+    // the idle tail of the last round but double the K/V tile traffic into
+    // LDS, and measure slower.)
+    const dim3 grid((unsigned)((p.Lq + kBM - 1) / kBM * p.B * p.Hq));
+    const dim3 block(kThreads);
+    if (mask) {
+      if (causal) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, true>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill16_mask_kernel<T, D, false>), grid, block, 0, s, p);
     } else {
-      if (mask) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, false>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((prefill16_kernel<T, D, false>), grid, block, 0, s, p);
+      if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves>), grid, block, 0, s, p);
     }
   }
   return hipGetLastError();
