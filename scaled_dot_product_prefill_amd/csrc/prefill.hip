@@ -350,9 +350,6 @@ struct Cfg16 {
   static constexpr int STEP_ROWS = NW * 64 / NCH;  // rows between a wave's lines
   static constexpr int NQ = D / 16;             // 16-byte Q vectors per lane
   static constexpr int NMB = D / 32;            // 32-row blocks of O^T
-  // D = 64: the per-row sum of P runs on the matrix cores as one more
-  // 32-row block whose V^T rows are all ones (the VALU is the scarcer unit)
-  static constexpr bool SUM_MFMA = (D == 64);
   static_assert(LINES % NW == 0, "tile lines");
   static_assert(STEP_ROWS % 16 == 0, "swizzle period");
 };
@@ -493,11 +490,8 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   f32x16 acc[C::NMB];
 #pragma unroll
   for (int mb = 0; mb < C::NMB; ++mb) acc[mb] = f32x16{};
-  f32x16 lacc = f32x16{};  // row sums from the matrix cores (SUM_MFMA)
   float m_run = kNegInf;   // reference max of the scaled scores (log2 units)
   float l_run = 0.f;       // running sum over this lane's half of the keys
-  constexpr uint32_t kOnes = std::is_same<T, TBF16>::value ? 0x3F803F80u : 0x3C003C00u;
-  const u32x4 ones = {kOnes, kOnes, kOnes, kOnes};
 
   auto qk = [&](const uint8_t* Kst, f32x16* sc) {
     const uint8_t* Ks = Kst + k_lane;
@@ -550,8 +544,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       const float corr = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
 #pragma unroll
       for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
-      if constexpr (C::SUM_MFMA) lacc *= corr;
-      else l_run *= corr;
+      l_run *= corr;
       m_run = m_new;
     }
   };
@@ -579,10 +572,10 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
             TBF16::split2(p0, p1, h, l);
             hi[kb][u][e] = h;
             lo[kb][u][e] = l;
-            if constexpr (!C::SUM_MFMA) l_run += p0 + p1;
+            l_run += p0 + p1;
           } else {
             hi[kb][u][e] = cvt_pk(T{}, p0, p1);
-            if constexpr (!C::SUM_MFMA) l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
+            l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
           }
         }
     }
@@ -604,10 +597,6 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
           acc[mb] = mma32(T{}, va, hi[kb][u], acc[mb]);
           if (BF && split) acc[mb] = mma32(T{}, va, lo[kb][u], acc[mb]);
         }
-        if constexpr (C::SUM_MFMA) {
-          lacc = mma32(T{}, ones, hi[kb][u], lacc);
-          if (BF && split) lacc = mma32(T{}, ones, lo[kb][u], lacc);
-        }
       }
   };
 
@@ -623,7 +612,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // back-to-back matrix ops stalls the VALU of the other wave on the SIMD.
   auto steady_slots = [&](const uint8_t* Kst, const uint8_t* Vst, f32x16* cur, f32x16* nxt) -> float {
     constexpr int NQK = C::NKB * C::NQ;
-    constexpr int GOPS = C::NMB + (C::SUM_MFMA ? 1 : 0);
+    constexpr int GOPS = C::NMB;
     constexpr int NOPS = NQK + C::NKB * 2 * GOPS;
     constexpr int W = SDPA_PF_WIN;
     constexpr int NEC = C::NKB * 8;            // EC items: (kb, u, e)
@@ -657,8 +646,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       } else {
         const int j = i - NQK, grp = j / GOPS, w = j % GOPS;
         const int kb = grp / 2, u = grp % 2;
-        if (w < C::NMB) acc[w] = mma32(T{}, opnd[i], hi[kb][u], acc[w]);
-        else lacc = mma32(T{}, ones, hi[kb][u], lacc);
+        acc[w] = mma32(T{}, opnd[i], hi[kb][u], acc[w]);
       }
     };
     auto ec_item = [&](int it) {
@@ -666,7 +654,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       const float p0 = fast_exp2(fmaf(cur[kb][8 * u + 2 * e], c, -m_use));
       const float p1 = fast_exp2(fmaf(cur[kb][8 * u + 2 * e + 1], c, -m_use));
       hi[kb][u][e] = cvt_pk(T{}, p0, p1);
-      if constexpr (!C::SUM_MFMA) l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
+      l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
     };
     // v_max3 written out: fmaxf on matrix-core results would first quieten
     // each operand (two extra VALU ops), and volatile keeps it in its slot
@@ -757,7 +745,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   for (; t < ntiles; ++t) general(t, std::true_type{});
 
   // ---- epilogue ----
-  const float l_tot = C::SUM_MFMA ? lacc[0] : sum_xor32(l_run);
+  const float l_tot = sum_xor32(l_run);
   float M = m_run, Ltot = l_tot;
   if (p.sinks) {
     const float sk = p.sinks[hq] * kLog2e;
