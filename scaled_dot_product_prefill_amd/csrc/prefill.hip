@@ -380,9 +380,6 @@ __device__ inline float dot2_ones(TBF16, uint32_t pk, float acc) {
 #ifndef SDPA_PF_WIN
 #define SDPA_PF_WIN 4
 #endif
-#ifndef SDPA_PF_LEAD
-#define SDPA_PF_LEAD 2
-#endif
 
 // Per wave (32 queries) and tile (64 keys), software-pipelined:
 //   S(t+1) = K(t+1) . Q^T  on the matrix cores  ||  P(t) = exp2(S(t) c - m)  on the VALU
@@ -623,7 +620,6 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     u32x4 opnd[NOPS];
     u32x4 hi[C::NKB][2];
     const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float mx = kNegInf;
     auto load_op = [&](int i) {
       if (i < NQK) {
         const int kb = i / C::NQ, s = i % C::NQ;
@@ -649,44 +645,62 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
         acc[w] = mma32(T{}, opnd[i], hi[kb][u], acc[w]);
       }
     };
-    auto ec_item = [&](int it) {
+    // EC item = two probabilities: (a) scaled score minus max, (b) exp2,
+    // (c) pack + row sum.  The stages of one item run in consecutive slots
+    // (a two slots ahead of c), so each slot mixes independent work of three
+    // items instead of one dependent chain.
+    float xs[NEC][2], ps[NEC][2];
+    auto ec_a = [&](int it) {
       const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
-      const float p0 = fast_exp2(fmaf(cur[kb][8 * u + 2 * e], c, -m_use));
-      const float p1 = fast_exp2(fmaf(cur[kb][8 * u + 2 * e + 1], c, -m_use));
-      hi[kb][u][e] = cvt_pk(T{}, p0, p1);
+      xs[it][0] = fmaf(cur[kb][8 * u + 2 * e], c, -m_use);
+      xs[it][1] = fmaf(cur[kb][8 * u + 2 * e + 1], c, -m_use);
+    };
+    auto ec_b = [&](int it) {
+      ps[it][0] = fast_exp2(xs[it][0]);
+      ps[it][1] = fast_exp2(xs[it][1]);
+    };
+    auto ec_c = [&](int it) {
+      const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
+      hi[kb][u][e] = cvt_pk(T{}, ps[it][0], ps[it][1]);
       l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
     };
     // v_max3 written out: fmaxf on matrix-core results would first quieten
-    // each operand (two extra VALU ops), and volatile keeps it in its slot
+    // each operand (two extra VALU ops), and volatile keeps it in its slot.
+    // Two running maxima halve the dependent chain.
+    float mx2[2] = {kNegInf, kNegInf};
     auto x_item = [&](int it) {
       const int kb = it / 8, r = 2 * (it % 8);
-      asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(mx) : "v"(mx), "v"(nxt[kb][r]), "v"(nxt[kb][r + 1]));
+      float& m = mx2[it & 1];
+      asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(nxt[kb][r]), "v"(nxt[kb][r + 1]));
     };
-    // item ranges of slot i: LEAD EC items run before the first matrix op,
-    // while the first operand reads are in flight; the other EC items spread
-    // evenly over [0, EC_END), X items over [X_BEG, NOPS)
-    constexpr int LEAD = SDPA_PF_LEAD;
-    auto ec_begin = [](int i) {
-      return i >= EC_END ? NEC : LEAD + (i * (NEC - LEAD) + EC_END - 1) / EC_END;
-    };
+    // item ranges: EC items finish (stage c) evenly over slots [0, EC_END),
+    // X items run over [X_BEG, NOPS)
+    auto ec_begin = [](int i) { return i >= EC_END ? NEC : (i * NEC + EC_END - 1) / EC_END; };
     auto x_begin = [](int i) {
       return i <= X_BEG ? 0 : (i >= NOPS ? NX : ((i - X_BEG) * NX + (NOPS - X_BEG) - 1) / (NOPS - X_BEG));
     };
 #pragma unroll
     for (int i = 0; i < W && i < NOPS; ++i) load_op(i);
 #pragma unroll
-    for (int it = 0; it < LEAD; ++it) ec_item(it);
+    for (int it = 0; it < ec_begin(2); ++it) ec_a(it);
+#pragma unroll
+    for (int it = 0; it < ec_begin(1); ++it) ec_b(it);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NOPS; ++i) {
       if (i + W < NOPS) load_op(i + W);
       do_op(i);
 #pragma unroll
-      for (int it = ec_begin(i); it < ec_begin(i + 1); ++it) ec_item(it);
+      for (int it = ec_begin(i + 2); it < ec_begin(i + 3); ++it) ec_a(it);
+#pragma unroll
+      for (int it = ec_begin(i + 1); it < ec_begin(i + 2); ++it) ec_b(it);
+#pragma unroll
+      for (int it = ec_begin(i); it < ec_begin(i + 1); ++it) ec_c(it);
 #pragma unroll
       for (int it = x_begin(i); it < x_begin(i + 1); ++it) x_item(it);
       __builtin_amdgcn_sched_barrier(0);
     }
+    const float mx = fmaxf(mx2[0], mx2[1]);
     return max_xor32(mx) * c;
   };
 
