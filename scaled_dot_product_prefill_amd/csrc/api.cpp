@@ -151,9 +151,15 @@ struct SplitPlan {
   int split_len = 0;
 };
 
-// Split of the key range for decode.  Automatic: enough workgroups to give
-// every compute unit several (about 1024 for 256 CUs), each split a whole
-// number of key tiles, never more splits than tiles.
+// Split of the key range for decode.  Automatic: start from one workgroup per
+// compute unit (MI355X: 256), then double the split count while a split would
+// still hold more than 32 key tiles (up to 16 workgroups per CU); never more
+// splits than tiles, each split a whole number of tiles.  Measured on the
+// GQA-8 D512 and long-context D128 decode shapes, this is within a few percent
+// of the best fixed split count for each.
+constexpr int64_t kDecodeCUs = 256;
+constexpr int64_t kDecodeMaxTilesPerSplit = 32;
+
 SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
   SplitPlan sp;
   const int64_t Lk = a->Lk;
@@ -169,7 +175,8 @@ SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
     const int64_t tk = decode_tile_keys(a->dtype, (int)a->D);
     const int64_t tiles = (Lk + tk - 1) / tk;
     const int64_t units = a->B * a->Hkv;
-    int64_t ns = (1024 + units - 1) / units;
+    int64_t ns = (kDecodeCUs + units - 1) / units;
+    while ((tiles + ns - 1) / ns > kDecodeMaxTilesPerSplit && ns * units < 16 * kDecodeCUs) ns *= 2;
     if (ns > tiles) ns = tiles;
     if (ns < 1) ns = 1;
     const int64_t tiles_per = (tiles + ns - 1) / ns;

@@ -155,10 +155,14 @@ def _sizes(B, Hq, Hkv, Lk, D, dtype):
 
 
 def test_split_plan(lib):
-    # long-context batch: B*Hkv = 64 units -> 16 splits of 8192 keys
+    # long-context batch: B*Hkv = 64 units start at 4 splits (256 workgroups)
+    # and double until a split holds <= 32 tiles of 64 keys: 64 splits of 2048
     a = _sizes(8, 32, 8, 131072, 128, sdpa.BF16)
-    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 16
-    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 0) == 8 * 32 * 16 * 130 * 4
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 0) == 8 * 32 * 64 * 130 * 4
+    # GQA-8 D512, B2, Lk=32768 (2048 tiles of 16 keys): 32 -> 64 splits
+    a = _sizes(2, 32, 4, 32768, 512, sdpa.F16)
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
     # GQA-8 D=512, B=1, Lk=1024: one 16-key tile per split
     a = _sizes(1, 32, 4, 1024, 512, sdpa.F16)
     assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
