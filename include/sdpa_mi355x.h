@@ -47,7 +47,10 @@
  *     contiguous; *_stride[0..2] are ELEMENT strides of the B, H and L dims.
  *     Base pointers must be 16-byte aligned and every stride * element size
  *     a multiple of 16 bytes (the input preparation rule of prepare_sdpa_input
- *     on the mlx 0.30.7 page: unit last-dim stride, aligned pointer).
+ *     on the mlx 0.30.7 page: unit last-dim stride, aligned pointer).  The
+ *     row (L) stride of k and v may be at most 8 MiB (SDPA_ERR_UNSUPPORTED
+ *     above): key tiles are addressed with 32-bit offsets from their first
+ *     row.
  *   - mask (optional, fp32) is indexed mask[b*s0 + hq*s1 + i*s2 + j*s3] with
  *     mask_stride[0..3] in elements; a stride of 0 broadcasts that dim (a
  *     [B,1,1,Lk] mask passes strides {Lk, 0, 0, 1}).  4-byte aligned.

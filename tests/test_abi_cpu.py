@@ -126,6 +126,9 @@ def test_prefill_validation(lib):
     assert _prefill(lib, mask=(1 << 45) + 2) == S.ERR_ALIGN
     assert _prefill(lib, mask=1 << 45, mask_stride=(0, 0, -1, 1)) == S.ERR_ARG
     assert _prefill(lib, lse=(1 << 40) + 16) == S.ERR_ARG     # lse overlaps q
+    big = (1 << 22) + 8                                        # 8 MiB + 16 B per bf16 row
+    assert _prefill(lib, k_stride=(2 * 64 * big, 64 * big, big)) == S.ERR_UNSUPPORTED
+    assert _prefill(lib, v_stride=(2 * 64 * big, 64 * big, big)) == S.ERR_UNSUPPORTED
     assert _prefill(lib, D=64, causal=1, Lq=100, Lk=7) == S.OK
     msg = lib.sdpa_last_error()
     assert msg == b""
