@@ -16,7 +16,9 @@
  *                 attention on large sequences" page;
  *   sdpa_decode   single-query "vector" attention (Lq == 1) with a single-pass
  *                 and a two-pass split-K variant -- the two vector kernels of
- *                 the "Add D512 support to Metal vector attention" page.
+ *                 the "Add D512 support to Metal vector attention" page --
+ *                 extended to a few query rows (Lq <= 16: speculative or
+ *                 chunked decoding, the qL4 control of that page).
  *
  * The optional inputs follow the SDPA graph attributes configured by
  * build_sdpa_graph on the "mlx 0.30.7 -- backend/cuda/
@@ -127,8 +129,11 @@ SDPA_API int sdpa_prefill(const sdpa_args *args, void *stream);
  * Returns what sdpa_prefill would return before launching. */
 SDPA_API int sdpa_prefill_check(const sdpa_args *args);
 
-/* Single-query decode (Lq == 1; causal has no effect there).
- * Supported: D in {64, 128, 256, 512}; dtype F32, F16, BF16; Hq / Hkv <= 16.
+/* Decode: single-query (Lq == 1) or multi-query (1 <= Lq <= 16) attention
+ * whose keys stream once per KV head.  The Lq query rows and the Hq / Hkv
+ * query heads sharing a KV head are processed together; causal is
+ * bottom-right within the query block (it has no effect for Lq == 1).
+ * Supported: D in {64, 128, 256, 512}; dtype F32, F16, BF16; any Hq / Hkv.
  * num_splits = 0 picks the split count automatically; 1 forces the
  * single-pass kernel; n >= 2 forces the two-pass split-K kernel pair with n
  * splits of the key range (n <= Lk).  The two-pass form needs a workspace of
@@ -147,7 +152,8 @@ SDPA_API int sdpa_decode_check(const sdpa_args *args, int num_splits,
 SDPA_API int sdpa_decode_num_splits(const sdpa_args *args, int num_splits);
 
 /* Workspace bytes sdpa_decode needs for this request and num_splits
- * (0 when the single-pass kernel is used or the request is invalid). */
+ * (0 when the single-pass kernel is used or the request is invalid):
+ * B * Hq * Lq * splits * (D + 2) * 4. */
 SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_splits);
 
 /* Static description of a status code. */

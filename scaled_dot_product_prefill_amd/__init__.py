@@ -5,7 +5,7 @@ kernels of the library.  PyTorch supplies device memory and the stream.  When
 the library is missing, every entry point raises -- there is no CPU path.
 
     prefill(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False)
-    decode(q, k, v, scale=None, mask=None, sinks=None, return_lse=False, num_splits=0)
+    decode(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False, num_splits=0)
 
 q: [B, Hq, Lq, D], k / v: [B, Hkv, Lk, D] (float32, float16 or bfloat16),
 mask: additive float tensor broadcastable to [B, Hq, Lq, Lk], sinks: [Hq].
@@ -210,17 +210,18 @@ def _size_args(q, k) -> SdpaArgs:
 
 
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
-           mask: Optional[torch.Tensor] = None, sinks: Optional[torch.Tensor] = None,
-           return_lse: bool = False, num_splits: int = 0,
+           causal: bool = False, mask: Optional[torch.Tensor] = None,
+           sinks: Optional[torch.Tensor] = None, return_lse: bool = False, num_splits: int = 0,
            workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
-    """Single-query attention (q has Lq == 1).  num_splits: 0 automatic,
+    """Decode attention: one query row (Lq == 1) or a few (Lq <= 16, bottom-right
+    causal within the block when ``causal``).  num_splits: 0 automatic,
     1 single-pass kernel, n >= 2 two-pass split-K with n key ranges."""
     lib = library()
     q, k, v, scale, mask, sinks = _decode_args(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
-    a = _make_args(q, k, v, o, scale, False, mask, sinks, lse)
+    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse)
     need = int(lib.sdpa_decode_workspace_bytes(ctypes.byref(a), int(num_splits)))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -146,6 +146,12 @@ int check_prefill(const sdpa_args* a) {
   return SDPA_OK;
 }
 
+// Decode: the Lq query rows times the G heads of a KV head are the columns of
+// 16-wide matrix tiles (multi-query decode, e.g. speculative or chunked
+// decoding); each chunk of 16 columns is one workgroup per key split.
+constexpr int kMaxDecodeLq = 16;
+int64_t decode_chunks(const sdpa_args* a) { return (a->Lq * (a->Hq / a->Hkv) + 15) / 16; }
+
 struct SplitPlan {
   int nsplit = 1;
   int split_len = 0;
@@ -174,7 +180,7 @@ SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
   } else {
     const int64_t tk = decode_tile_keys(a->dtype, (int)a->D);
     const int64_t tiles = (Lk + tk - 1) / tk;
-    const int64_t units = a->B * a->Hkv;
+    const int64_t units = a->B * a->Hkv * decode_chunks(a);
     int64_t ns = (kDecodeCUs + units - 1) / units;
     while ((tiles + ns - 1) / ns > kDecodeMaxTilesPerSplit && ns * units < 16 * kDecodeCUs) ns *= 2;
     if (ns > tiles) ns = tiles;
@@ -189,22 +195,21 @@ SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
 
 size_t workspace_for(const sdpa_args* a, const SplitPlan& sp) {
   if (sp.nsplit <= 1) return 0;
-  return (size_t)a->B * a->Hq * sp.nsplit * (a->D + 2) * sizeof(float);
+  return (size_t)a->B * a->Hq * a->Lq * sp.nsplit * (a->D + 2) * sizeof(float);
 }
 
 int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_bytes, SplitPlan* out) {
   int st = check_common(a);
   if (st != SDPA_OK) return st;
-  if (a->Lq != 1)
-    return fail(SDPA_ERR_UNSUPPORTED, "decode needs Lq == 1, got %lld", (long long)a->Lq);
+  if (a->Lq > kMaxDecodeLq)
+    return fail(SDPA_ERR_UNSUPPORTED, "decode supports 1 <= Lq <= %d, got %lld", kMaxDecodeLq, (long long)a->Lq);
   if (a->D != 64 && a->D != 128 && a->D != 256 && a->D != 512)
     return fail(SDPA_ERR_UNSUPPORTED, "decode supports D in {64, 128, 256, 512}, got %lld", (long long)a->D);
-  if (a->Hq / a->Hkv > 16)
-    return fail(SDPA_ERR_UNSUPPORTED, "decode supports Hq / Hkv <= 16, got %lld", (long long)(a->Hq / a->Hkv));
   if (num_splits < 0 || num_splits > a->Lk)
     return fail(SDPA_ERR_ARG, "num_splits must be in [0, Lk], got %d", num_splits);
   SplitPlan sp = plan_splits(a, num_splits);
-  if ((int64_t)sp.nsplit * a->Hkv * a->B > kMaxInt) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
+  if ((int64_t)sp.nsplit * decode_chunks(a) * a->Hkv * a->B > kMaxInt)
+    return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
   const size_t need = workspace_for(a, sp);
   if (need > 0) {
     if (!ws) return fail(SDPA_ERR_WORKSPACE, "two-pass decode needs a workspace of %zu bytes", need);
@@ -240,6 +245,7 @@ AttnParams make_params(const sdpa_args& a) {
   p.causal_off = (int)(a.Lk - a.Lq);
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.nsplit = 1;
+  p.nchunk = 1;
   p.split_len = (int)a.Lk;
   return p;
 }
@@ -284,10 +290,12 @@ int sdpa_decode(const sdpa_args* args, int num_splits, void* workspace, size_t w
   sdpa::AttnParams p = sdpa::make_params(*args);
   p.nsplit = sp.nsplit;
   p.split_len = sp.split_len;
+  p.nchunk = (int)sdpa::decode_chunks(args);
+  if (!args->causal) p.causal_off = p.Lk;  // every key visible to every query row
   if (sp.nsplit > 1) {
     float* ws = (float*)workspace;
     p.part_o = ws;
-    p.part_ml = ws + (size_t)args->B * args->Hq * sp.nsplit * args->D;
+    p.part_ml = ws + (size_t)args->B * args->Hq * args->Lq * sp.nsplit * args->D;
   }
   return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
 }

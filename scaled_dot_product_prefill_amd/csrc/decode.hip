@@ -31,6 +31,35 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
+// Work unit of a decode workgroup and the matrix column of one lane.  Block
+// index = ((b * Hkv + hk) * nchunk + chunk) * nsplit + split.  The G query
+// heads of the KV head times the Lq query rows form the columns of the 16x16
+// tiles, column c = qi * G + h, 16 per chunk; lane column n is c = 16 chunk + n.
+// Query row qi sees keys j <= causal_off + qi (bottom-right causal; without
+// causal masking causal_off is Lk, so every key passes).
+struct DecodeUnit {
+  int split, hk, b;
+  bool ok;        // lane column is a real (query row, head)
+  int hq, qi;     // its query head and query row (0 for padding columns)
+  int last_key;   // last visible key of that row
+};
+__device__ inline DecodeUnit decode_unit(const AttnParams& p, int n) {
+  DecodeUnit u;
+  u.split = blockIdx.x % p.nsplit;
+  int r = blockIdx.x / p.nsplit;
+  const int chunk = r % p.nchunk;
+  r /= p.nchunk;
+  u.hk = r % p.Hkv;
+  u.b = r / p.Hkv;
+  const int c = 16 * chunk + n;
+  u.ok = c < p.Lq * p.group;
+  const int cc = u.ok ? c : 0;
+  u.qi = cc / p.group;
+  u.hq = u.hk * p.group + cc % p.group;
+  u.last_key = p.causal_off + u.qi;
+  return u;
+}
+
 template <class T, int D>
 struct DecodeCfg {
   static constexpr int ES = T::kBytes;
@@ -90,12 +119,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   const int n = lane & 15;   // head column of the 16x16 tiles (also the K row of the A operand)
   const int g4 = lane >> 4;  // lane group
 
-  const int split = blockIdx.x % p.nsplit;
-  const int bk = blockIdx.x / p.nsplit;
-  const int hk = bk % p.Hkv;
-  const int b = bk / p.Hkv;
-  const bool head_ok = n < p.group;
-  const int hq = hk * p.group + (head_ok ? n : 0);  // query head of this lane's column
+  const DecodeUnit u = decode_unit(p, n);
+  const int split = u.split, hk = u.hk, b = u.b, hq = u.hq, qi = u.qi;
+  const bool head_ok = u.ok;
 
   const int kbeg = split * p.split_len;
   const int kend = min(p.Lk, kbeg + p.split_len);
@@ -108,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   u32x4 qreg[C::NSW];
   {
     const int s0 = wave < C::QSPLIT ? wave * C::NSW : 0;
-    const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1];
+    const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1] + (int64_t)qi * p.qs[2];
 #pragma unroll
     for (int s = 0; s < C::NSW; ++s) {
       u32x4 v = ldg16_cached(row + (4 * (s0 + s) + g4) * C::VEC);
@@ -117,7 +143,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   }
 
   // mask row of this lane's head: four consecutive keys per 16-key block
-  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] : nullptr;
+  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] + (int64_t)qi * p.ms[2] : nullptr;
   const bool mask_vec = MASK && p.ms[3] == 1 && (((uintptr_t)mrow) & 15) == 0;
 
   f32x4 acc[C::NOB];
@@ -235,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
       for (int r = 0; r < 4; ++r) {
         float x = sc[blk][r] * p.scale_log2;
         if (MASK) x += kLog2e * mk[r];
-        x = jb + r < kend ? x : kNegInf;
+        x = (jb + r < kend && jb + r <= u.last_key) ? x : kNegInf;
         sc[blk][r] = x;
         mx = fmaxf(mx, x);
       }
@@ -332,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   // ---- epilogue ----
   float l_tot = l_run + xor16(l_run);
   l_tot = sum_xor32(l_tot);
-  const int64_t bh = (int64_t)b * p.Hq + hq;
+  const int64_t bh = ((int64_t)b * p.Hq + hq) * p.Lq + qi;  // (b, hq, query row)
   auto out_d = [&](int i, int r) {
     const int rho = 16 * (wave * C::NOB + i) + 4 * g4 + r;
     return C::F32 ? vt_row_to_d<C::NCH, C::VEC>(rho) : rho;
@@ -363,7 +389,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
       lse = (M + fast_log2(Ltot)) * kLn2;
     }
     if (head_ok) {
-      S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1];
+      S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)qi * p.os[2];
 #pragma unroll
       for (int i = 0; i < C::NOB; ++i)
 #pragma unroll
@@ -424,12 +450,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   const int n = lane & 15;
   const int g4 = lane >> 4;
 
-  const int split = blockIdx.x % p.nsplit;
-  const int bk = blockIdx.x / p.nsplit;
-  const int hk = bk % p.Hkv;
-  const int b = bk / p.Hkv;
-  const bool head_ok = n < p.group;
-  const int hq = hk * p.group + (head_ok ? n : 0);
+  const DecodeUnit u = decode_unit(p, n);
+  const int split = u.split, hk = u.hk, b = u.b, hq = u.hq, qi = u.qi;
+  const bool head_ok = u.ok;
 
   const int kbeg = split * p.split_len;
   const int kend = min(p.Lk, kbeg + p.split_len);
@@ -441,14 +464,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   // Q^T operand: vector s = chunk 4s + g4 of the head row
   u32x4 qreg[C::NQ];
   {
-    const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1];
+    const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1] + (int64_t)qi * p.qs[2];
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
       const u32x4 v = ldg16_cached(row + (4 * s + g4) * 8);
       qreg[s] = head_ok ? v : u32x4{0, 0, 0, 0};
     }
   }
-  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] : nullptr;
+  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] + (int64_t)qi * p.ms[2] : nullptr;
 
   // ---- per-lane direct-load offsets (fixed across tiles): wave w issues
   //      lines w, w + 4, ...; lines [0, LINES) are K, the rest V
@@ -553,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
       for (int r = 0; r < 4; ++r) {
         float x = sc[blk][r] * p.scale_log2;
         if (MASK) x += kLog2e * mk[blk][r];
-        x = jb + r < kend ? x : kNegInf;
+        x = (jb + r < kend && jb + r <= u.last_key) ? x : kNegInf;
         sc[blk][r] = x;
         mx = fmaxf(mx, x);
       }
@@ -604,7 +627,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   // ---- epilogue (identical in every wave; each writes its rows of O)
   float l_tot = l_run + xor16(l_run);
   l_tot = sum_xor32(l_tot);
-  const int64_t bh = (int64_t)b * p.Hq + hq;
+  const int64_t bh = ((int64_t)b * p.Hq + hq) * p.Lq + qi;  // (b, hq, query row)
   if constexpr (SPLIT) {
     if (head_ok) {
       float* po = p.part_o + (bh * p.nsplit + split) * D;
@@ -630,7 +653,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
       lse = (M + fast_log2(Ltot)) * kLn2;
     }
     if (head_ok) {
-      S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1];
+      S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)qi * p.os[2];
 #pragma unroll
       for (int i = 0; i < C::NOB; ++i) {
         const f32x4 o = acc[i] * so;
@@ -659,10 +682,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   __shared__ f32x4 part[NSG][NDQ];
   const int tid = threadIdx.x;
   const int nslice = D / (NDQ * 4);
-  const int64_t bh = blockIdx.x / nslice;
+  const int64_t bh = blockIdx.x / nslice;  // ((b * Hq + hq) * Lq + qi)
   const int d0 = (blockIdx.x % nslice) * NDQ * 4;
-  const int hq = (int)(bh % p.Hq);
-  const int b = (int)(bh / p.Hq);
+  const int qi = (int)(bh % p.Lq);
+  const int hq = (int)(bh / p.Lq % p.Hq);
+  const int b = (int)(bh / p.Lq / p.Hq);
   const float* pml = p.part_ml + bh * p.nsplit * 2;
   const float* po = p.part_o + bh * p.nsplit * D;
   const float sk = p.sinks ? p.sinks[hq] * kLog2e : kNegInf;
@@ -703,7 +727,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   if (sg == 0) {
     for (int g = 1; g < NSG; ++g) o += part[g][dq];
     const float inv = live ? 1.f / L : 0.f;
-    S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + d0 + 4 * dq;
+    S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)qi * p.os[2] + d0 + 4 * dq;
 #pragma unroll
     for (int e = 0; e < 4; ++e) orow[e] = T::from_f32(o[e] * inv);
     if (p.lse && blockIdx.x % nslice == 0 && dq == 0)
@@ -713,7 +737,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
 
 template <class T, int D>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
-  const dim3 grid((unsigned)((int64_t)p.nsplit * p.Hkv * p.B));
+  const dim3 grid((unsigned)((int64_t)p.nsplit * p.nchunk * p.Hkv * p.B));
   const dim3 block(kThreads);
   const bool mask = p.mask != nullptr;
   constexpr bool F32 = std::is_same<T, TF32>::value;
@@ -728,7 +752,7 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nslice = D / (D < kMergeCols ? D : kMergeCols);
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)p.B * p.Hq * nslice)),
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((int64_t)p.B * p.Hq * p.Lq * nslice)),
                        dim3(kMergeThreads), 0, s, p);
   } else {
     if constexpr (F32) {

@@ -25,9 +25,10 @@ struct AttnParams {
   float scale_log2;  // scale * log2(e)
   // decode only
   int nsplit;        // number of key-range splits (1 = single pass)
+  int nchunk;        // decode: 16-column chunks of the Lq * G (query row, head) columns
   int split_len;     // keys per split
-  float* part_o;     // [B*Hq, nsplit, D]  fp32 partial numerators
-  float* part_ml;    // [B*Hq, nsplit, 2]  fp32 (running max in log2 units, sum)
+  float* part_o;     // [B*Hq*Lq, nsplit, D]  fp32 partial numerators
+  float* part_ml;    // [B*Hq*Lq, nsplit, 2]  fp32 (running max in log2 units, sum)
 };
 
 AttnParams make_params(const sdpa_args& a);

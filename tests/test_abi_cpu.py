@@ -138,9 +138,8 @@ def test_prefill_validation(lib):
 
 def test_decode_validation(lib):
     assert _decode(lib) == S.OK
-    assert _decode(lib, Lq=2) == S.ERR_UNSUPPORTED
+    assert _decode(lib, Lq=17) == S.ERR_UNSUPPORTED           # multi-query decode: Lq <= 16
     assert _decode(lib, D=96) == S.ERR_UNSUPPORTED
-    assert _decode(lib, Hq=34) == S.ERR_UNSUPPORTED           # group of 17
     assert _decode(lib, num_splits=-1) == S.ERR_ARG
     assert _decode(lib, num_splits=65) == S.ERR_ARG           # more splits than keys
     assert _decode(lib, num_splits=4, ws=None) == S.ERR_WORKSPACE
@@ -151,9 +150,9 @@ def test_decode_validation(lib):
         assert lib.sdpa_status_string(st)
 
 
-def _sizes(B, Hq, Hkv, Lk, D, dtype):
+def _sizes(B, Hq, Hkv, Lk, D, dtype, Lq=1):
     a = sdpa.SdpaArgs()
-    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.D, a.dtype, a.scale = B, Hq, Hkv, 1, Lk, D, dtype, 1.0
+    a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.D, a.dtype, a.scale = B, Hq, Hkv, Lq, Lk, D, dtype, 1.0
     return a
 
 
@@ -169,6 +168,13 @@ def test_split_plan(lib):
     # GQA-8 D=512, B=1, Lk=1024: one 16-key tile per split
     a = _sizes(1, 32, 4, 1024, 512, sdpa.F16)
     assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
+    # multi-query decode: Lq * G = 4 * 8 columns = 2 chunks of 16 per KV head
+    # -> 8 units start at 32 splits, doubled once to 32 tiles per split;
+    # partials are kept per query row
+    a = _sizes(1, 32, 4, 32768, 512, sdpa.F16, Lq=4)
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
+    assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 0) == 1 * 32 * 4 * 64 * 514 * 4
+    a = _sizes(1, 32, 4, 1024, 512, sdpa.F16)
     # forced counts and single pass
     assert lib.sdpa_decode_num_splits(ctypes.byref(a), 1) == 1
     assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 1) == 0

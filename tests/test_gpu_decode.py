@@ -1,8 +1,9 @@
 """GPU parity of the decode kernels (sdpa_decode through the C ABI: single-pass,
 and two-pass split-K + merge) against the fp64 oracle: the whole GQA-8 D=512
 grid (Lk 1k/8k/32k, B 1/2, fp16/bf16/fp32, with and without sinks), the
-long-context masked batch at full size, and edge cases (fully masked splits,
-all keys masked, KV-cache slices, every head dim and group size)."""
+long-context masked batch at full size, edge cases (fully masked splits,
+all keys masked, KV-cache slices, every head dim and group size) and
+multi-query decode (Lq <= 16, causal within the block)."""
 import math
 
 import numpy as np
@@ -111,11 +112,55 @@ def test_single_pass_matches_two_pass_and_prefill():
 
 
 def test_decode_errors():
-    x = to_dev(random_case(3400, 1, 4, 2, 2, 64, 128, "fp16"))
+    x = to_dev(random_case(3400, 1, 4, 2, 17, 64, 128, "fp16"))
     with pytest.raises(sdpa.SdpaError) as e:
-        sdpa.decode(x["q"], x["k"], x["v"])                # Lq = 2
+        sdpa.decode(x["q"], x["k"], x["v"])                # Lq = 17 > 16
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
-    x = to_dev(random_case(3401, 1, 34, 2, 1, 64, 128, "fp16"))
+    x = to_dev(random_case(3401, 1, 4, 2, 1, 64, 96, "fp16"))
     with pytest.raises(sdpa.SdpaError) as e:
-        sdpa.decode(x["q"], x["k"], x["v"])                # group of 17 > 16
+        sdpa.decode(x["q"], x["k"], x["v"])                # D = 96
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
+
+
+# Multi-query decode (Lq query rows per head, speculative / chunked decoding):
+# the rows and the G heads of a KV head share the 16 columns of the matrix
+# tiles, 16 columns per workgroup; causal is bottom-right within the block.
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("Lq,G", [(2, 8), (4, 8), (8, 4), (16, 1), (3, 17)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_query(dtype, Lq, G, causal):
+    Hkv, D, Lk = 2, (512 if G == 8 else 128), 1500
+    x = random_case(3500 + 17 * Lq + G, 2, Hkv * G, Hkv, Lq, Lk, D, dtype, mask=True,
+                    mask_neg_inf_frac=0.05, sinks=(Lq == 4))
+    d = to_dev(x)
+    sc = 1 / math.sqrt(D)
+    for ns in (0, 1, 7):
+        out, l = sdpa.decode(d["q"], d["k"], d["v"], scale=sc, causal=causal, mask=d["mask"],
+                             sinks=d["sinks"], return_lse=True, num_splits=ns)
+        torch.cuda.synchronize()
+        compare_full(out, l, x, sc, dtype, f"Lq{Lq} G{G} causal={causal} splits={ns}", causal=causal)
+
+
+def test_multi_query_more_rows_than_keys():
+    # causal with Lq > Lk: the first Lq - Lk rows see no key (O = 0, LSE = -inf,
+    # or LSE = sink when sinks are given)
+    for sinks in (False, True):
+        x = random_case(3600 + sinks, 1, 8, 2, 12, 5, 128, "bf16", sinks=sinks)
+        d = to_dev(x)
+        for ns in (1, 3):
+            out, l = sdpa.decode(d["q"], d["k"], d["v"], causal=True, sinks=d["sinks"],
+                                 return_lse=True, num_splits=ns)
+            torch.cuda.synchronize()
+            assert torch.all(out[:, :, :7] == 0)
+            compare_full(out, l, x, 1 / math.sqrt(128), "bf16", f"Lq>Lk sinks={sinks} splits={ns}",
+                         causal=True)
+
+
+def test_multi_query_matches_prefill():
+    x = to_dev(random_case(3700, 2, 32, 4, 8, 4096, 128, "fp16", sinks=True))
+    a = sdpa.decode(x["q"], x["k"], x["v"], causal=True, sinks=x["sinks"])
+    c = sdpa.prefill(x["q"], x["k"], x["v"], causal=True, sinks=x["sinks"])
+    torch.cuda.synchronize()
+    err = (a.float() - c.float()).abs().max().item()
+    say(f"  multi-query decode vs prefill: {err:.3e}")
+    assert err <= 2e-3
