@@ -20,7 +20,7 @@ form with MI355X's published peaks.  ``cpu_baseline`` is the fp64 oracle timed
 on a bounded sample of the same workload on the host cores.
 
 Other workloads (for profiling): --workload dit_fp16|dit_fp32|causal_bf16|
-long_decode_bf16|<gqa8 decode name>.
+long_decode_bf16|<gqa8 decode name>|mq4_gqa8_decode_b1_lk32768_fp16 (multi-query decode).
 """
 from __future__ import annotations
 
@@ -58,7 +58,7 @@ def prefill_flops(w) -> int:
 def decode_bytes(w) -> int:
     es = 4 if w.dtype == "fp32" else 2
     kv = 2 * w.B * w.Hkv * w.Lk * w.D * es
-    qo = 2 * w.B * w.Hq * w.D * es
+    qo = 2 * w.B * w.Hq * w.Lq * w.D * es
     mask = 4 * w.B * w.Lk if w.mask else 0
     return kv + qo + mask
 
@@ -131,16 +131,16 @@ def cpu_baseline_decode(w, budget_s: float = 8.0):
     es = 4 if w.dtype == "fp32" else 2
     units = [(b, hk) for b in range(w.B) for hk in range(w.Hkv)]
     for b, hk in units:
-        q = torch.stack([workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, hk * G + i, 1, w.D, dt)
+        q = torch.stack([workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, hk * G + i, w.Lq, w.D, dt)
                          for i in range(G)])[None]
         k = workloads.slice_normal(w.cfg_id, workloads.TENSOR_K, b, hk, w.Lk, w.D, dt)[None, None]
         v = workloads.slice_normal(w.cfg_id, workloads.TENSOR_V, b, hk, w.Lk, w.D, dt)[None, None]
         mask = workloads.tail_mask(1, w.Lk) if w.mask else None
         t0 = time.perf_counter()
-        sdpa_reference(q, k, v, scale=w.scale, mask=mask)
+        sdpa_reference(q, k, v, scale=w.scale, causal=w.causal, mask=mask)
         t_used += time.perf_counter() - t0
         done += 1
-        nbytes += 2 * w.Lk * w.D * es + 2 * G * w.D * es + (4 * w.Lk if w.mask else 0)
+        nbytes += 2 * w.Lk * w.D * es + 2 * G * w.Lq * w.D * es + (4 * w.Lk if w.mask else 0)
         if t_used >= budget_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -199,10 +199,8 @@ def main():
                           "steps": args.steps + args.warmup}))
         return
     pre_w = workloads.DIT_FP16 if wl == "default" else workloads.ALL[wl]
-    run_prefill = wl == "default" or pre_w.Lq > 1
-    dec_w = workloads.LONG_DECODE if wl == "default" else (pre_w if pre_w.Lq == 1 else None)
-    if wl != "default" and pre_w.Lq == 1:
-        run_prefill = False
+    run_prefill = wl == "default" or not pre_w.is_decode
+    dec_w = workloads.LONG_DECODE if wl == "default" else (pre_w if pre_w.is_decode else None)
 
     print(f"[bench] generating inputs ({wl})", file=sys.stderr, flush=True)
     P = workloads.make_inputs(pre_w, device=dev) if run_prefill else None
@@ -226,8 +224,8 @@ def main():
             if tp: tp.ev[i][1].record()
         if Dd is not None:
             if td: td.ev[i][0].record()
-            sdpa.decode(Dd["q"], Dd["k"], Dd["v"], scale=dec_w.scale, mask=Dd["mask"],
-                        sinks=Dd["sinks"], workspace=ws, out=dec_out)
+            sdpa.decode(Dd["q"], Dd["k"], Dd["v"], scale=dec_w.scale, causal=dec_w.causal,
+                        mask=Dd["mask"], sinks=Dd["sinks"], workspace=ws, out=dec_out)
             if td: td.ev[i][1].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -277,8 +275,9 @@ def main():
                             "traffic": load_traffic("decode_" + dec_w.name),
                             "kernel": "decode_kernel + merge_kernel", "bytes_per_launch": nbytes}}
         cfg["workload"] = (cfg.get("workload", "") + " + " if P is not None else "") + dec_w.name
-        cfg["decode"] = {"B": dec_w.B, "Hq": dec_w.Hq, "Hkv": dec_w.Hkv, "Lk": dec_w.Lk, "D": dec_w.D,
-                         "dtype": dec_w.dtype, "mask": dec_w.mask, "sinks": dec_w.sinks}
+        cfg["decode"] = {"B": dec_w.B, "Hq": dec_w.Hq, "Hkv": dec_w.Hkv, "Lq": dec_w.Lq, "Lk": dec_w.Lk,
+                         "D": dec_w.D, "dtype": dec_w.dtype, "causal": dec_w.causal, "mask": dec_w.mask,
+                         "sinks": dec_w.sinks}
         if P is None:
             res.update(value=dec["value"], unit="GB/s", dtype=dec_w.dtype, roofline=dec["roofline"])
         res["decode"] = dec

@@ -164,3 +164,16 @@ def test_multi_query_matches_prefill():
     err = (a.float() - c.float()).abs().max().item()
     say(f"  multi-query decode vs prefill: {err:.3e}")
     assert err <= 2e-3
+
+
+@pytest.mark.timeout(600)
+def test_multi_query_full_size():
+    # the bench workload (4 causal query rows, GQA-8 D512, Lk 32768) in the
+    # launch configuration bench.py times (automatic splits), all heads
+    w = workloads.MQ_DECODE
+    say("multi-query decode full size", w)
+    x = workloads.make_inputs(w)
+    d = to_dev(x)
+    out, l = sdpa.decode(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, return_lse=True)
+    torch.cuda.synchronize()
+    compare_full(out, l, x, w.scale, w.dtype, f"{w.name} auto", causal=w.causal)

@@ -59,6 +59,11 @@ class Workload:
     sinks: bool = False
     sink_scale: float = 1.0
     lse: bool = False
+    decode: bool = False           # run through sdpa_decode (always so when Lq == 1)
+
+    @property
+    def is_decode(self) -> bool:
+        return self.decode or self.Lq == 1
 
     @property
     def scale(self) -> float:
@@ -92,8 +97,14 @@ GQA_DECODE = [gqa_decode(B, Lk, dt, s)
               for Lk in (1024, 8192, 32768) for B in (1, 2)
               for dt in ("fp16", "bf16", "fp32") for s in (False, True)]
 
+# Multi-query decode (next-row extension, not one of the five families): the
+# GQA-8 D512 shape with a block of 4 query rows per head, causal within the
+# block -- the qL4 control of the D512 page, i.e. speculative decoding.
+MQ_DECODE = Workload("mq4_gqa8_decode_b1_lk32768_fp16", 6, B=1, Hq=32, Hkv=4, Lq=4, Lk=32768,
+                     D=512, dtype="fp16", causal=True, decode=True)
+
 ALL: Dict[str, Workload] = {w.name: w for w in
-                            [TINY, DIT_FP16, DIT_FP32, CAUSAL, LONG_DECODE, *GQA_DECODE]}
+                            [TINY, DIT_FP16, DIT_FP32, CAUSAL, LONG_DECODE, *GQA_DECODE, MQ_DECODE]}
 
 
 # ---- generators --------------------------------------------------------------
