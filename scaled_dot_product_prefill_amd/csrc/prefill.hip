@@ -441,8 +441,10 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   }
   // bf16 probabilities carry 8 significant bits; rows that average few keys
   // would show that rounding directly in O, so such workgroups feed P.V with
-  // P = hi + lo (two bf16 products).  Many-key rows average it away.
-  const bool split_p = std::is_same<T, TBF16>::value && (MASK || kend <= 1024);
+  // P = hi + lo (two bf16 products).  Rows past 256 keys average it away
+  // (the row sum adds the same rounded probabilities, so only the relative
+  // weights are perturbed, by ~2^-9 / sqrt(keys)).
+  const bool split_p = std::is_same<T, TBF16>::value && (MASK || kend <= 256);
 
   // ---- direct buffer -> LDS loads.  Wave w fills lines w, w + NW, ... of a
   // tile; line i of a wave sits i * STEP_ROWS rows below line 0 and both
