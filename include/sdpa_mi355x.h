@@ -122,7 +122,8 @@ typedef struct sdpa_args {
 } sdpa_args;
 
 /* Prefill / full self-attention, any Lq >= 1, Lk >= 1.
- * Supported: D in {64, 128}; dtype F32, F16, BF16.  One kernel launch. */
+ * Supported: D in {64, 128} for F32, F16 and BF16; D = 256 for F16 and BF16.
+ * One kernel launch. */
 SDPA_API int sdpa_prefill(const sdpa_args *args, void *stream);
 
 /* Host-only validation of a prefill request (no GPU work, no HIP calls).

@@ -139,8 +139,9 @@ int check_common(const sdpa_args* a) {
 int check_prefill(const sdpa_args* a) {
   int st = check_common(a);
   if (st != SDPA_OK) return st;
-  if (a->D != 64 && a->D != 128)
-    return fail(SDPA_ERR_UNSUPPORTED, "prefill supports D in {64, 128}, got %lld", (long long)a->D);
+  if (a->D != 64 && a->D != 128 && !(a->D == 256 && a->dtype != SDPA_F32))
+    return fail(SDPA_ERR_UNSUPPORTED, "prefill supports D in {64, 128} (and 256 for fp16/bf16), got %lld",
+                (long long)a->D);
   const int64_t grid = ((a->Lq + 127) / 128) * a->B * a->Hq;
   if (grid > kMaxInt) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
   return SDPA_OK;

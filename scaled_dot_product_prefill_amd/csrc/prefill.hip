@@ -351,7 +351,10 @@ struct Cfg16 {
   static constexpr int NQ = D / 16;             // 16-byte Q vectors per lane
   static constexpr int NMB = D / 32;            // 32-row blocks of O^T
   static_assert(LINES % NW == 0, "tile lines");
-  static_assert(STEP_ROWS % 16 == 0, "swizzle period");
+  // lines i and i + KVAR of a wave share the K swizzle (period 16 rows)
+  static constexpr int KVAR = STEP_ROWS % 16 == 0 ? 1 : 16 / STEP_ROWS;
+  static_assert(KVAR == 1 || KVAR == 2, "swizzle period");
+  static_assert(STEP_ROWS % 4 == 0, "V swizzle period");
 };
 
 // The reference max is only moved (and O, l rescaled) when a row's tile max
@@ -451,11 +454,15 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // swizzles repeat every 16 rows: one per-lane offset plus a uniform step.
   const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
   const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
-  uint32_t koff, voff;
+  uint32_t koff[C::KVAR], voff;
   {
     const int pos = wave * 64 + lane;  // 16-byte slot of line 0
     const int row = pos / C::NCH, pch = pos % C::NCH;
-    koff = (uint32_t)(row * p.ks[2] * 2 + (pch ^ swz_k<C::NCH>(row)) * 16);
+#pragma unroll
+    for (int k = 0; k < C::KVAR; ++k) {
+      const int rk = row + k * C::STEP_ROWS;  // a line KVAR steps further repeats it
+      koff[k] = (uint32_t)(row * p.ks[2] * 2 + (pch ^ swz_k<C::NCH>(rk)) * 16);
+    }
     voff = (uint32_t)(row * p.vs[2] * 2 + (pch ^ swz_v<C::NCH>(row)) * 16);
   }
   const uint32_t krow = (uint32_t)(p.ks[2] * 2), vrow = (uint32_t)(p.vs[2] * 2);
@@ -465,17 +472,17 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     const int rows = p.Lk - j0;
     return rows >= C::BN ? 0xffffffffu : (uint32_t)(rows - 1) * rowb + C::RB;
   };
-  auto issue = [&](const S* base, int64_t rs, uint32_t rowb, uint32_t off, uint32_t step, uint8_t* st,
-                   int t) {
+  auto issue = [&](const S* base, int64_t rs, uint32_t rowb, const uint32_t* off, int noff, uint32_t step,
+                   uint8_t* st, int t) {
     const int j0 = t * C::BN;
     const S* tb = base + (int64_t)j0 * rs;
     const uint32_t nb = tile_bytes(j0, rowb);
     const uint32_t la = lds_addr(st) + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < C::LPW; ++i) dma16(tb, nb, la + NW * i * 1024, off, i * step);
+    for (int i = 0; i < C::LPW; ++i) dma16(tb, nb, la + NW * i * 1024, off[i % noff], i * step);
   };
-  auto issue_k = [&](int t, uint8_t* st) { issue(kbase, p.ks[2], krow, koff, kstep, st, t); };
-  auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, voff, vstep, st, t); };
+  auto issue_k = [&](int t, uint8_t* st) { issue(kbase, p.ks[2], krow, koff, C::KVAR, kstep, st, t); };
+  auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, &voff, 1, vstep, st, t); };
 
   // ---- per-lane LDS read offsets
   const uint32_t k_lane = l32 * C::RB;                 // + (32 kb) rows
@@ -746,16 +753,18 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     }
   };
   int t = 0;
-  const int n_steady = split_p ? 0 : max(0, min(n_int - 1, ntiles - 2));
-  for (; t + 1 < n_steady; t += 2) {
-    steady(t, std::integral_constant<int, 0>{}, sa, sb);
-    steady(t + 1, std::integral_constant<int, 1>{}, sb, sa);
-  }
-  if (t < n_steady) {
-    steady(t, std::integral_constant<int, 0>{}, sa, sb);
+  if constexpr (D <= 128) {
+    const int n_steady = split_p ? 0 : max(0, min(n_int - 1, ntiles - 2));
+    for (; t + 1 < n_steady; t += 2) {
+      steady(t, std::integral_constant<int, 0>{}, sa, sb);
+      steady(t + 1, std::integral_constant<int, 1>{}, sb, sa);
+    }
+    if (t < n_steady) {
+      steady(t, std::integral_constant<int, 0>{}, sa, sb);
 #pragma unroll
-    for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
-    ++t;
+      for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
+      ++t;
+    }
   }
   for (; t < n_int; ++t) general(t, std::false_type{});
   for (; t < ntiles; ++t) general(t, std::true_type{});
@@ -792,7 +801,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
 // masked variants keep a second score tile plus the mask gathers live across
 // the pipeline and get the whole register file.
 template <class T, int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(64 * NW, 2) void prefill16_kernel(AttnParams p) {
+__global__ __launch_bounds__(64 * NW, D >= 256 ? 1 : 2) void prefill16_kernel(AttnParams p) {
   prefill16_body<T, D, CAUSAL, false, NW>(p);
 }
 template <class T, int D, bool CAUSAL>
@@ -831,13 +840,24 @@ hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class T>
+hipError_t launch_d(const AttnParams& p, bool causal, hipStream_t s) {
+  switch (p.D) {
+    case 64: return launch_t<T, 64>(p, causal, s);
+    case 128: return launch_t<T, 128>(p, causal, s);
+    default:
+      if constexpr (std::is_same<T, TF32>::value) return hipErrorInvalidValue;  // rejected by the API
+      else return launch_t<T, 256>(p, causal, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const AttnParams& p, int dtype, bool causal, hipStream_t s) {
   switch (dtype) {
-    case SDPA_F32: return p.D == 64 ? launch_t<TF32, 64>(p, causal, s) : launch_t<TF32, 128>(p, causal, s);
-    case SDPA_F16: return p.D == 64 ? launch_t<TF16, 64>(p, causal, s) : launch_t<TF16, 128>(p, causal, s);
-    default: return p.D == 64 ? launch_t<TBF16, 64>(p, causal, s) : launch_t<TBF16, 128>(p, causal, s);
+    case SDPA_F32: return launch_d<TF32>(p, causal, s);
+    case SDPA_F16: return launch_d<TF16>(p, causal, s);
+    default: return launch_d<TBF16>(p, causal, s);
   }
 }
 

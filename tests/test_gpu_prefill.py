@@ -58,6 +58,24 @@ def test_prefill_grid(dtype, D, case):
     compare_full(out, l, x, sc, dtype, f"grid{case}-{dtype}-D{D}", causal=causal)
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("case", range(len(GRID)))
+def test_prefill_grid_d256(dtype, case):
+    # head dim 256: 16-bit inputs only
+    B, Hq, Hkv, Lq, Lk, causal, mask, sinks = GRID[case]
+    say(f"prefill grid {dtype} D=256 case={GRID[case]}")
+    x = random_case(3000 + 10 * case, B, Hq, Hkv, Lq, Lk, 256, dtype, mask=mask, sinks=sinks,
+                    sink_scale=2.0, mask_neg_inf_frac=0.1)
+    out, l, sc = _run(x, dtype, causal=causal)
+    compare_full(out, l, x, sc, dtype, f"grid{case}-{dtype}-D256", causal=causal)
+
+
+def test_d256_long_causal_sampled():
+    # head dim 256 over 32 key tiles: steady state, rescales, ragged causal edge
+    w = workloads.CAUSAL.with_(name="causal_bf16_d256", B=1, Hq=4, Hkv=2, Lq=2048, Lk=2048, D=256)
+    _full_size(w, heads=[(0, 0), (0, 3)], rows=[0, 1, 63, 64, 127, 128, 1000, 2047])
+
+
 def _full_size(w, heads, rows):
     say("full size", w)
     x = workloads.make_inputs(w)
@@ -165,6 +183,10 @@ def test_gqa_equals_repeated_kv():
 
 def test_rejects_unsupported():
     x = to_dev(random_case(2008, 1, 2, 2, 8, 8, 96, "fp16"))
+    with pytest.raises(sdpa.SdpaError) as e:
+        sdpa.prefill(x["q"], x["k"], x["v"])
+    assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
+    x = to_dev(random_case(2009, 1, 2, 2, 8, 8, 256, "fp32"))   # D = 256 is 16-bit only
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.prefill(x["q"], x["k"], x["v"])
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
