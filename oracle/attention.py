@@ -25,7 +25,14 @@ notes):
     adds exp(sink) to the softmax denominator only;
   * the log-sum-exp output is natural-log and includes the sink term;
   * a row with no visible key and no sink yields O = 0 and LSE = -inf;
-  * scale multiplies the dot product (in fp64 here), then the mask is added.
+  * scale multiplies the dot product (in fp64 here), then the mask is added;
+  * per-batch lengths (the padding mask that ``build_sdpa_graph`` turns on
+    with ``set_seq_len_q`` / ``set_seq_len_kv``): batch b has its first
+    seq_len_q[b] query rows and seq_len_kv[b] keys (clamped to [0, Lq] and
+    [0, Lk]); the rest is padding.  A padding key is seen by no row; a
+    padding row sees no key (so it is written as an empty row); bottom-right
+    causal alignment uses the batch's own lengths:
+    j <= i + (seq_len_kv[b] - seq_len_q[b]).
 
 Steps per (b, hq), g = hq // G, in the order of the definition:
   1. convert the inputs exactly to fp64;
@@ -55,12 +62,15 @@ def _f64(x) -> np.ndarray:
 
 def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
                    mask=None, sinks=None, rows: Optional[Sequence[int]] = None,
-                   heads: Optional[Sequence[Tuple[int, int]]] = None
+                   heads: Optional[Sequence[Tuple[int, int]]] = None,
+                   seqlens_q=None, seqlens_k=None
                    ) -> Tuple[np.ndarray, np.ndarray]:
     """Naive attention in fp64.
 
     q: [B, Hq, Lq, D]; k, v: [B, Hkv, Lk, D]; mask: anything broadcastable to
-    [B, Hq, Lq, Lk] (additive, may hold -inf); sinks: [Hq] or None.
+    [B, Hq, Lq, Lk] (additive, may hold -inf); sinks: [Hq] or None;
+    seqlens_q, seqlens_k: per-batch valid lengths [B] or None (= Lq, Lk).
+    Padding entries of q, k and v are never read, so they may hold anything.
 
     ``rows`` restricts the computation to those query indices (same for every
     head); ``heads`` restricts it to those (b, hq) pairs.  The result then has
@@ -86,18 +96,27 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
     O = np.zeros((len(pairs), len(row_idx), D))
     LSE = np.full((len(pairs), len(row_idx)), -np.inf)
 
-    # causal visibility, bottom-right aligned: j <= i + (Lk - Lq)
-    if causal:
-        hidden = np.arange(Lk)[None, :] > (row_idx[:, None] + (Lk - Lq))
+    def lengths(b):
+        lq = Lq if seqlens_q is None else min(max(int(_f64(seqlens_q)[b]), 0), Lq)
+        lk = Lk if seqlens_k is None else min(max(int(_f64(seqlens_k)[b]), 0), Lk)
+        return lq, lk
 
     for n, (b, hq) in enumerate(pairs):
         g = hq // G                                   # KV head of this query head
-        # step 2: explicit score matrix
-        S = scale * (Q[b, hq, row_idx, :] @ K[b, g].T)
+        lq, lk = lengths(b)
+        real = row_idx < lq                           # non-padding query rows
+        # step 2: explicit score matrix over the batch's own keys; padding
+        # rows see no key
+        S = scale * (np.where(real[:, None], Q[b, hq, row_idx, :], 0.0) @ K[b, g, :lk].T)
         if M is not None:
-            S = S + M[b, hq][row_idx, :]
+            S = S + M[b, hq][row_idx, :lk]
+        hidden = ~real[:, None] & np.ones((1, lk), dtype=bool)
         if causal:
-            S = np.where(hidden, -np.inf, S)
+            # bottom-right aligned on the batch's lengths: j <= i + (lk - lq)
+            hidden |= np.arange(lk)[None, :] > (row_idx[:, None] + (lk - lq))
+        S = np.where(hidden, -np.inf, S)
+        if lk == 0:
+            S = np.full((len(row_idx), 1), -np.inf)    # no key at all
         # step 3: row max, including the sink logit
         m = S.max(axis=1)
         if S_ is not None:
@@ -110,8 +129,9 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
         if S_ is not None:
             den = den + np.exp(S_[hq] - m_safe)
         # step 5: normalise; empty rows stay O = 0, LSE = -inf
+        Vb = V[b, g, :lk] if lk > 0 else np.zeros((1, D))
         with np.errstate(divide="ignore", invalid="ignore"):
-            O[n] = np.where(live[:, None], (e @ V[b, g]) / den[:, None], 0.0)
+            O[n] = np.where(live[:, None], (e @ Vb) / den[:, None], 0.0)
             LSE[n] = np.where(live, m_safe + np.log(den), -np.inf)
 
     if heads is None:

@@ -20,7 +20,8 @@ def _np(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def brute_attention(q, k, v, scale, causal=False, mask=None, sinks=None, dps=50):
+def brute_attention(q, k, v, scale, causal=False, mask=None, sinks=None, dps=50,
+                    seqlens_q=None, seqlens_k=None):
     mp.mp.dps = dps
     Q, K, V = _np(q), _np(k), _np(v)
     B, Hq, Lq, D = Q.shape
@@ -32,15 +33,18 @@ def brute_attention(q, k, v, scale, causal=False, mask=None, sinks=None, dps=50)
     LSE = np.zeros((B, Hq, Lq))
     sc = mp.mpf(float(scale))
     for b in range(B):
+        # this batch's query block and key block (the leading rows / keys)
+        nq = Lq if seqlens_q is None else sorted((0, int(seqlens_q[b]), Lq))[1]
+        nk = Lk if seqlens_k is None else sorted((0, int(seqlens_k[b]), Lk))[1]
         for h in range(Hq):
             kv = h // group
             for i in range(Lq):
                 weights = []
-                for j in range(Lk):
+                for j in range(nk if i < nq else 0):
                     # a query at position i (counted from the end of the query
                     # block) may look at keys no later than its own position
                     # counted from the end of the key block
-                    if causal and (Lk - 1 - j) < (Lq - 1 - i):
+                    if causal and (nk - 1 - j) < (nq - 1 - i):
                         continue
                     add = mp.mpf(0)
                     if M is not None:

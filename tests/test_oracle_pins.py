@@ -280,8 +280,63 @@ def pin_split_merge(ref):
     _close(wa * Oa + wb * Ob, O, 1e-13, "merge O")
 
 
+SEQLEN_CASES = [
+    # (B, Hq, Hkv, Lq, Lk, D, causal, mask, sinks, seqlens_q, seqlens_k)
+    (3, 2, 1, 4, 6, 3, True, False, False, [4, 2, 3], [6, 3, 5]),
+    (3, 2, 2, 3, 5, 4, False, True, True, [3, 0, 1], [0, 5, 2]),   # empty batches
+    (2, 4, 2, 1, 7, 4, False, False, True, [1, 1], [7, 4]),         # decode shape
+    (2, 2, 1, 5, 4, 2, True, False, True, [5, 2], [2, 4]),          # lq_b > lk_b
+]
+
+
+def pin_seqlens(ref):
+    """Per-batch lengths (padding masks): brute force on tiny shapes, padding
+    equal to truncation, and padding contents never read."""
+    for n, (B, Hq, Hkv, Lq, Lk, D, causal, mask, sinks, sq, sk) in enumerate(SEQLEN_CASES):
+        x = random_case(150 + n, B, Hq, Hkv, Lq, Lk, D, "fp32", mask=mask, sinks=sinks,
+                        sink_scale=2.0, mask_neg_inf_frac=0.2)
+        sq_, sk_ = np.array(sq), np.array(sk)
+        kw = dict(scale=0.8, causal=causal, mask=x["mask"], sinks=x["sinks"])
+        O, L = ref(x["q"], x["k"], x["v"], seqlens_q=sq_, seqlens_k=sk_, **kw)
+        Ob, Lb = brute_attention(x["q"], x["k"], x["v"], 0.8, causal, x["mask"], x["sinks"],
+                                 seqlens_q=sq, seqlens_k=sk)
+        _close(O, Ob, 1e-12, f"seqlens brute {n} O")
+        _close(L, Lb, 1e-12, f"seqlens brute {n} LSE")
+        for b in range(B):
+            lq, lk = sq[b], sk[b]
+            if lq == 0 or lk == 0:
+                continue
+            m = None if x["mask"] is None else x["mask"][b:b + 1, :, :lq, :lk]
+            Ot, Lt = ref(x["q"][b:b + 1, :, :lq], x["k"][b:b + 1, :, :lk], x["v"][b:b + 1, :, :lk],
+                         scale=0.8, causal=causal, mask=m, sinks=x["sinks"])
+            _close(O[b, :, :lq], Ot[0], 1e-14, f"seqlens truncation {n}.{b} O")
+            _close(L[b, :, :lq], Lt[0], 1e-14, f"seqlens truncation {n}.{b} LSE")
+        # padding rows are empty rows: O = 0, LSE = sink or -inf
+        for b in range(B):
+            assert np.all(O[b, :, sq[b]:] == 0.0)
+            want = -np.inf if x["sinks"] is None else np.asarray(x["sinks"], np.float64)[:, None]
+            _close(L[b, :, sq[b]:], np.broadcast_to(want, L[b, :, sq[b]:].shape), 0, "padding row LSE")
+        # garbage in the padding changes nothing
+        q2, k2, v2 = x["q"].clone(), x["k"].clone(), x["v"].clone()
+        for b in range(B):
+            q2[b, :, sq[b]:] = float("nan")
+            k2[b, :, sk[b]:] = 1e30
+            v2[b, :, sk[b]:] = float("nan")
+        O2, L2 = ref(q2, k2, v2, seqlens_q=sq_, seqlens_k=sk_, **kw)
+        _close(O2, O, 0, f"seqlens garbage {n} O")
+        _close(L2, L, 0, f"seqlens garbage {n} LSE")
+    # lengths at the tensor extents equal no lengths at all
+    x = random_case(160, 2, 2, 2, 4, 6, 3, "fp32", mask=True, sinks=True)
+    kw = dict(scale=0.8, causal=True, mask=x["mask"], sinks=x["sinks"])
+    O, L = ref(x["q"], x["k"], x["v"], **kw)
+    O2, L2 = ref(x["q"], x["k"], x["v"], seqlens_q=np.array([4, 9]), seqlens_k=np.array([6, 6]), **kw)
+    _close(O2, O, 0, "full lengths O")
+    _close(L2, L, 0, "full lengths LSE")
+
+
 PINS = [pin_hand_examples, pin_brute_force, pin_torch_sdpa, pin_torch_lse,
-        pin_probabilities, pin_invariants, pin_gqa_equals_repeat, pin_split_merge]
+        pin_probabilities, pin_invariants, pin_gqa_equals_repeat, pin_split_merge,
+        pin_seqlens]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -320,15 +375,18 @@ def test_d512_grid_covers_page_cases():
 # ---------------------------------------------------------------------------
 
 MUTANTS = {
-    "causal_top_left": ("(row_idx[:, None] + (Lk - Lq))", "(row_idx[:, None])"),
-    "causal_off_by_one": ("hidden = np.arange(Lk)[None, :] >", "hidden = np.arange(Lk)[None, :] >="),
+    "causal_top_left": ("(row_idx[:, None] + (lk - lq))", "(row_idx[:, None])"),
+    "causal_off_by_one": ("hidden |= np.arange(lk)[None, :] >", "hidden |= np.arange(lk)[None, :] >="),
+    "causal_on_tensor_extents": ("(row_idx[:, None] + (lk - lq))", "(row_idx[:, None] + (Lk - Lq))"),
+    "padding_rows_see_keys": ("real = row_idx < lq ", "real = row_idx < Lq "),
+    "padding_keys_seen": ("int(_f64(seqlens_k)[b])", "int(_f64(seqlens_k)[b]) + 1"),
     "sink_not_in_denominator": ("den = den + np.exp(S_[hq] - m_safe)", "den = den"),
     "sink_not_in_max": ("m = np.maximum(m, S_[hq])", "m = m"),
     "head_map_modulo": ("        g = hq // G ", "        g = hq % Hkv "),
     "scale_dropped": ("S = scale * (", "S = ("),
-    "mask_sign": ("S = S + M[b, hq][row_idx, :]", "S = S - M[b, hq][row_idx, :]"),
+    "mask_sign": ("S = S + M[b, hq][row_idx, :lk]", "S = S - M[b, hq][row_idx, :lk]"),
     "lse_without_max": ("m_safe + np.log(den), -np.inf", "np.log(den), -np.inf"),
-    "values_from_keys": ("(e @ V[b, g])", "(e @ K[b, g])"),
+    "values_from_keys": ("Vb = V[b, g, :lk]", "Vb = K[b, g, :lk]"),
     "exp_sign": ("e = np.exp(S - m_safe[:, None])", "e = np.exp(m_safe[:, None] - S)"),
     "lse_log2": ("m_safe + np.log(den)", "m_safe + np.log2(den)"),
 }
