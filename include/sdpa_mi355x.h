@@ -37,6 +37,16 @@
  *     the sink term);
  *   - a row that sees no key and has no sink gets O = 0 and lse = -inf; a row
  *     that sees no key but has a sink gets O = 0 and lse = sink.
+ *   - per-batch lengths (optional; the padding mask of the cuDNN graph on the
+ *     mlx 0.30.7 page: set_padding_mask with set_seq_len_q / set_seq_len_kv):
+ *     batch b holds seqlens_q[b] real query rows and seqlens_k[b] real keys,
+ *     the leading ones of its L extents (values are clamped to [0, Lq] and
+ *     [0, Lk]; a NULL array means the full extent).  Keys past seqlens_k[b]
+ *     are seen by no row and never read into a result (their memory may hold
+ *     anything, e.g. the unused tail of a fixed-capacity KV cache); query rows
+ *     past seqlens_q[b] see no key and are written like any row that sees no
+ *     key; causal alignment uses the batch's own lengths:
+ *     j <= i + (seqlens_k[b] - seqlens_q[b]).
  *   - fp32 inputs are computed in full fp32 (no reduced-precision products).
  *
  * Memory, ownership, threading:
@@ -59,6 +69,11 @@
  *   - sinks (optional) is fp32 [Hq], contiguous (the cuDNN path on the mlx
  *     page converts sinks to float32 in prepare_sdpa_sinks).
  *   - lse (optional output) is fp32 [B, Hq, Lq], contiguous.
+ *   - seqlens_q / seqlens_k (optional) are int32 [B] device arrays, 4-byte
+ *     aligned, read by the kernels (the host never reads them).  A
+ *     fixed-capacity KV cache [B, Hkv, T, D] is passed as it is, no copy:
+ *     Lk = T, or any Lk <= T with the head stride still T * D, plus
+ *     seqlens_k for the fill level of each batch.
  *   - o must not overlap q, k, v, mask, sinks or lse.
  *
  * Errors: every argument is checked on the host BEFORE anything is enqueued;
@@ -78,7 +93,7 @@
 extern "C" {
 #endif
 
-#define SDPA_MI355X_ABI_VERSION 1
+#define SDPA_MI355X_ABI_VERSION 2
 
 #ifndef SDPA_API
 #define SDPA_API __attribute__((visibility("default")))
@@ -119,6 +134,8 @@ typedef struct sdpa_args {
   const float *mask; int64_t mask_stride[4]; /* optional [B, Hq, Lq, Lk] fp32 */
   const float *sinks;                        /* optional [Hq] fp32            */
   float *lse;                                /* optional [B, Hq, Lq] fp32 out */
+  const int32_t *seqlens_q;                  /* optional [B] real query rows  */
+  const int32_t *seqlens_k;                  /* optional [B] real keys        */
 } sdpa_args;
 
 /* Prefill / full self-attention, any Lq >= 1, Lk >= 1.

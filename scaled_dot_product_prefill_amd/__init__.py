@@ -4,11 +4,14 @@ Argument marshalling only: every step of the attention runs in the HIP
 kernels of the library.  PyTorch supplies device memory and the stream.  When
 the library is missing, every entry point raises -- there is no CPU path.
 
-    prefill(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False)
-    decode(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False, num_splits=0)
+    prefill(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False,
+            seqlens_q=None, seqlens_k=None)
+    decode(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False,
+           num_splits=0, seqlens_q=None, seqlens_k=None)
 
 q: [B, Hq, Lq, D], k / v: [B, Hkv, Lk, D] (float32, float16 or bfloat16),
-mask: additive float tensor broadcastable to [B, Hq, Lq, Lk], sinks: [Hq].
+mask: additive float tensor broadcastable to [B, Hq, Lq, Lk], sinks: [Hq],
+seqlens_q / seqlens_k: per-batch real query rows / keys [B] (padding masks).
 Returns O ([B, Hq, Lq, D], dtype of q) or (O, LSE) with LSE fp32 [B, Hq, Lq].
 """
 from __future__ import annotations
@@ -56,6 +59,8 @@ class SdpaArgs(ctypes.Structure):
         ("mask", ctypes.c_void_p), ("mask_stride", ctypes.c_int64 * 4),
         ("sinks", ctypes.c_void_p),
         ("lse", ctypes.c_void_p),
+        ("seqlens_q", ctypes.c_void_p),
+        ("seqlens_k", ctypes.c_void_p),
     ]
 
 
@@ -122,7 +127,7 @@ def _fill(a: SdpaArgs, name: str, t: Optional[torch.Tensor]):
             st[i] = t.stride(i)
 
 
-def _make_args(q, k, v, o, scale, causal, mask, sinks, lse) -> SdpaArgs:
+def _make_args(q, k, v, o, scale, causal, mask, sinks, lse, seqlens_q=None, seqlens_k=None) -> SdpaArgs:
     B, Hq, Lq, D = q.shape
     a = SdpaArgs()
     a.B, a.Hq, a.Lq, a.D = B, Hq, Lq, D
@@ -139,7 +144,19 @@ def _make_args(q, k, v, o, scale, causal, mask, sinks, lse) -> SdpaArgs:
             a.mask_stride[i] = mask.stride(i)
     a.sinks = sinks.data_ptr() if sinks is not None else None
     a.lse = lse.data_ptr() if lse is not None else None
+    a.seqlens_q = seqlens_q.data_ptr() if seqlens_q is not None else None
+    a.seqlens_k = seqlens_k.data_ptr() if seqlens_k is not None else None
     return a
+
+
+def _lengths(x, B: int, device, name: str):
+    """Per-batch lengths as a contiguous int32 [B] tensor on the device."""
+    if x is None:
+        return None
+    t = torch.as_tensor(x).to(device=device, dtype=torch.int32).reshape(-1).contiguous()
+    if t.numel() != B:
+        raise ValueError(f"{name} must have B = {B} entries, got {t.numel()}")
+    return t
 
 
 def _common(q, k, v, scale, mask, sinks, Lq_expected=None):
@@ -168,14 +185,18 @@ def _common(q, k, v, scale, mask, sinks, Lq_expected=None):
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
             causal: bool = False, mask: Optional[torch.Tensor] = None,
             sinks: Optional[torch.Tensor] = None, return_lse: bool = False,
-            out: Optional[torch.Tensor] = None):
-    """Fused attention forward over a whole query block (prefill / full self-attention)."""
+            out: Optional[torch.Tensor] = None, seqlens_q=None, seqlens_k=None):
+    """Fused attention forward over a whole query block (prefill / full
+    self-attention).  seqlens_q / seqlens_k: real query rows / keys of each
+    batch (the rest is padding; padding rows come out as rows with no key)."""
     lib = library()
     q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
-    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse)
+    sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
+    sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
+    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib.sdpa_prefill(ctypes.byref(a), ctypes.c_void_p(stream))
     if st != 0:
@@ -212,16 +233,21 @@ def _size_args(q, k) -> SdpaArgs:
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
            causal: bool = False, mask: Optional[torch.Tensor] = None,
            sinks: Optional[torch.Tensor] = None, return_lse: bool = False, num_splits: int = 0,
-           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None):
+           workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+           seqlens_q=None, seqlens_k=None):
     """Decode attention: one query row (Lq == 1) or a few (Lq <= 16, bottom-right
     causal within the block when ``causal``).  num_splits: 0 automatic,
-    1 single-pass kernel, n >= 2 two-pass split-K with n key ranges."""
+    1 single-pass kernel, n >= 2 two-pass split-K with n key ranges.
+    seqlens_k: fill level of each batch's KV cache (k, v may be the whole
+    fixed-capacity cache); seqlens_q: real query rows of each batch."""
     lib = library()
     q, k, v, scale, mask, sinks = _decode_args(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
     o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
-    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse)
+    sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
+    sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
+    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
     need = int(lib.sdpa_decode_workspace_bytes(ctypes.byref(a), int(num_splits)))
     if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

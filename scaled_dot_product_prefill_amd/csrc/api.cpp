@@ -110,6 +110,10 @@ int check_common(const sdpa_args* a) {
       if (a->mask_stride[d] < 0) return fail(SDPA_ERR_ARG, "mask stride %d is negative", d);
   }
   if (a->sinks && (uintptr_t)a->sinks % 4 != 0) return fail(SDPA_ERR_ALIGN, "sinks is not 4-byte aligned");
+  if (a->seqlens_q && (uintptr_t)a->seqlens_q % 4 != 0)
+    return fail(SDPA_ERR_ALIGN, "seqlens_q is not 4-byte aligned");
+  if (a->seqlens_k && (uintptr_t)a->seqlens_k % 4 != 0)
+    return fail(SDPA_ERR_ALIGN, "seqlens_k is not 4-byte aligned");
   if (a->lse && (uintptr_t)a->lse % 4 != 0) return fail(SDPA_ERR_ALIGN, "lse is not 4-byte aligned");
 
   // the output must not overlap any input or the other output
@@ -125,13 +129,16 @@ int check_common(const sdpa_args* a) {
     em.hi = em.lo + (uintptr_t)(last * 4);
     em.valid = true;
   }
-  Extent es_, el;
+  Extent es_, el, esq, esk;
   if (a->sinks) { es_.lo = (uintptr_t)a->sinks; es_.hi = es_.lo + a->Hq * 4; es_.valid = true; }
   if (a->lse) { el.lo = (uintptr_t)a->lse; el.hi = el.lo + a->B * a->Hq * a->Lq * 4; el.valid = true; }
+  if (a->seqlens_q) { esq.lo = (uintptr_t)a->seqlens_q; esq.hi = esq.lo + a->B * 4; esq.valid = true; }
+  if (a->seqlens_k) { esk.lo = (uintptr_t)a->seqlens_k; esk.hi = esk.lo + a->B * 4; esk.valid = true; }
   if (overlaps(eo, eq) || overlaps(eo, ek) || overlaps(eo, ev) || overlaps(eo, em) ||
-      overlaps(eo, es_) || overlaps(eo, el))
+      overlaps(eo, es_) || overlaps(eo, el) || overlaps(eo, esq) || overlaps(eo, esk))
     return fail(SDPA_ERR_ARG, "o overlaps an input or lse");
-  if (overlaps(el, eq) || overlaps(el, ek) || overlaps(el, ev) || overlaps(el, em) || overlaps(el, es_))
+  if (overlaps(el, eq) || overlaps(el, ek) || overlaps(el, ev) || overlaps(el, em) || overlaps(el, es_) ||
+      overlaps(el, esq) || overlaps(el, esk))
     return fail(SDPA_ERR_ARG, "lse overlaps an input");
   return SDPA_OK;
 }
@@ -243,7 +250,9 @@ AttnParams make_params(const sdpa_args& a) {
   p.B = (int)a.B; p.Hq = (int)a.Hq; p.Hkv = (int)a.Hkv;
   p.Lq = (int)a.Lq; p.Lk = (int)a.Lk; p.D = (int)a.D;
   p.group = (int)(a.Hq / a.Hkv);
-  p.causal_off = (int)(a.Lk - a.Lq);
+  p.causal = a.causal;
+  p.seqlens_q = a.seqlens_q;
+  p.seqlens_k = a.seqlens_k;
   p.scale_log2 = a.scale * 1.4426950408889634f;
   p.nsplit = 1;
   p.nchunk = 1;
@@ -292,7 +301,6 @@ int sdpa_decode(const sdpa_args* args, int num_splits, void* workspace, size_t w
   p.nsplit = sp.nsplit;
   p.split_len = sp.split_len;
   p.nchunk = (int)sdpa::decode_chunks(args);
-  if (!args->causal) p.causal_off = p.Lk;  // every key visible to every query row
   if (sp.nsplit > 1) {
     float* ws = (float*)workspace;
     p.part_o = ws;
@@ -317,6 +325,6 @@ const char* sdpa_status_string(int status) {
 
 const char* sdpa_last_error(void) { return sdpa::g_last_error.c_str(); }
 
-const char* sdpa_version(void) { return "sdpa_mi355x abi 1, gfx950 (CDNA4)"; }
+const char* sdpa_version(void) { return "sdpa_mi355x abi 2, gfx950 (CDNA4)"; }
 
 }  // extern "C"

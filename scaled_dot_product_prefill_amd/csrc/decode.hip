@@ -35,13 +35,15 @@ constexpr int kThreads = 64 * kWaves;
 // index = ((b * Hkv + hk) * nchunk + chunk) * nsplit + split.  The G query
 // heads of the KV head times the Lq query rows form the columns of the 16x16
 // tiles, column c = qi * G + h, 16 per chunk; lane column n is c = 16 chunk + n.
-// Query row qi sees keys j <= causal_off + qi (bottom-right causal; without
-// causal masking causal_off is Lk, so every key passes).
+// The batch has lk real keys and lq real query rows (per-batch lengths, else
+// Lk and Lq).  Query row qi < lq sees keys j < lk with j <= lk - lq + qi
+// under bottom-right causal masking; rows from lq on see no key.
 struct DecodeUnit {
   int split, hk, b;
   bool ok;        // lane column is a real (query row, head)
   int hq, qi;     // its query head and query row (0 for padding columns)
-  int last_key;   // last visible key of that row
+  int lk;         // real keys of the batch
+  int last_key;   // last visible key of that row (-1: none)
 };
 __device__ inline DecodeUnit decode_unit(const AttnParams& p, int n) {
   DecodeUnit u;
@@ -56,7 +58,9 @@ __device__ inline DecodeUnit decode_unit(const AttnParams& p, int n) {
   const int cc = u.ok ? c : 0;
   u.qi = cc / p.group;
   u.hq = u.hk * p.group + cc % p.group;
-  u.last_key = p.causal_off + u.qi;
+  const int lq = batch_len(p.seqlens_q, u.b, p.Lq);
+  u.lk = batch_len(p.seqlens_k, u.b, p.Lk);
+  u.last_key = u.qi >= lq ? -1 : (p.causal ? u.lk - lq + u.qi : u.lk);
   return u;
 }
 
@@ -124,7 +128,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   const bool head_ok = u.ok;
 
   const int kbeg = split * p.split_len;
-  const int kend = min(p.Lk, kbeg + p.split_len);
+  const int kend = min(u.lk, kbeg + p.split_len);
   const int ntiles = kend > kbeg ? (kend - kbeg + C::TK - 1) / C::TK : 0;
 
   const S* kp = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
@@ -455,7 +459,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   const bool head_ok = u.ok;
 
   const int kbeg = split * p.split_len;
-  const int kend = min(p.Lk, kbeg + p.split_len);
+  const int kend = min(u.lk, kbeg + p.split_len);
   const int ntiles = kend > kbeg ? (kend - kbeg + C::TK - 1) / C::TK : 0;
 
   const S* kp = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];

@@ -98,6 +98,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
   const int i0 = qt * kBM;            // first query row of the workgroup
   const int iw = i0 + 32 * wave;      // first query row of this wave
   const int my_i = iw + l32;          // this lane's query row
+  // real query rows and keys of this batch; bottom-right causal offset
+  const int lq = batch_len(p.seqlens_q, b, p.Lq);
+  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int coff = lk - lq;
 
   const S* qp = (const S*)p.q + b * p.qs[0] + hq * p.qs[1];
   const S* kp = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
@@ -106,7 +110,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
   // ---- Q row of this lane as B operands: vector s holds chunk 2s + g ----
   u32x4 qreg[C::NQ];
   {
-    const bool ok = my_i < p.Lq;
+    const bool ok = my_i < lq;
     const S* row = qp + (int64_t)(ok ? my_i : 0) * p.qs[2];
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
@@ -115,11 +119,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
     }
   }
 
-  // key range of the workgroup (bottom-right causal)
-  int kend = p.Lk;
-  if (CAUSAL) kend = min(kend, i0 + kBM + p.causal_off);
+  // key range of the workgroup's real rows (bottom-right causal)
+  int kend = i0 < lq ? lk : 0;
+  if (CAUSAL) kend = min(kend, min(i0 + kBM, lq) + coff);
   const int ntiles = kend > 0 ? (kend + C::BN - 1) / C::BN : 0;
-  const int wave_last_key = CAUSAL ? iw + 31 + p.causal_off : p.Lk - 1;
+  const int wave_last_key = CAUSAL ? iw + 31 + coff : lk - 1;
   // bf16 probabilities carry 8 significant bits; rows that average few keys
   // would show that rounding directly in O, so such workgroups feed P.V with
   // P = hi + lo (two bf16 products).  Many-key rows average it away.
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
       const int u = tid + kThreads * it;
       const int key = u / C::NCH, c = u % C::NCH;
       const int j = j0 + key;
-      kpre[it] = j < p.Lk ? ldg16_cached(kp + (int64_t)j * p.ks[2] + c * C::VEC)
+      kpre[it] = j < lk ? ldg16_cached(kp + (int64_t)j * p.ks[2] + c * C::VEC)
                           : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = j0 + 4 * kg + r;
-        vpre[it][r] = j < p.Lk ? ldg16_cached(vp + (int64_t)j * p.vs[2] + c * C::VEC)
+        vpre[it][r] = j < lk ? ldg16_cached(vp + (int64_t)j * p.vs[2] + c * C::VEC)
                                : u32x4{0, 0, 0, 0};
       }
     }
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
     if (t + 1 < ntiles) prefetch(j0 + C::BN);
 
     if (j0 > wave_last_key) continue;  // nothing visible to this wave's rows
-    const bool edge = (j0 + C::BN > p.Lk) || (CAUSAL && j0 + C::BN - 1 > iw + p.causal_off);
+    const bool edge = (j0 + C::BN > lk) || (CAUSAL && j0 + C::BN - 1 > iw + coff);
 
     // ---- S^T = K . Q^T for the tile ----
     f32x16 sc[C::NKB];
@@ -224,13 +228,13 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
         float x = sc[kb][r] * p.scale_log2;
         const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
         if (MASK) {
-          const int ii = my_i < p.Lq ? my_i : p.Lq - 1;
-          const int jj = j < p.Lk ? j : p.Lk - 1;
+          const int ii = my_i < lq ? my_i : lq - 1;
+          const int jj = j < lk ? j : lk - 1;
           x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] +
                                (int64_t)jj * p.ms[3]];
         }
         if (edge) {
-          const bool vis = (j < p.Lk) && (!CAUSAL || j <= my_i + p.causal_off);
+          const bool vis = (j < lk) && (!CAUSAL || j <= my_i + coff);
           x = vis ? x : kNegInf;
         }
         sc[kb][r] = x;
@@ -302,8 +306,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
     }
   }
 
-  // ---- epilogue: normalise, sink, LSE ----
-  const float l_tot = l_run + xor32(l_run);
+  // ---- epilogue: normalise, sink, LSE.  Padding rows see no key. ----
+  float l_tot = l_run + xor32(l_run);
+  if (my_i >= lq) {
+    m_run = kNegInf;
+    l_tot = 0.f;
+  }
   float M = m_run;
   float Ltot = l_tot;
   if (p.sinks) {
@@ -416,13 +424,17 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   const int i0 = qt * BM;
   const int iw = i0 + 32 * wave;
   const int my_i = iw + l32;
+  // real query rows and keys of this batch; bottom-right causal offset
+  const int lq = batch_len(p.seqlens_q, b, p.Lq);
+  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int coff = lk - lq;
 
   // exponent scale c = |scale| log2(e); a negative scale is moved into Q
   const float c = fabsf(p.scale_log2);
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   u32x4 qreg[C::NQ];
   {
-    const bool ok = my_i < p.Lq;
+    const bool ok = my_i < lq;
     const S* row = (const S*)p.q + b * p.qs[0] + hq * p.qs[1] + (int64_t)(ok ? my_i : 0) * p.qs[2];
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
@@ -432,14 +444,15 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     }
   }
 
-  int kend = p.Lk;
-  if (CAUSAL) kend = min(kend, i0 + BM + p.causal_off);
+  // key range of the workgroup's real rows (bottom-right causal)
+  int kend = i0 < lq ? lk : 0;
+  if (CAUSAL) kend = min(kend, min(i0 + BM, lq) + coff);
   const int ntiles = kend > 0 ? (kend + C::BN - 1) / C::BN : 0;
   // tiles [0, n_int) have every key visible to every row of the workgroup
   int n_int = 0;
   if (!MASK) {
-    int full = p.Lk;
-    if (CAUSAL) full = min(full, i0 + 1 + p.causal_off);
+    int full = lk;
+    if (CAUSAL) full = min(full, i0 + 1 + coff);
     n_int = full > 0 ? min(ntiles, full / C::BN) : 0;
   }
   // bf16 probabilities carry 8 significant bits; rows that average few keys
@@ -467,9 +480,9 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   }
   const uint32_t krow = (uint32_t)(p.ks[2] * 2), vrow = (uint32_t)(p.vs[2] * 2);
   const uint32_t kstep = C::STEP_ROWS * krow, vstep = C::STEP_ROWS * vrow;
-  // bytes of a tile that hold keys < Lk (rows past Lk read as zero)
+  // bytes of a tile that hold real keys (rows from lk on read as zero)
   auto tile_bytes = [&](int j0, uint32_t rowb) -> uint32_t {
-    const int rows = p.Lk - j0;
+    const int rows = lk - j0;
     return rows >= C::BN ? 0xffffffffu : (uint32_t)(rows - 1) * rowb + C::RB;
   };
   auto issue = [&](const S* base, int64_t rs, uint32_t rowb, const uint32_t* off, int noff, uint32_t step,
@@ -522,7 +535,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       mx = max_xor32(mx) * c;
     } else {
       const int j0 = t * C::BN;
-      const int ii = my_i < p.Lq ? my_i : p.Lq - 1;
+      const int ii = my_i < lq ? my_i : lq - 1;
       mx = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb)
@@ -531,10 +544,10 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
           const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
           float x = sc[kb][r] * c;
           if (MASK) {
-            const int jj = j < p.Lk ? j : p.Lk - 1;
+            const int jj = j < lk ? j : lk - 1;
             x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]];
           }
-          const bool vis = (j < p.Lk) && (!CAUSAL || j <= my_i + p.causal_off);
+          const bool vis = (j < lk) && (!CAUSAL || j <= my_i + coff);
           x = vis ? x : kNegInf;
           sc[kb][r] = x;
           mx = fmaxf(mx, x);
@@ -769,8 +782,12 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   for (; t < n_int; ++t) general(t, std::false_type{});
   for (; t < ntiles; ++t) general(t, std::true_type{});
 
-  // ---- epilogue ----
-  const float l_tot = sum_xor32(l_run);
+  // ---- epilogue (padding rows see no key) ----
+  float l_tot = sum_xor32(l_run);
+  if (my_i >= lq) {
+    m_run = kNegInf;
+    l_tot = 0.f;
+  }
   float M = m_run, Ltot = l_tot;
   if (p.sinks) {
     const float sk = p.sinks[hq] * kLog2e;

@@ -149,6 +149,12 @@ __device__ inline u32x4 ldg16(const void* p) {
 }
 __device__ inline u32x4 ldg16_cached(const void* p) { return *(const u32x4*)p; }
 
+// Real rows of batch b along an extent of L rows: lens[b] clamped to [0, L],
+// or L when there is no per-batch length array.
+__device__ inline int batch_len(const int32_t* lens, int b, int L) {
+  return lens ? min(max(lens[b], 0), L) : L;
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);

@@ -21,7 +21,9 @@ struct AttnParams {
   float* lse;
   int B, Hq, Hkv, Lq, Lk, D;
   int group;         // Hq / Hkv
-  int causal_off;    // Lk - Lq (bottom-right alignment)
+  int causal;        // bottom-right causal masking (decode; prefill has it as a template flag)
+  const int32_t* seqlens_q;  // optional [B] real query rows per batch
+  const int32_t* seqlens_k;  // optional [B] real keys per batch
   float scale_log2;  // scale * log2(e)
   // decode only
   int nsplit;        // number of key-range splits (1 = single pass)

@@ -30,18 +30,18 @@ def check(got, ref, dtype_name, what, lse=False):
     return rep
 
 
-def compare_full(out, lse, x, scale, dtype_name, what, causal=False):
+def compare_full(out, lse, x, scale, dtype_name, what, causal=False, **kw):
     O, L = sdpa_reference(x["q"], x["k"], x["v"], scale=scale, causal=causal,
-                          mask=x["mask"], sinks=x["sinks"])
+                          mask=x["mask"], sinks=x["sinks"], **kw)
     check(out.float().cpu(), O, dtype_name, what)
     if lse is not None:
         check(lse.cpu(), L, dtype_name, what, lse=True)
 
 
-def compare_sampled(out, lse, x_cpu, scale, dtype_name, what, heads, rows, causal=False):
+def compare_sampled(out, lse, x_cpu, scale, dtype_name, what, heads, rows, causal=False, **kw):
     """Compare selected (b, hq) pairs and query rows against the oracle."""
     O, L = sdpa_reference(x_cpu["q"], x_cpu["k"], x_cpu["v"], scale=scale, causal=causal,
-                          mask=x_cpu["mask"], sinks=x_cpu["sinks"], rows=rows, heads=heads)
+                          mask=x_cpu["mask"], sinks=x_cpu["sinks"], rows=rows, heads=heads, **kw)
     got = np.stack([out[b, h, rows].float().cpu().numpy() for b, h in heads])
     check(got, O, dtype_name, what)
     if lse is not None:

@@ -55,7 +55,7 @@ int main(void) {
   printf("sizeof %zu\n", sizeof(sdpa_args));
   F(B) F(Hq) F(Hkv) F(Lq) F(Lk) F(D) F(dtype) F(causal) F(scale) F(reserved)
   F(q) F(q_stride) F(k) F(k_stride) F(v) F(v_stride) F(o) F(o_stride)
-  F(mask) F(mask_stride) F(sinks) F(lse)
+  F(mask) F(mask_stride) F(sinks) F(lse) F(seqlens_q) F(seqlens_k)
   return 0;
 }
 """
@@ -129,7 +129,13 @@ def test_prefill_validation(lib):
     big = (1 << 22) + 8                                        # 8 MiB + 16 B per bf16 row
     assert _prefill(lib, k_stride=(2 * 64 * big, 64 * big, big)) == S.ERR_UNSUPPORTED
     assert _prefill(lib, v_stride=(2 * 64 * big, 64 * big, big)) == S.ERR_UNSUPPORTED
+    assert _prefill(lib, seqlens_q=(1 << 46), seqlens_k=(1 << 46) + 64) == S.OK
+    assert _prefill(lib, seqlens_k=(1 << 46) + 2) == S.ERR_ALIGN
+    assert _prefill(lib, seqlens_q=(1 << 46) + 1) == S.ERR_ALIGN
+    assert _prefill(lib, seqlens_k=(1 << 40) + 64) == S.OK             # inputs may overlap
+    assert _prefill(lib, seqlens_k=(1 << 40) + 3 * (1 << 32) + 64) == S.ERR_ARG   # inside o
     assert _prefill(lib, D=64, causal=1, Lq=100, Lk=7) == S.OK
+
     msg = lib.sdpa_last_error()
     assert msg == b""
     _prefill(lib, D=96)
