@@ -20,7 +20,8 @@ form with MI355X's published peaks.  ``cpu_baseline`` is the fp64 oracle timed
 on a bounded sample of the same workload on the host cores.
 
 Other workloads (for profiling): --workload dit_fp16|dit_fp32|causal_bf16|
-long_decode_bf16|<gqa8 decode name>|mq4_gqa8_decode_b1_lk32768_fp16 (multi-query decode).
+long_decode_bf16|<gqa8 decode name>|mq4_gqa8_decode_b1_lk32768_fp16 (multi-query decode)|
+kvcache_ragged_decode_bf16 (KV cache with per-batch fill levels; GB/s over the filled part).
 """
 from __future__ import annotations
 
@@ -57,7 +58,9 @@ def prefill_flops(w) -> int:
 
 def decode_bytes(w) -> int:
     es = 4 if w.dtype == "fp32" else 2
-    kv = 2 * w.B * w.Hkv * w.Lk * w.D * es
+    fill = w.seqlens_k()
+    keys = w.B * w.Lk if fill is None else int(fill.sum())     # real keys over the batch
+    kv = 2 * keys * w.Hkv * w.D * es
     qo = 2 * w.B * w.Hq * w.Lq * w.D * es
     mask = 4 * w.B * w.Lk if w.mask else 0
     return kv + qo + mask
@@ -130,17 +133,20 @@ def cpu_baseline_decode(w, budget_s: float = 8.0):
     done, nbytes, t_used = 0, 0, 0.0
     es = 4 if w.dtype == "fp32" else 2
     units = [(b, hk) for b in range(w.B) for hk in range(w.Hkv)]
+    fill = w.seqlens_k()
     for b, hk in units:
         q = torch.stack([workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, hk * G + i, w.Lq, w.D, dt)
                          for i in range(G)])[None]
         k = workloads.slice_normal(w.cfg_id, workloads.TENSOR_K, b, hk, w.Lk, w.D, dt)[None, None]
         v = workloads.slice_normal(w.cfg_id, workloads.TENSOR_V, b, hk, w.Lk, w.D, dt)[None, None]
         mask = workloads.tail_mask(1, w.Lk) if w.mask else None
+        sk = None if fill is None else fill[b:b + 1]
         t0 = time.perf_counter()
-        sdpa_reference(q, k, v, scale=w.scale, causal=w.causal, mask=mask)
+        sdpa_reference(q, k, v, scale=w.scale, causal=w.causal, mask=mask, seqlens_k=sk)
         t_used += time.perf_counter() - t0
         done += 1
-        nbytes += 2 * w.Lk * w.D * es + 2 * G * w.Lq * w.D * es + (4 * w.Lk if w.mask else 0)
+        keys = w.Lk if fill is None else int(fill[b])
+        nbytes += 2 * keys * w.D * es + 2 * G * w.Lq * w.D * es + (4 * w.Lk if w.mask else 0)
         if t_used >= budget_s:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -225,7 +231,8 @@ def main():
         if Dd is not None:
             if td: td.ev[i][0].record()
             sdpa.decode(Dd["q"], Dd["k"], Dd["v"], scale=dec_w.scale, causal=dec_w.causal,
-                        mask=Dd["mask"], sinks=Dd["sinks"], workspace=ws, out=dec_out)
+                        mask=Dd["mask"], sinks=Dd["sinks"], workspace=ws, out=dec_out,
+                        seqlens_k=Dd.get("seqlens_k"))
             if td: td.ev[i][1].record()
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -278,6 +285,8 @@ def main():
         cfg["decode"] = {"B": dec_w.B, "Hq": dec_w.Hq, "Hkv": dec_w.Hkv, "Lq": dec_w.Lq, "Lk": dec_w.Lk,
                          "D": dec_w.D, "dtype": dec_w.dtype, "causal": dec_w.causal, "mask": dec_w.mask,
                          "sinks": dec_w.sinks}
+        if dec_w.fill is not None:
+            cfg["decode"]["seqlens_k"] = [int(x) for x in dec_w.seqlens_k()]
         if P is None:
             res.update(value=dec["value"], unit="GB/s", dtype=dec_w.dtype, roofline=dec["roofline"])
         res["decode"] = dec

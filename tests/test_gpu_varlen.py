@@ -103,3 +103,19 @@ def test_decode_whole_cache_equals_slices():
         err = (whole[b:b + 1].float() - part.float()).abs().max().item()
         say(f"  batch {b} fill {fill[b]}: max diff {err:.3e}")
         assert err <= 2e-3
+
+
+@pytest.mark.timeout(600)
+def test_kvcache_ragged_full_size():
+    """The ragged KV-cache decode workload at full size (B8 Hq32 Hkv8 D128, a
+    131072-slot cache per (batch, KV head) with per-batch fill levels), every
+    output row against the oracle, in the launch configuration bench.py times."""
+    import workloads
+    w = workloads.KVCACHE_DECODE
+    say("decode full size", w, "fill", list(w.seqlens_k()))
+    x = workloads.make_inputs(w)
+    d = to_dev(x)
+    out, lse = sdpa.decode(d["q"], d["k"], d["v"], scale=w.scale, return_lse=True,
+                           seqlens_k=d["seqlens_k"])
+    torch.cuda.synchronize()
+    compare_full(out, lse, x, w.scale, w.dtype, w.name, seqlens_k=w.seqlens_k())

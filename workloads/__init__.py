@@ -15,7 +15,9 @@ Recipe (the same for every tensor):
   * sinks (one logit per query head) are float32 N(0, 1) from
     ``default_rng([0, cfg, 3])`` (times ``sink_scale``);
   * the long-context decode mask is float32 [B, 1, 1, Lk]: 0 for the leading
-    keys and -inf for the trailing floor(Lk / 10) keys of every batch.
+    keys and -inf for the trailing floor(Lk / 10) keys of every batch;
+  * ragged KV-cache fill levels (per-batch key counts) are uniform integers
+    in [Lk / 8, Lk] from ``default_rng([0, cfg, 4])``.
 
 Seed 0 follows the reproducer script on the "Add D512 support to Metal vector
 attention" page (its ``SEED``); the shapes follow the pages' workloads (the
@@ -32,7 +34,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 import torch
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_SINKS = 0, 1, 2, 3
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_SINKS, TENSOR_FILL = 0, 1, 2, 3, 4
 
 DTYPES = {
     "fp32": torch.float32,
@@ -60,6 +62,7 @@ class Workload:
     sink_scale: float = 1.0
     lse: bool = False
     decode: bool = False           # run through sdpa_decode (always so when Lq == 1)
+    fill: Optional[str] = None     # None | "ragged" (per-batch KV-cache fill levels)
 
     @property
     def is_decode(self) -> bool:
@@ -75,6 +78,13 @@ class Workload:
 
     def with_(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
+
+    def seqlens_k(self) -> Optional[np.ndarray]:
+        """Per-batch key counts (int32 [B]) of a ragged KV cache, else None."""
+        if self.fill != "ragged":
+            return None
+        rng = np.random.default_rng([0, self.cfg_id, TENSOR_FILL])
+        return rng.integers(self.Lk // 8, self.Lk + 1, size=self.B).astype(np.int32)
 
 
 # The five workload families.  Sizes are the ones the pages measure on; the
@@ -103,8 +113,16 @@ GQA_DECODE = [gqa_decode(B, Lk, dt, s)
 MQ_DECODE = Workload("mq4_gqa8_decode_b1_lk32768_fp16", 6, B=1, Hq=32, Hkv=4, Lq=4, Lk=32768,
                      D=512, dtype="fp16", causal=True, decode=True)
 
+# Ragged KV cache (next-row extension): the long-context decode shape as a
+# fixed-capacity cache of 131072 slots per (batch, KV head) whose batches are
+# filled to different levels (the padding mask of the cuDNN graph, with
+# per-batch seq_len_kv).
+KVCACHE_DECODE = Workload("kvcache_ragged_decode_bf16", 7, B=8, Hq=32, Hkv=8, Lq=1, Lk=131072,
+                          D=128, dtype="bf16", fill="ragged")
+
 ALL: Dict[str, Workload] = {w.name: w for w in
-                            [TINY, DIT_FP16, DIT_FP32, CAUSAL, LONG_DECODE, *GQA_DECODE, MQ_DECODE]}
+                            [TINY, DIT_FP16, DIT_FP32, CAUSAL, LONG_DECODE, *GQA_DECODE, MQ_DECODE,
+                             KVCACHE_DECODE]}
 
 
 # ---- generators --------------------------------------------------------------
@@ -152,7 +170,11 @@ def make_inputs(w: Workload, device="cpu") -> Dict[str, Optional[torch.Tensor]]:
     v = tensor_normal(w.cfg_id, TENSOR_V, w.B, w.Hkv, w.Lk, w.D, dt, device)
     mask = tail_mask(w.B, w.Lk).to(device) if w.mask == "tail10" else None
     sinks = sinks_normal(w.cfg_id, w.Hq, w.sink_scale).to(device) if w.sinks else None
-    return {"q": q, "k": k, "v": v, "mask": mask, "sinks": sinks}
+    out = {"q": q, "k": k, "v": v, "mask": mask, "sinks": sinks}
+    fill = w.seqlens_k()
+    if fill is not None:
+        out["seqlens_k"] = torch.from_numpy(fill).to(device)
+    return out
 
 
 def random_case(seed: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D: int,
