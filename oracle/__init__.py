@@ -5,3 +5,4 @@ leg may import this package.  It shares no code with the HIP library and never
 imports it; the product path never calls it.
 """
 from .attention import sdpa_reference, allclose_report  # noqa: F401
+from .backward import sdpa_backward_reference  # noqa: F401
