@@ -174,6 +174,53 @@ SDPA_API int sdpa_decode_num_splits(const sdpa_args *args, int num_splits);
  * B * Hq * Lq * splits * (D + 2) * 4. */
 SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_splits);
 
+/* ---- gradients ------------------------------------------------------------
+ * The backward pass of sdpa_prefill, following the two backward kernels of
+ * the rustytorch "flash_attention.metal" page (one pass per query block for
+ * dQ, one per key block for dK and dV, P recomputed from the log-sum-exp,
+ * D_i = dO_i . O_i) with the inputs and attributes of build_sdpa_backward_graph
+ * on the mlx 0.30.7 page (q, k, v, o, dO, statistics; scale, bottom-right
+ * causal mask, additive bias, sink token):
+ *
+ *     P = exp(S - LSE),  dS = P * (dO V^T - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+ *     dsinks[hq] = -sum_{b,i} exp(sinks[hq] - LSE[b,hq,i]) D[b,hq,i].
+ *
+ * `fwd` is the argument block of the forward call whose output is being
+ * differentiated: q, k, v, mask, sinks, seqlens_q / seqlens_k, scale and
+ * causal as there; lse (its log-sum-exp, REQUIRED) is read, not written.
+ * o (the forward's output) is part of the signature, as in the cuDNN graph,
+ * and is validated, but D_i is formed as sum_j P_ij (dO V^T)_ij, which equals
+ * dO_i . O_i without inheriting the rounding of a 16-bit O; o is not read.
+ * dK and dV of a KV head sum over the
+ * Hq / Hkv query heads that read it.  The mask is a constant (no gradient).
+ * Padding rows (past seqlens_q[b]) get dQ = 0, padding keys dK = dV = 0.
+ * Supported: dtype F16 or BF16, D in {64, 128}.  dq, dk, dv are written in
+ * the input dtype with the layout rules of q, k, v (last dim contiguous,
+ * 16-byte aligned pointers and strides); dsinks (optional, used only with
+ * sinks) is fp32 [Hq].  The workspace (device memory, 16-byte aligned,
+ * caller-owned, need not be initialised) holds
+ * sdpa_prefill_backward_workspace_bytes() = 8 * B * Hq * Lq bytes.  Four
+ * kernels are enqueued on `stream`; nothing is allocated or synchronised.
+ * The outputs must not overlap each other, the inputs or the workspace. */
+typedef struct sdpa_bwd_args {
+  const void *dout; int64_t dout_stride[3];  /* [B, Hq,  Lq, D] upstream gradient */
+  void *dq;         int64_t dq_stride[3];    /* [B, Hq,  Lq, D] output            */
+  void *dk;         int64_t dk_stride[3];    /* [B, Hkv, Lk, D] output            */
+  void *dv;         int64_t dv_stride[3];    /* [B, Hkv, Lk, D] output            */
+  float *dsinks;                             /* optional [Hq] fp32 output         */
+} sdpa_bwd_args;
+
+SDPA_API int sdpa_prefill_backward(const sdpa_args *fwd, const sdpa_bwd_args *grad,
+                                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Host-only validation of a backward request (no GPU work, no HIP calls). */
+SDPA_API int sdpa_prefill_backward_check(const sdpa_args *fwd, const sdpa_bwd_args *grad,
+                                         const void *workspace, size_t workspace_bytes);
+
+/* Workspace bytes sdpa_prefill_backward needs (0 for an invalid request). */
+SDPA_API size_t sdpa_prefill_backward_workspace_bytes(const sdpa_args *fwd);
+
 /* Static description of a status code. */
 SDPA_API const char *sdpa_status_string(int status);
 

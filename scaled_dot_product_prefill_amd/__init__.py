@@ -9,6 +9,10 @@ the library is missing, every entry point raises -- there is no CPU path.
     decode(q, k, v, scale=None, causal=False, mask=None, sinks=None, return_lse=False,
            num_splits=0, seqlens_q=None, seqlens_k=None)
 
+    prefill_backward(q, k, v, o, lse, dout, scale=None, causal=False, mask=None, sinks=None,
+                     seqlens_q=None, seqlens_k=None, want_dsinks=False)
+    attention(q, k, v, ...)   autograd-aware prefill (forward + backward kernels)
+
 q: [B, Hq, Lq, D], k / v: [B, Hkv, Lk, D] (float32, float16 or bfloat16),
 mask: additive float tensor broadcastable to [B, Hq, Lq, Lk], sinks: [Hq],
 seqlens_q / seqlens_k: per-batch real query rows / keys [B] (padding masks).
@@ -23,8 +27,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_bytes",
-           "SdpaArgs", "library", "library_path", "Status", "SdpaError"]
+__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_bytes", "prefill_backward",
+           "attention", "SdpaArgs", "SdpaBwdArgs", "library", "library_path", "Status", "SdpaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "lib", "libsdpa_mi355x.so")
@@ -64,6 +68,17 @@ class SdpaArgs(ctypes.Structure):
     ]
 
 
+class SdpaBwdArgs(ctypes.Structure):
+    """Mirror of ``struct sdpa_bwd_args`` (include/sdpa_mi355x.h)."""
+    _fields_ = [
+        ("dout", ctypes.c_void_p), ("dout_stride", ctypes.c_int64 * 3),
+        ("dq", ctypes.c_void_p), ("dq_stride", ctypes.c_int64 * 3),
+        ("dk", ctypes.c_void_p), ("dk_stride", ctypes.c_int64 * 3),
+        ("dv", ctypes.c_void_p), ("dv_stride", ctypes.c_int64 * 3),
+        ("dsinks", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -96,6 +111,13 @@ def library():
     lib.sdpa_last_error.restype = ctypes.c_char_p
     lib.sdpa_version.argtypes = []
     lib.sdpa_version.restype = ctypes.c_char_p
+    G = ctypes.POINTER(SdpaBwdArgs)
+    lib.sdpa_prefill_backward.argtypes = [P, G, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.sdpa_prefill_backward.restype = ctypes.c_int
+    lib.sdpa_prefill_backward_check.argtypes = [P, G, ctypes.c_void_p, ctypes.c_size_t]
+    lib.sdpa_prefill_backward_check.restype = ctypes.c_int
+    lib.sdpa_prefill_backward_workspace_bytes.argtypes = [P]
+    lib.sdpa_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
     _lib = lib
     return lib
 
@@ -258,3 +280,80 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
     if st != 0:
         _raise(st)
     return (o, lse) if return_lse else o
+
+
+def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                     lse: torch.Tensor, dout: torch.Tensor, *, scale: Optional[float] = None,
+                     causal: bool = False, mask: Optional[torch.Tensor] = None,
+                     sinks: Optional[torch.Tensor] = None, seqlens_q=None, seqlens_k=None,
+                     want_dsinks: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Gradients of prefill(q, k, v, ...) = o (with log-sum-exp ``lse``) for the
+    upstream gradient ``dout``: returns (dq, dk, dv) or, with ``want_dsinks``,
+    (dq, dk, dv, dsinks).  fp16 / bf16 inputs, D in {64, 128}."""
+    lib = library()
+    q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
+    o, dout = _prep(o, "o"), _prep(dout, "dout")
+    B, Hq, Lq, D = q.shape
+    if o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("o and dout must have the shape of q")
+    lse = lse.to(torch.float32).contiguous()
+    if lse.shape != (B, Hq, Lq):
+        raise ValueError(f"lse must be [B, Hq, Lq] = {(B, Hq, Lq)}, got {tuple(lse.shape)}")
+    sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
+    sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
+    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
+    dq = torch.empty_like(q, memory_format=torch.contiguous_format)
+    dk = torch.empty_like(k, memory_format=torch.contiguous_format)
+    dv = torch.empty_like(v, memory_format=torch.contiguous_format)
+    ds = torch.empty(Hq, dtype=torch.float32, device=q.device) if (want_dsinks and sinks is not None) else None
+    g = SdpaBwdArgs()
+    for n, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        setattr(g, n, t.data_ptr())
+        st = getattr(g, n + "_stride")
+        for i in range(3):
+            st[i] = t.stride(i)
+    g.dsinks = ds.data_ptr() if ds is not None else None
+    need = int(lib.sdpa_prefill_backward_workspace_bytes(ctypes.byref(a)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.sdpa_prefill_backward(ctypes.byref(a), ctypes.byref(g), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    if st != 0:
+        _raise(st)
+    if want_dsinks:
+        return dq, dk, dv, (ds if ds is not None else None)
+    return dq, dk, dv
+
+
+class _Attention(torch.autograd.Function):
+    """prefill forward and its backward kernels as one autograd node."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, sinks, scale, causal, mask, seqlens_q, seqlens_k):
+        o, lse = prefill(q, k, v, scale=scale, causal=causal, mask=mask, sinks=sinks, return_lse=True,
+                         seqlens_q=seqlens_q, seqlens_k=seqlens_k)
+        ctx.save_for_backward(q, k, v, o, lse, sinks)
+        ctx.opts = (scale, causal, mask, seqlens_q, seqlens_k)
+        return o
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, o, lse, sinks = ctx.saved_tensors
+        scale, causal, mask, sq, sk = ctx.opts
+        want = sinks is not None and ctx.needs_input_grad[3]
+        res = prefill_backward(q, k, v, o, lse, dout.contiguous(), scale=scale, causal=causal, mask=mask,
+                               sinks=sinks, seqlens_q=sq, seqlens_k=sk, want_dsinks=want)
+        dq, dk, dv = res[:3]
+        ds = res[3] if want else None
+        return dq, dk, dv, ds, None, None, None, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+              causal: bool = False, mask: Optional[torch.Tensor] = None,
+              sinks: Optional[torch.Tensor] = None, seqlens_q=None, seqlens_k=None) -> torch.Tensor:
+    """Differentiable fused attention: prefill() forward, prefill_backward()
+    gradients for q, k, v and (fp32) sinks.  The mask is a constant."""
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    return _Attention.apply(q, k, v, sinks, scale, causal, mask, seqlens_q, seqlens_k)

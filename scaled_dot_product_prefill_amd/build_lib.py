@@ -23,7 +23,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsdpa_mi355x.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["prefill.hip", "decode.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "decode.hip", "backward.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

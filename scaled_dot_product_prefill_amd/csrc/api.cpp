@@ -229,6 +229,83 @@ int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_b
   return SDPA_OK;
 }
 
+// Backward: the forward's checks (o and lse are inputs), 16-bit only,
+// D in {64, 128}, and the gradient outputs.
+size_t backward_workspace(const sdpa_args* a) { return (size_t)a->B * a->Hq * a->Lq * 2 * sizeof(float); }
+
+int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, size_t ws_bytes) {
+  int st = check_common(a);
+  if (st != SDPA_OK) return st;
+  if (!g) return fail(SDPA_ERR_NULL, "gradient arguments are NULL");
+  if (a->dtype == SDPA_F32) return fail(SDPA_ERR_UNSUPPORTED, "backward supports F16 and BF16 inputs");
+  if (a->D != 64 && a->D != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "backward supports D in {64, 128}, got %lld", (long long)a->D);
+  if (!a->lse) return fail(SDPA_ERR_NULL, "backward needs the forward's lse");
+  if (!g->dout || !g->dq || !g->dk || !g->dv) return fail(SDPA_ERR_NULL, "dout, dq, dk and dv must be non-NULL");
+  const void* ptrs[4] = {g->dout, g->dq, g->dk, g->dv};
+  const int64_t* strides[4] = {g->dout_stride, g->dq_stride, g->dk_stride, g->dv_stride};
+  const char* names[4] = {"dout", "dq", "dk", "dv"};
+  for (int t = 0; t < 4; ++t) {
+    if ((uintptr_t)ptrs[t] % 16 != 0) return fail(SDPA_ERR_ALIGN, "%s is not 16-byte aligned", names[t]);
+    for (int d = 0; d < 3; ++d) {
+      if (strides[t][d] < 0) return fail(SDPA_ERR_ARG, "%s stride %d is negative", names[t], d);
+      if ((strides[t][d] * 2) % 16 != 0)
+        return fail(SDPA_ERR_ALIGN, "%s stride %d (%lld elements) is not a multiple of 16 bytes", names[t], d,
+                    (long long)strides[t][d]);
+    }
+  }
+  if (g->dout_stride[2] * 2 > kMaxRowBytes)
+    return fail(SDPA_ERR_UNSUPPORTED, "dout row stride above %lld bytes", (long long)kMaxRowBytes);
+  if (a->q_stride[2] * 2 > kMaxRowBytes)
+    return fail(SDPA_ERR_UNSUPPORTED, "q row stride above %lld bytes", (long long)kMaxRowBytes);
+  if (g->dq_stride[2] < a->D || g->dk_stride[2] < a->D || g->dv_stride[2] < a->D)
+    return fail(SDPA_ERR_ARG, "gradient rows overlap (row stride < D)");
+  if (g->dsinks && (uintptr_t)g->dsinks % 4 != 0) return fail(SDPA_ERR_ALIGN, "dsinks is not 4-byte aligned");
+  const size_t need = backward_workspace(a);
+  if (!ws) return fail(SDPA_ERR_WORKSPACE, "backward needs a workspace of %zu bytes", need);
+  if ((uintptr_t)ws % 16 != 0) return fail(SDPA_ERR_ALIGN, "workspace is not 16-byte aligned");
+  if (ws_bytes < need) return fail(SDPA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+
+  // outputs: disjoint from each other, from every input and from the workspace
+  const Extent outs[4] = {tensor_extent(g->dq, g->dq_stride, a->B, a->Hq, a->Lq, a->D, 2),
+                          tensor_extent(g->dk, g->dk_stride, a->B, a->Hkv, a->Lk, a->D, 2),
+                          tensor_extent(g->dv, g->dv_stride, a->B, a->Hkv, a->Lk, a->D, 2), Extent{}};
+  Extent eds;
+  if (g->dsinks) { eds.lo = (uintptr_t)g->dsinks; eds.hi = eds.lo + a->Hq * 4; eds.valid = true; }
+  Extent ews;
+  ews.lo = (uintptr_t)ws; ews.hi = ews.lo + need; ews.valid = true;
+  Extent ins[12];
+  int n = 0;
+  ins[n++] = tensor_extent(a->q, a->q_stride, a->B, a->Hq, a->Lq, a->D, 2);
+  ins[n++] = tensor_extent(a->k, a->k_stride, a->B, a->Hkv, a->Lk, a->D, 2);
+  ins[n++] = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, a->D, 2);
+  ins[n++] = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, a->D, 2);
+  ins[n++] = tensor_extent(g->dout, g->dout_stride, a->B, a->Hq, a->Lq, a->D, 2);
+  { Extent e; e.lo = (uintptr_t)a->lse; e.hi = e.lo + a->B * a->Hq * a->Lq * 4; e.valid = true; ins[n++] = e; }
+  if (a->mask) {
+    const int64_t last = (a->B - 1) * a->mask_stride[0] + (a->Hq - 1) * a->mask_stride[1] +
+                         (a->Lq - 1) * a->mask_stride[2] + (a->Lk - 1) * a->mask_stride[3] + 1;
+    Extent e; e.lo = (uintptr_t)a->mask; e.hi = e.lo + (uintptr_t)(last * 4); e.valid = true; ins[n++] = e;
+  }
+  if (a->sinks) { Extent e; e.lo = (uintptr_t)a->sinks; e.hi = e.lo + a->Hq * 4; e.valid = true; ins[n++] = e; }
+  if (a->seqlens_q) { Extent e; e.lo = (uintptr_t)a->seqlens_q; e.hi = e.lo + a->B * 4; e.valid = true; ins[n++] = e; }
+  if (a->seqlens_k) { Extent e; e.lo = (uintptr_t)a->seqlens_k; e.hi = e.lo + a->B * 4; e.valid = true; ins[n++] = e; }
+  ins[n++] = ews;
+  Extent all_out[4] = {outs[0], outs[1], outs[2], eds};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = i + 1; j < 4; ++j)
+      if (overlaps(all_out[i], all_out[j])) return fail(SDPA_ERR_ARG, "gradient outputs overlap each other");
+    for (int j = 0; j < n; ++j)
+      if (overlaps(all_out[i], ins[j])) return fail(SDPA_ERR_ARG, "a gradient output overlaps an input or the workspace");
+  }
+  for (int j = 0; j + 1 < n; ++j)
+    if (overlaps(ews, ins[j])) return fail(SDPA_ERR_ARG, "workspace overlaps an input");
+  const int64_t grid = ((a->Lq + 127) / 128) * a->B * a->Hq;
+  const int64_t gridk = ((a->Lk + 127) / 128) * a->B * a->Hkv;
+  if (grid > kMaxInt || gridk > kMaxInt) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
+  return SDPA_OK;
+}
+
 int launch_status(hipError_t e) {
   if (e != hipSuccess) return fail(SDPA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -307,6 +384,26 @@ int sdpa_decode(const sdpa_args* args, int num_splits, void* workspace, size_t w
     p.part_ml = ws + (size_t)args->B * args->Hq * args->Lq * sp.nsplit * args->D;
   }
   return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
+}
+
+int sdpa_prefill_backward_check(const sdpa_args* fwd, const sdpa_bwd_args* grad, const void* workspace,
+                                size_t workspace_bytes) {
+  int st = sdpa::check_backward(fwd, grad, workspace, workspace_bytes);
+  return st == SDPA_OK ? sdpa::ok() : st;
+}
+
+size_t sdpa_prefill_backward_workspace_bytes(const sdpa_args* fwd) {
+  if (sdpa::check_sizes(fwd) != SDPA_OK) return 0;
+  return sdpa::backward_workspace(fwd);
+}
+
+int sdpa_prefill_backward(const sdpa_args* fwd, const sdpa_bwd_args* grad, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  int st = sdpa::check_backward(fwd, grad, workspace, workspace_bytes);
+  if (st != SDPA_OK) return st;
+  sdpa::AttnParams p = sdpa::make_params(*fwd);
+  return sdpa::launch_status(sdpa::launch_backward(p, *grad, fwd->scale, (float*)workspace, fwd->dtype,
+                                                   fwd->causal != 0, (hipStream_t)stream));
 }
 
 const char* sdpa_status_string(int status) {

@@ -1,0 +1,558 @@
+// Gradients of the prefill attention (fp16 / bf16 inputs, D in {64, 128}).
+//
+// The structure follows the two backward kernels of the rustytorch
+// "flash_attention.metal" page: one kernel per query block computes dQ
+// ("Flash Attention backward kernel for dQ"), one per key block computes dK
+// and dV ("... for dK and dV"); both recompute P = exp(S - LSE) from the
+// forward's log-sum-exp instead of storing it, and use D_i = dO_i . O_i:
+//
+//     dS = P * (dO V^T - D),   dQ = scale dS K,   dK = scale dS^T Q,   dV = P^T dO.
+//
+// The inputs are those of build_sdpa_backward_graph on the "mlx 0.30.7 --
+// backend/cuda/scaled_dot_product_attention.cpp" page (q, k, v, o, dO and the
+// statistics, with scale, bottom-right causal mask, additive bias and sink
+// token).  A sink only enters the denominator, so it changes dQ, dK, dV only
+// through the LSE; its own gradient is -sum_i exp(sink - LSE_i) D_i.
+//
+// D_i is formed as sum_j P_ij dP_ij, which equals dO_i . O_i, instead of from
+// the stored O: a 16-bit O carries its rounding (and the forward's P
+// rounding) into every dS of the row, which showed as errors of a few 1e-3 in
+// bf16 dQ for rows with few keys.
+//
+// Kernels, in launch order:
+//   bwd_prep_kernel   LSE_i in log2 units (+inf for rows without a key or
+//                     past the batch's length) into the workspace;
+//   bwd_dq_kernel     workgroup = 128 query rows of one (batch, query head);
+//                     each wave owns 32 rows, key tiles stream through LDS
+//                     twice: S^T = K Q^T and dP^T = V dO^T (lanes own
+//                     queries) give D_i on the first pass (written to the
+//                     workspace), then dQ^T += K^T dS^T on the second;
+//   bwd_dkv_kernel    workgroup = 128 keys of one (batch, KV head); each wave
+//                     owns 32 keys and walks the query tiles of every query
+//                     head of the group: S = Q K^T and dP = dO V^T (lanes own
+//                     keys), then dV^T += dO^T P and dK^T += Q^T dS, so the
+//                     group's heads add up in registers (no atomics);
+//   bwd_dsink_kernel  the sink gradient, one workgroup per query head.
+// The matrix products are 32x32x16 MFMAs with fp32 accumulation; P and dS
+// enter the second products rounded to the input type, except that bf16 dS
+// (8 significant bits; dQ and dK are sums of terms of both signs) goes in as
+// bf16 hi + lo, two products.
+#include <type_traits>
+
+#include "sdpa_device.hpp"
+#include "sdpa_internal.hpp"
+
+namespace sdpa {
+namespace {
+
+constexpr int kBwdWaves = 4;
+constexpr int kBwdThreads = 64 * kBwdWaves;
+
+// A 64-row tile of a [rows, D] 16-bit matrix in LDS: unpadded rows whose
+// 16-byte chunks are XOR-swizzled by the row (period 16 rows), filled by
+// direct buffer -> LDS loads: wave w writes 1 KiB lines w, w + 4, ...
+template <int D>
+struct Tile64 {
+  static constexpr int ROWS = 64;
+  static constexpr int RB = D * 2;                      // row bytes
+  static constexpr int NCH = D / 8;                     // 16-byte chunks per row
+  static constexpr int BYTES = ROWS * RB;
+  static constexpr int LINES = BYTES / 1024;
+  static constexpr int LPW = LINES / kBwdWaves;         // lines per wave
+  static constexpr int STEP_ROWS = kBwdWaves * 64 / NCH;  // rows between a wave's lines
+  static_assert(LINES % kBwdWaves == 0 && STEP_ROWS % 16 == 0, "tile lines");
+  __device__ static constexpr int swz(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & 7); }
+};
+
+struct BwdParams {
+  AttnParams f;          // the forward's arguments (o and lse are inputs here)
+  const void* dout;
+  int64_t dos[3];
+  void* dq;
+  int64_t dqs[3];
+  void* dk;
+  int64_t dks[3];
+  void* dv;
+  int64_t dvs[3];
+  float* dsinks;
+  float scale;
+  float* ws_d;           // [B*Hq*Lq] D_i
+  float* ws_l;           // [B*Hq*Lq] LSE_i * log2(e), +inf for rows without a key
+};
+
+// Per-lane source offset of the direct loads of a Tile64: the 16 bytes that
+// land in LDS row r, chunk c come from logical chunk c ^ swz(r) of row r.
+template <int D>
+__device__ inline uint32_t tile_lane_off(int wave, int lane, int64_t row_stride_elems) {
+  using L = Tile64<D>;
+  const int pos = wave * 64 + lane;
+  const int row = pos / L::NCH, pch = pos % L::NCH;
+  return (uint32_t)(row * row_stride_elems * 2 + (pch ^ L::swz(row)) * 16);
+}
+
+// Issue this wave's direct loads of rows [r0, r0 + 64) of a matrix (rows >=
+// nrows read as zero) into the Tile64 whose LDS byte address is `lds`.
+template <int D>
+__device__ inline void tile_issue(const uint16_t* base, int64_t rs, int r0, int nrows, uint32_t off,
+                                  uint32_t lds, int wave) {
+  using L = Tile64<D>;
+  const uint16_t* tb = base + (int64_t)r0 * rs;
+  const int rows = nrows - r0;
+  const uint32_t rowb = (uint32_t)(rs * 2);
+  const uint32_t nb = rows >= 64 ? 0xffffffffu : (uint32_t)(rows - 1) * rowb + L::RB;
+#pragma unroll
+  for (int i = 0; i < L::LPW; ++i)
+    dma16(tb, nb, lds + (wave + kBwdWaves * i) * 1024, off, i * L::STEP_ROWS * rowb);
+}
+
+// Matrix-core A operand from a Tile64, row-major: A[m = row rb + lane%32][k =
+// 16 s + 8 (lane/32) + e].  rb is a multiple of 16.
+template <int D>
+__device__ inline u32x4 tile_rows(const uint8_t* t, int rb, int s, int l32, int g) {
+  using L = Tile64<D>;
+  const int row = rb + l32;
+  return lds_read16(t + row * L::RB + (((2 * s + g) ^ L::swz(row)) * 16));
+}
+
+// Matrix-core A operand from a Tile64, transposed: A[m = column 32 mb + lane%32]
+// [k = kappa] = X[rb + 8 (kappa/4 % 2) + 4 (lane/32) + kappa % 4][column], the
+// row order in which a 32x32 accumulator's registers 8u..8u+7 are packed as
+// the B operand (u = k-step, rb = 32 * block + 16 * u).
+template <int D>
+__device__ inline u32x4 tile_cols(const uint8_t* t, int rb, int mb, int lane) {
+  using L = Tile64<D>;
+  const int r16 = lane & 15, g = lane >> 5, dh = (lane >> 4) & 1;
+  const int vr = rb + 4 * g + (r16 >> 2);
+  const int ch = 4 * mb + 2 * dh + ((r16 >> 1) & 1);
+  const uint8_t* p0 = t + vr * L::RB + ((ch ^ L::swz(vr)) * 16) + (r16 & 1) * 8;
+  const uint8_t* p1 = t + (vr + 8) * L::RB + ((ch ^ L::swz(vr + 8)) * 16) + (r16 & 1) * 8;
+  const u32x2 a0 = lds_read_tr16(p0), a1 = lds_read_tr16(p1);
+  return u32x4{a0[0], a0[1], a1[0], a1[1]};
+}
+
+// registers 8u .. 8u+7 of an accumulator as a packed B operand
+template <class T>
+__device__ inline u32x4 pack_b(const f32x16& x, int u) {
+  return u32x4{cvt_pk(T{}, x[8 * u + 0], x[8 * u + 1]), cvt_pk(T{}, x[8 * u + 2], x[8 * u + 3]),
+               cvt_pk(T{}, x[8 * u + 4], x[8 * u + 5]), cvt_pk(T{}, x[8 * u + 6], x[8 * u + 7])};
+}
+
+// registers 8u .. 8u+7 as bf16 hi + lo pairs (about 16 significant bits)
+__device__ inline void pack_b_split(const f32x16& x, int u, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t h, l;
+    TBF16::split2(x[8 * u + 2 * e], x[8 * u + 2 * e + 1], h, l);
+    hi[e] = h;
+    lo[e] = l;
+  }
+}
+
+// ---- the LSE in log2 units ------------------------------------------------
+__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams bp) {
+  const AttnParams& p = bp.f;
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Lq;
+  const int64_t row = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
+  if (row >= nrows) return;
+  const int i = (int)(row % p.Lq);
+  const int b = (int)(row / p.Lq / p.Hq);
+  const float lse = i < batch_len(p.seqlens_q, b, p.Lq) ? p.lse[row] : kNegInf;
+  bp.ws_l[row] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+}
+
+// ---- dQ ---------------------------------------------------------------------
+template <class T, int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams bp) {
+  const AttnParams& p = bp.f;
+  using L = Tile64<D>;
+  constexpr int NQ = D / 16, NMB = D / 32, NKB = 2;
+  using S = uint16_t;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * L::BYTES];  // (K, V) x 2 stages
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  const int nqt = (p.Lq + 127) / 128;
+  int qt, bh;
+  prefill_tile((int)blockIdx.x, (int)gridDim.x, nqt, p.B * p.Hq, CAUSAL, qt, bh);
+  const int b = bh / p.Hq, hq = bh % p.Hq, hk = hq / p.group;
+  const int lq = batch_len(p.seqlens_q, b, p.Lq);
+  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int coff = lk - lq;
+  const int i0 = qt * 128;
+  const int my_i = i0 + 32 * wave + l32;
+  const bool ok = my_i < lq;
+  const float c = p.scale_log2;
+
+  // this lane's query row: Q and dO as B operands, its LSE and D
+  u32x4 qreg[NQ], doreg[NQ];
+  {
+    const int ii = ok ? my_i : 0;
+    const S* qr = (const S*)p.q + b * p.qs[0] + hq * p.qs[1] + (int64_t)ii * p.qs[2];
+    const S* dr = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1] + (int64_t)ii * bp.dos[2];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const u32x4 a = ldg16_cached(qr + (2 * s + g) * 8), d = ldg16_cached(dr + (2 * s + g) * 8);
+      qreg[s] = ok ? a : u32x4{0, 0, 0, 0};
+      doreg[s] = ok ? d : u32x4{0, 0, 0, 0};
+    }
+  }
+  const int64_t wrow = ((int64_t)b * p.Hq + hq) * p.Lq + (ok ? my_i : 0);
+  const float lse2 = ok ? bp.ws_l[wrow] : __builtin_inff();
+
+  int kend = i0 < lq ? lk : 0;
+  if (CAUSAL) kend = min(kend, min(i0 + 128, lq) + coff);
+  const int ntiles = kend > 0 ? (kend + 63) / 64 : 0;
+  int n_int = 0;  // tiles whose every key every row of the workgroup sees
+  if (!MASK) {
+    int full = lk;
+    if (CAUSAL) full = min(full, i0 + 1 + coff);
+    n_int = full > 0 ? min(ntiles, full / 64) : 0;
+  }
+
+  const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
+  const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
+  const uint32_t koff = tile_lane_off<D>(wave, lane, p.ks[2]);
+  const uint32_t voff = tile_lane_off<D>(wave, lane, p.vs[2]);
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int t) {
+    const uint32_t st = lds0 + (t & 1) * 2 * L::BYTES;
+    tile_issue<D>(kbase, p.ks[2], 64 * t, lk, koff, st, wave);
+    tile_issue<D>(vbase, p.vs[2], 64 * t, lk, voff, st + L::BYTES, wave);
+  };
+
+  // S^T and dP^T of key block kb of tile t (stage Ks / Vs), and P^T
+  auto scores = [&](const uint8_t* Ks, const uint8_t* Vs, int t, int kb, bool edge, f32x16& pr, f32x16& dpt) {
+    f32x16 st = f32x16{};
+    dpt = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      st = mma32(T{}, tile_rows<D>(Ks, 32 * kb, s, l32, g), qreg[s], st);
+      dpt = mma32(T{}, tile_rows<D>(Vs, 32 * kb, s, l32, g), doreg[s], dpt);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = st[r] * c;
+      if (edge) {
+        const int j = 64 * t + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (MASK) {
+          const int ii = ok ? my_i : 0, jj = j < lk ? j : lk - 1;
+          x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]];
+        }
+        const bool vis = j < lk && (!CAUSAL || j <= my_i + coff);
+        x = vis ? x : kNegInf;
+      }
+      pr[r] = fast_exp2(x - lse2);
+    }
+  };
+
+  // pass 1: D_i = sum_j P_ij dP_ij
+  float dsum = 0.f;
+  if (ntiles > 0) issue(0);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<0>();
+    lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
+    if (t + 1 < ntiles) issue(t + 1);
+    const uint8_t* Ks = smem + (t & 1) * 2 * L::BYTES;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 pr, dpt;
+      scores(Ks, Ks + L::BYTES, t, kb, t >= n_int, pr, dpt);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dsum = fmaf(pr[r], dpt[r], dsum);
+    }
+  }
+  const float dval = ok ? sum_xor32(dsum) : 0.f;
+  if (my_i < p.Lq && g == 0) bp.ws_d[((int64_t)b * p.Hq + hq) * p.Lq + my_i] = dval;
+
+  // pass 2: dS = P (dP - D),  dQ^T += K^T dS^T
+  f32x16 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+  if (ntiles > 0) {
+    lds_barrier();  // every wave is done with the last tile of pass 1
+    issue(0);
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<0>();
+    lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
+    if (t + 1 < ntiles) issue(t + 1);
+    const uint8_t* Ks = smem + (t & 1) * 2 * L::BYTES;
+    constexpr bool BF = std::is_same<T, TBF16>::value;
+    u32x4 dsp[NKB][2], dsl[NKB][2];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      f32x16 pr, dpt, ds;
+      scores(Ks, Ks + L::BYTES, t, kb, t >= n_int, pr, dpt);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dpt[r] - dval);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        if constexpr (BF) pack_b_split(ds, u, dsp[kb][u], dsl[kb][u]);
+        else dsp[kb][u] = pack_b<T>(ds, u);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const u32x4 ka = tile_cols<D>(Ks, 32 * kb + 16 * u, mb, lane);
+          acc[mb] = mma32(T{}, ka, dsp[kb][u], acc[mb]);
+          if constexpr (BF) acc[mb] = mma32(T{}, ka, dsl[kb][u], acc[mb]);
+        }
+  }
+
+  if (my_i < p.Lq) {
+    S* orow = (S*)bp.dq + b * bp.dqs[0] + hq * bp.dqs[1] + (int64_t)my_i * bp.dqs[2];
+    const float sc = bp.scale;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x2 w = {cvt_pk(T{}, acc[mb][4 * q4] * sc, acc[mb][4 * q4 + 1] * sc),
+                         cvt_pk(T{}, acc[mb][4 * q4 + 2] * sc, acc[mb][4 * q4 + 3] * sc)};
+        *(u32x2*)(orow + 32 * mb + 8 * q4 + 4 * g) = w;
+      }
+  }
+}
+
+// ---- dK, dV -------------------------------------------------------------------
+template <class T, int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
+  const AttnParams& p = bp.f;
+  using L = Tile64<D>;
+  constexpr int NQ = D / 16, NMB = D / 32;
+  constexpr int STAGE = 2 * L::BYTES + 2048;  // Q, dO, LSE line, D line
+  using S = uint16_t;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // key blocks in increasing order: under causal masking the first key
+  // blocks are seen by the most query rows, so the heaviest go first
+  const int nbh = p.B * p.Hkv;
+  const int kt = (int)blockIdx.x / nbh, bhk = (int)blockIdx.x % nbh;
+  const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+  const int lq = batch_len(p.seqlens_q, b, p.Lq);
+  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int coff = lk - lq;
+  const int k0 = kt * 128;
+  const int kw0 = k0 + 32 * wave;
+  const int my_j = kw0 + l32;
+  const bool kok = my_j < lk;
+  const float c = p.scale_log2;
+
+  // this lane's key and value rows as B operands (zero past the batch's keys)
+  u32x4 kreg[NQ], vreg[NQ];
+  {
+    const int jj = kok ? my_j : 0;
+    const S* kr = (const S*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)jj * p.ks[2];
+    const S* vr = (const S*)p.v + b * p.vs[0] + hk * p.vs[1] + (int64_t)jj * p.vs[2];
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const u32x4 a = ldg16_cached(kr + (2 * s + g) * 8), d = ldg16_cached(vr + (2 * s + g) * 8);
+      kreg[s] = kok ? a : u32x4{0, 0, 0, 0};
+      vreg[s] = kok ? d : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // query tiles [qt0, nqt) of each of the group's heads
+  const int ibeg = CAUSAL ? max(0, k0 - coff) : 0;
+  const int qt0 = ibeg / 64;
+  const int nqt = k0 < lk ? (lq + 63) / 64 : 0;
+  const int per_head = max(0, nqt - qt0);
+  const int ntiles = per_head * p.group;
+
+  const uint32_t qoff = tile_lane_off<D>(wave, lane, p.qs[2]);
+  const uint32_t dooff = tile_lane_off<D>(wave, lane, bp.dos[2]);
+  const uint32_t lds0 = lds_addr(smem);
+  auto issue = [&](int t) {
+    const int hq = hk * p.group + t / per_head;
+    const int q0 = 64 * (qt0 + t % per_head);
+    const uint32_t st = lds0 + (t & 1) * STAGE;
+    const S* qb = (const S*)p.q + b * p.qs[0] + hq * p.qs[1];
+    const S* db = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1];
+    tile_issue<D>(qb, p.qs[2], q0, lq, qoff, st, wave);
+    tile_issue<D>(db, bp.dos[2], q0, lq, dooff, st + L::BYTES, wave);
+    if (wave == 0) {
+      const int64_t r0 = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
+      const uint32_t nb = (uint32_t)min(64, p.Lq - q0) * 4;
+      dma16(bp.ws_l + r0, nb, st + 2 * L::BYTES, lane * 16, 0);
+      dma16(bp.ws_d + r0, nb, st + 2 * L::BYTES + 1024, lane * 16, 0);
+    }
+  };
+
+  f32x16 dk[NMB], dv[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) dk[mb] = dv[mb] = f32x16{};
+
+  if (ntiles > 0) issue(0);
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<0>();
+    lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
+    if (t + 1 < ntiles) issue(t + 1);
+    const int hq = hk * p.group + t / per_head;
+    const int q0 = 64 * (qt0 + t % per_head);
+    // nothing of this wave's keys is visible to the tile's rows
+    if (kw0 >= lk || (CAUSAL && kw0 > q0 + 63 + coff)) continue;
+    const bool edge = MASK || q0 + 64 > lq || kw0 + 32 > lk || (CAUSAL && kw0 + 31 > q0 + coff);
+    const uint8_t* Qs = smem + (t & 1) * STAGE;
+    const uint8_t* Ds = Qs + L::BYTES;
+    const float* Ls = (const float*)(Qs + 2 * L::BYTES);
+    const float* Dv = Ls + 256;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      f32x16 s_ = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+        s_ = mma32(T{}, tile_rows<D>(Qs, 32 * qb, s, l32, g), kreg[s], s_);
+        dp = mma32(T{}, tile_rows<D>(Ds, 32 * qb, s, l32, g), vreg[s], dp);
+      }
+      f32x16 pr, ds;
+#pragma unroll
+      for (int rh = 0; rh < 4; ++rh) {
+        // rows 32 qb + 8 rh + 4 g + (0..3) of the tile
+        const int ib = 32 * qb + 8 * rh + 4 * g;
+        const f32x4 l4 = *(const f32x4*)(Ls + ib);
+        const f32x4 d4 = *(const f32x4*)(Dv + ib);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * rh + e;
+          float x = s_[r] * c;
+          if (edge) {
+            const int i = q0 + ib + e;
+            if (MASK) {
+              const int ii = i < lq ? i : lq - 1, jj = kok ? my_j : lk - 1;
+              x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]];
+            }
+            const bool vis = kok && i < lq && (!CAUSAL || my_j <= i + coff);
+            x = vis ? x : kNegInf;
+          }
+          const float pv = fast_exp2(x - l4[e]);
+          pr[r] = pv;
+          ds[r] = pv * (dp[r] - d4[e]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        constexpr bool BF = std::is_same<T, TBF16>::value;
+        const u32x4 pb = pack_b<T>(pr, u);
+        u32x4 db, dl;
+        if constexpr (BF) pack_b_split(ds, u, db, dl);
+        else db = pack_b<T>(ds, u);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          dv[mb] = mma32(T{}, tile_cols<D>(Ds, 32 * qb + 16 * u, mb, lane), pb, dv[mb]);
+          const u32x4 qa = tile_cols<D>(Qs, 32 * qb + 16 * u, mb, lane);
+          dk[mb] = mma32(T{}, qa, db, dk[mb]);
+          if constexpr (BF) dk[mb] = mma32(T{}, qa, dl, dk[mb]);
+        }
+      }
+    }
+  }
+
+  if (my_j < p.Lk) {
+    S* kr = (S*)bp.dk + b * bp.dks[0] + hk * bp.dks[1] + (int64_t)my_j * bp.dks[2];
+    S* vr = (S*)bp.dv + b * bp.dvs[0] + hk * bp.dvs[1] + (int64_t)my_j * bp.dvs[2];
+    const float sc = bp.scale;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const u32x2 wk = {cvt_pk(T{}, dk[mb][4 * q4] * sc, dk[mb][4 * q4 + 1] * sc),
+                          cvt_pk(T{}, dk[mb][4 * q4 + 2] * sc, dk[mb][4 * q4 + 3] * sc)};
+        const u32x2 wv = {cvt_pk(T{}, dv[mb][4 * q4], dv[mb][4 * q4 + 1]),
+                          cvt_pk(T{}, dv[mb][4 * q4 + 2], dv[mb][4 * q4 + 3])};
+        *(u32x2*)(kr + 32 * mb + 8 * q4 + 4 * g) = wk;
+        *(u32x2*)(vr + 32 * mb + 8 * q4 + 4 * g) = wv;
+      }
+  }
+}
+
+// ---- sink gradient: -sum over batches and rows of exp(sink - LSE_i) D_i ------
+__global__ __launch_bounds__(kBwdThreads) void bwd_dsink_kernel(BwdParams bp) {
+  const AttnParams& p = bp.f;
+  __shared__ float red[kBwdWaves];
+  const int hq = blockIdx.x;
+  const float sk = p.sinks[hq] * kLog2e;
+  float acc = 0.f;
+  for (int b = 0; b < p.B; ++b) {
+    const int64_t r0 = ((int64_t)b * p.Hq + hq) * p.Lq;
+    for (int i = threadIdx.x; i < p.Lq; i += kBwdThreads)
+      acc -= fast_exp2(sk - bp.ws_l[r0 + i]) * bp.ws_d[r0 + i];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) bp.dsinks[hq] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+template <class T, int D, bool CAUSAL, bool MASK>
+hipError_t launch_main(const BwdParams& bp, hipStream_t s) {
+  const AttnParams& p = bp.f;
+  const dim3 block(kBwdThreads);
+  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, MASK>), dim3((unsigned)((p.Lq + 127) / 128 * p.B * p.Hq)),
+                     block, 0, s, bp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, MASK>), dim3((unsigned)((p.Lk + 127) / 128 * p.B * p.Hkv)),
+                     block, 0, s, bp);
+  return hipGetLastError();
+}
+
+template <class T, int D>
+hipError_t launch_td(const BwdParams& bp, bool causal, hipStream_t s) {
+  const AttnParams& p = bp.f;
+  const int64_t nrows = (int64_t)p.B * p.Hq * p.Lq;
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((nrows + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads),
+                     0, s, bp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool mask = p.mask != nullptr;
+  if (causal) e = mask ? launch_main<T, D, true, true>(bp, s) : launch_main<T, D, true, false>(bp, s);
+  else e = mask ? launch_main<T, D, false, true>(bp, s) : launch_main<T, D, false, false>(bp, s);
+  if (e != hipSuccess) return e;
+  if (bp.dsinks) {
+    hipLaunchKernelGGL(bwd_dsink_kernel, dim3((unsigned)p.Hq), dim3(kBwdThreads), 0, s, bp);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <class T>
+hipError_t launch_t(const BwdParams& bp, bool causal, hipStream_t s) {
+  return bp.f.D == 64 ? launch_td<T, 64>(bp, causal, s) : launch_td<T, 128>(bp, causal, s);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float scale, float* ws, int dtype,
+                           bool causal, hipStream_t s) {
+  BwdParams bp{};
+  bp.f = p;
+  bp.scale = scale;
+  bp.dout = g.dout;
+  bp.dq = g.dq;
+  bp.dk = g.dk;
+  bp.dv = g.dv;
+  for (int d = 0; d < 3; ++d) {
+    bp.dos[d] = g.dout_stride[d];
+    bp.dqs[d] = g.dq_stride[d];
+    bp.dks[d] = g.dk_stride[d];
+    bp.dvs[d] = g.dv_stride[d];
+  }
+  bp.dsinks = g.dsinks;
+  const size_t nrows = (size_t)p.B * p.Hq * p.Lq;
+  bp.ws_d = ws;
+  bp.ws_l = ws + nrows;
+  if (p.sinks == nullptr) bp.dsinks = nullptr;
+  return dtype == SDPA_BF16 ? launch_t<TBF16>(bp, causal, s) : launch_t<TF16>(bp, causal, s);
+}
+
+}  // namespace sdpa

@@ -38,6 +38,9 @@ AttnParams make_params(const sdpa_args& a);
 // Kernel launchers: return hipSuccess or the launch error.
 hipError_t launch_prefill(const AttnParams& p, int dtype, bool causal, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s);
+// Gradients: ws holds 2 * B * Hq * Lq floats (D_i, then the LSE in log2 units).
+hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float scale, float* ws, int dtype,
+                           bool causal, hipStream_t s);
 
 // Decode tiling shared by the host heuristics and the kernels.
 int decode_tile_keys(int dtype, int D);

@@ -205,3 +205,66 @@ def test_python_binding_has_no_cpu_path():
     x = torch.zeros(1, 1, 4, 64)
     with pytest.raises(ValueError, match="GPU tensors"):
         sdpa.prefill(x, x, x)
+
+
+def test_backward_struct_layout_matches_c():
+    src = r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "sdpa_mi355x.h"
+#define F(f) printf("%s %zu\n", #f, offsetof(sdpa_bwd_args, f));
+int main(void) {
+  printf("sizeof %zu\n", sizeof(sdpa_bwd_args));
+  F(dout) F(dout_stride) F(dq) F(dq_stride) F(dk) F(dk_stride) F(dv) F(dv_stride) F(dsinks)
+  return 0;
+}
+"""
+    with tempfile.TemporaryDirectory() as td:
+        c = os.path.join(td, "layout.c")
+        exe = os.path.join(td, "layout")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-I", HEADER_DIR, c, "-o", exe], check=True)
+        out = subprocess.run([exe], capture_output=True, text=True, check=True).stdout
+    got = dict(l.split() for l in out.strip().splitlines())
+    assert int(got.pop("sizeof")) == ctypes.sizeof(sdpa.SdpaBwdArgs)
+    for name, off in got.items():
+        assert getattr(sdpa.SdpaBwdArgs, name).offset == int(off), name
+
+
+def _bwd(lib, ws=1 << 45, ws_bytes=1 << 30, gkw=None, **kw):
+    kw.setdefault("lse", 1 << 44)
+    a = _args(**kw)
+    g = sdpa.SdpaBwdArgs()
+    base = 1 << 41
+    for i, n in enumerate(("dout", "dq", "dk", "dv")):
+        setattr(g, n, base + i * (1 << 32))
+        st = getattr(g, n + "_stride")
+        L, H = (64, 8) if n in ("dout", "dq") else (64, 2)
+        st[0], st[1], st[2] = H * L * 128, L * 128, 128
+    for k_, v_ in (gkw or {}).items():
+        if isinstance(v_, tuple):
+            arr = getattr(g, k_)
+            for i, x in enumerate(v_):
+                arr[i] = x
+        else:
+            setattr(g, k_, v_)
+    return lib.sdpa_prefill_backward_check(ctypes.byref(a), ctypes.byref(g), ws, ws_bytes)
+
+
+def test_backward_validation(lib):
+    assert _bwd(lib) == S.OK
+    assert _bwd(lib, dtype=sdpa.F32) == S.ERR_UNSUPPORTED
+    assert _bwd(lib, D=96) == S.ERR_UNSUPPORTED
+    assert _bwd(lib, lse=None) == S.ERR_NULL
+    assert _bwd(lib, gkw={"dq": None}) == S.ERR_NULL
+    assert _bwd(lib, gkw={"dk": (1 << 41) + 8}) == S.ERR_ALIGN
+    assert _bwd(lib, gkw={"dv_stride": (2 * 64 * 128, 64 * 128, 100)}) == S.ERR_ALIGN
+    assert _bwd(lib, gkw={"dk": (1 << 41) + (1 << 32) + 64}) == S.ERR_ARG      # dk inside dq
+    assert _bwd(lib, gkw={"dq": (1 << 40) + 64}) == S.ERR_ARG                  # dq inside q
+    assert _bwd(lib, gkw={"dsinks": (1 << 46) + 2}) == S.ERR_ALIGN
+    assert _bwd(lib, ws=None) == S.ERR_WORKSPACE
+    assert _bwd(lib, ws_bytes=64) == S.ERR_WORKSPACE
+    assert _bwd(lib, ws=(1 << 45) + 8) == S.ERR_ALIGN
+    assert _bwd(lib, ws=(1 << 41) + 64) == S.ERR_ARG                           # workspace inside dout
+    a = _args()
+    assert lib.sdpa_prefill_backward_workspace_bytes(ctypes.byref(a)) == 2 * 8 * 64 * 2 * 4

@@ -1,0 +1,133 @@
+"""GPU parity of the attention gradients (sdpa_prefill_backward through the C
+ABI) against the fp64 gradient oracle: a grid of small cases spanning several
+tiles with ragged tails (GQA, bottom-right causal with Lq != Lk, rows without
+keys, additive mask with -inf entries, sinks and their gradient, per-batch
+lengths with NaN in the padding) for fp16 / bf16 and D = 64 / 128, plus the
+autograd wrapper.
+
+Tolerance: gradients are linear in dO, so the forward's elementwise bound
+(abs 2e-3, rel 1e-2 for 16-bit inputs) is applied with the absolute part
+scaled by the tensor's largest reference magnitude (at least 1):
+|got - ref| <= 2e-3 * max(1, max|ref|) + 1e-2 * |ref|.  The kernels round P
+and dS to the input type (unit roundoff 2^-11 fp16, 2^-8 bf16) before the
+second products and accumulate in fp32, which stays inside this bound."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import scaled_dot_product_prefill_amd as sdpa
+from oracle import allclose_report, sdpa_backward_reference
+from tests.gpu_util import say, to_dev
+from workloads import DTYPES, random_case
+
+pytestmark = pytest.mark.gpu
+
+
+def _report(got, ref, what):
+    ref = np.asarray(ref, dtype=np.float64)
+    s = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
+    rep = allclose_report(got.float().cpu().numpy(), ref, 2e-3 * s, 1e-2)
+    ok = rep["ok"] and rep["norm_rel"] <= 1e-2
+    say(f"  {what}: max_abs={rep['max_abs']:.3e} (scale {s:.3g}) norm_rel={rep['norm_rel']:.3e} ok={ok}")
+    return None if ok else f"{what}: {rep}"
+
+
+def _check_all(pairs):
+    """Report every gradient, then fail on the first mismatch."""
+    bad = [m for m in (_report(g, r, w) for g, r, w in pairs) if m]
+    assert not bad, bad
+
+
+def _dout(seed, shape, dtype):
+    g = np.random.default_rng([2, seed]).standard_normal(shape, dtype=np.float32)
+    return torch.from_numpy(g).to(DTYPES[dtype])
+
+
+def _run(x, dout, dtype, causal, sq=None, sk=None, want_dsinks=False):
+    d = to_dev(x)
+    D = x["q"].shape[-1]
+    sc = 1.0 / math.sqrt(D)
+    o, lse = sdpa.prefill(d["q"], d["k"], d["v"], scale=sc, causal=causal, mask=d["mask"], sinks=d["sinks"],
+                          return_lse=True, seqlens_q=sq, seqlens_k=sk)
+    res = sdpa.prefill_backward(d["q"], d["k"], d["v"], o, lse, dout.cuda(), scale=sc, causal=causal,
+                                mask=d["mask"], sinks=d["sinks"], seqlens_q=sq, seqlens_k=sk,
+                                want_dsinks=want_dsinks)
+    torch.cuda.synchronize()
+    return res, sc
+
+
+# (B, Hq, Hkv, Lq, Lk, causal, mask, sinks)
+GRID = [
+    (1, 2, 2, 200, 333, False, False, False),   # ragged non-causal
+    (2, 4, 2, 300, 300, True, False, False),    # causal Lq == Lk, GQA
+    (1, 2, 1, 100, 357, True, False, True),     # bottom-right causal Lq < Lk, sinks
+    (1, 2, 2, 260, 130, True, False, False),    # Lq > Lk: leading rows see nothing
+    (1, 3, 1, 129, 257, False, True, True),     # mask with -inf entries and sinks
+    (2, 2, 2, 64, 64, True, True, False),       # causal + mask together
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("case", range(len(GRID)))
+def test_backward_grid(dtype, D, case):
+    B, Hq, Hkv, Lq, Lk, causal, mask, sinks = GRID[case]
+    say(f"backward {dtype} D={D} case={GRID[case]}")
+    x = random_case(5000 + 10 * case + D, B, Hq, Hkv, Lq, Lk, D, dtype, mask=mask, sinks=sinks,
+                    sink_scale=2.0, mask_neg_inf_frac=0.1)
+    dout = _dout(5000 + case, x["q"].shape, dtype)
+    (dq, dk, dv, ds), sc = _run(x, dout, dtype, causal, want_dsinks=True)
+    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=causal,
+                                             mask=x["mask"], sinks=x["sinks"])
+    pairs = [(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")]
+    if sinks:
+        pairs.append((ds, rs, "dsinks"))
+    else:
+        assert ds is None
+    _check_all(pairs)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_backward_seqlens(dtype):
+    B, Hq, Hkv, Lq, Lk, D = 3, 4, 2, 300, 333, 128
+    sq, sk = [300, 129, 0], [333, 200, 3]
+    x = random_case(5100, B, Hq, Hkv, Lq, Lk, D, dtype, sinks=True, sink_scale=2.0)
+    dout = _dout(5100, x["q"].shape, dtype)
+    y = dict(x)
+    y["q"], y["k"], y["v"] = x["q"].clone(), x["k"].clone(), x["v"].clone()
+    dpad = dout.clone()
+    for b in range(B):
+        y["q"][b, :, sq[b]:] = float("nan")
+        dpad[b, :, sq[b]:] = float("nan")
+        y["k"][b, :, sk[b]:] = float("nan")
+        y["v"][b, :, sk[b]:] = float("nan")
+    (dq, dk, dv, ds), sc = _run(y, dpad, dtype, True, sq, sk, want_dsinks=True)
+    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+                                             sinks=x["sinks"], seqlens_q=np.array(sq), seqlens_k=np.array(sk))
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")])
+
+
+def test_autograd_wrapper_matches_entry_point():
+    x = to_dev(random_case(5200, 2, 4, 2, 150, 150, 64, "bf16", sinks=True))
+    q, k, v = (x[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
+    s = x["sinks"].clone().requires_grad_(True)
+    o = sdpa.attention(q, k, v, causal=True, sinks=s)
+    dout = _dout(5200, o.shape, "bf16").cuda()
+    o.backward(dout)
+    o2, lse = sdpa.prefill(x["q"], x["k"], x["v"], causal=True, sinks=x["sinks"], return_lse=True)
+    dq, dk, dv, ds = sdpa.prefill_backward(x["q"], x["k"], x["v"], o2, lse, dout, causal=True,
+                                           sinks=x["sinks"], want_dsinks=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2)
+    for a, b_ in ((q.grad, dq), (k.grad, dk), (v.grad, dv), (s.grad, ds)):
+        assert torch.equal(a, b_)
+
+
+def test_backward_rejects_unsupported():
+    x = to_dev(random_case(5300, 1, 2, 2, 8, 8, 64, "fp32"))
+    o, lse = sdpa.prefill(x["q"], x["k"], x["v"], return_lse=True)
+    with pytest.raises(sdpa.SdpaError) as e:
+        sdpa.prefill_backward(x["q"], x["k"], x["v"], o, lse, o)
+    assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
