@@ -21,7 +21,8 @@ on a bounded sample of the same workload on the host cores.
 
 Other workloads (for profiling): --workload dit_fp16|dit_fp32|causal_bf16|
 long_decode_bf16|<gqa8 decode name>|mq4_gqa8_decode_b1_lk32768_fp16 (multi-query decode)|
-kvcache_ragged_decode_bf16 (KV cache with per-batch fill levels; GB/s over the filled part).
+kvcache_ragged_decode_bf16 (KV cache with per-batch fill levels; GB/s over the filled part)|
+causal_bf16_bwd (gradients of the causal prefill; 10*D flops per visible pair).
 """
 from __future__ import annotations
 
@@ -54,6 +55,12 @@ def visible_pairs(Lq: int, Lk: int, causal: bool) -> int:
 
 def prefill_flops(w) -> int:
     return 4 * w.D * visible_pairs(w.Lq, w.Lk, w.causal) * w.B * w.Hq
+
+
+def backward_flops(w) -> int:
+    """5 products of 2*D flops per visible pair (S recomputed, dP, dV, dK, dQ):
+    the usual 2.5x of the forward count."""
+    return 10 * w.D * visible_pairs(w.Lq, w.Lk, w.causal) * w.B * w.Hq
 
 
 def decode_bytes(w) -> int:
@@ -119,6 +126,34 @@ def cpu_baseline_prefill(w, budget_s: float = 12.0):
             "kind": "oracle",
             "sample": f"{done} of {len(pairs)} (batch, head) slices of {w.name}, all {w.Lq} query rows, "
                       f"fp64 numpy, {t_used:.1f} s"}
+
+
+def cpu_baseline_backward(w, budget_s: float = 12.0):
+    """fp64 gradient oracle on whole (b, head) slices of the workload until ~budget_s."""
+    import workloads
+    from oracle import sdpa_backward_reference
+    from threadpoolctl import threadpool_info
+
+    dt = w.torch_dtype
+    done, flops, t_used = 0, 0, 0.0
+    pairs = [(b, h) for b in range(w.B) for h in range(w.Hq)]
+    for b, h in pairs:
+        hk = h // (w.Hq // w.Hkv)
+        q = workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, h, w.Lq, w.D, dt)[None, None]
+        k = workloads.slice_normal(w.cfg_id, workloads.TENSOR_K, b, hk, w.Lk, w.D, dt)[None, None]
+        v = workloads.slice_normal(w.cfg_id, workloads.TENSOR_V, b, hk, w.Lk, w.D, dt)[None, None]
+        do = workloads.slice_normal(w.cfg_id, workloads.TENSOR_DOUT, b, h, w.Lq, w.D, dt)[None, None]
+        t0 = time.perf_counter()
+        sdpa_backward_reference(q, k, v, do, scale=w.scale, causal=w.causal)
+        t_used += time.perf_counter() - t0
+        done += 1
+        flops += 10 * w.D * visible_pairs(w.Lq, w.Lk, w.causal)
+        if t_used >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / t_used / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (batch, head) slices of {w.name} (gradients), fp64 numpy, "
+                      f"{t_used:.1f} s"}
 
 
 def cpu_baseline_decode(w, budget_s: float = 8.0):
@@ -220,13 +255,22 @@ def main():
     if P is not None:
         pre_out = torch.empty_like(P["q"])
         want_lse = pre_w.lse
+        if pre_w.grad:
+            # the forward once, outside the timed region: o and lse feed the gradients
+            fwd_o, fwd_lse = sdpa.prefill(P["q"], P["k"], P["v"], scale=pre_w.scale, causal=pre_w.causal,
+                                          mask=P["mask"], sinks=P["sinks"], return_lse=True)
+            bws = torch.empty(max(16, 8 * pre_w.B * pre_w.Hq * pre_w.Lq), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
     def step(tp=None, td=None, i=0):
         if P is not None:
             if tp: tp.ev[i][0].record()
-            sdpa.prefill(P["q"], P["k"], P["v"], scale=pre_w.scale, causal=pre_w.causal,
-                         mask=P["mask"], sinks=P["sinks"], return_lse=want_lse, out=pre_out)
+            if pre_w.grad:
+                sdpa.prefill_backward(P["q"], P["k"], P["v"], fwd_o, fwd_lse, P["dout"], scale=pre_w.scale,
+                                      causal=pre_w.causal, mask=P["mask"], sinks=P["sinks"], workspace=bws)
+            else:
+                sdpa.prefill(P["q"], P["k"], P["v"], scale=pre_w.scale, causal=pre_w.causal,
+                             mask=P["mask"], sinks=P["sinks"], return_lse=want_lse, out=pre_out)
             if tp: tp.ev[i][1].record()
         if Dd is not None:
             if td: td.ev[i][0].record()
@@ -257,19 +301,20 @@ def main():
     if P is not None:
         pm = sorted(tp.ms())
         avg = sum(pm) / len(pm)
-        fl = prefill_flops(pre_w)
+        fl = backward_flops(pre_w) if pre_w.grad else prefill_flops(pre_w)
         tf = fl / (avg * 1e-3) / 1e12
         peak = PEAK_TFLOPS[pre_w.dtype]
         res.update(value=round(tf, 2), unit="TFLOP/s", dtype=pre_w.dtype)
         res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                            "frac": round(tf / peak, 4), "traffic": load_traffic("prefill_" + pre_w.name),
-                           "kernel": "prefill_kernel", "avg_ms": round(avg, 5),
+                           "kernel": ("bwd_prep + bwd_dq + bwd_dkv kernels" if pre_w.grad else "prefill_kernel"),
+                           "avg_ms": round(avg, 5),
                            "median_ms": round(pm[len(pm) // 2], 5),
                            "flops_per_launch": fl}
         cfg["workload"] = pre_w.name
         cfg.update(prefill={"B": pre_w.B, "Hq": pre_w.Hq, "Hkv": pre_w.Hkv, "Lq": pre_w.Lq,
                             "Lk": pre_w.Lk, "D": pre_w.D, "dtype": pre_w.dtype,
-                            "causal": pre_w.causal, "lse": pre_w.lse})
+                            "causal": pre_w.causal, "lse": pre_w.lse, "gradients": pre_w.grad})
     if Dd is not None:
         dm = sorted(td.ms())
         avg = sum(dm) / len(dm)
@@ -294,7 +339,7 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
         if P is not None:
-            res["cpu_baseline"] = cpu_baseline_prefill(pre_w)
+            res["cpu_baseline"] = cpu_baseline_backward(pre_w) if pre_w.grad else cpu_baseline_prefill(pre_w)
             if Dd is not None:
                 res["decode"]["cpu_baseline"] = cpu_baseline_decode(dec_w)
         else:

@@ -27,16 +27,18 @@
 //                     twice: S^T = K Q^T and dP^T = V dO^T (lanes own
 //                     queries) give D_i on the first pass (written to the
 //                     workspace), then dQ^T += K^T dS^T on the second;
-//   bwd_dkv_kernel    workgroup = 128 keys of one (batch, KV head); each wave
+//   bwd_dkv_kernel    workgroup = 256 keys of one (batch, KV head), 8 waves
+//                     (two per SIMD: K rows in registers, V rows in LDS, so
+//                     a wave fits half the register file); each wave
 //                     owns 32 keys and walks the query tiles of every query
 //                     head of the group: S = Q K^T and dP = dO V^T (lanes own
 //                     keys), then dV^T += dO^T P and dK^T += Q^T dS, so the
 //                     group's heads add up in registers (no atomics);
 //   bwd_dsink_kernel  the sink gradient, one workgroup per query head.
 // The matrix products are 32x32x16 MFMAs with fp32 accumulation; P and dS
-// enter the second products rounded to the input type, except that bf16 dS
-// (8 significant bits; dQ and dK are sums of terms of both signs) goes in as
-// bf16 hi + lo, two products.
+// enter the second products rounded to the input type.  (With D formed from
+// P and dP, bf16 dS fed as hi + lo pairs measured no more accurate than one
+// bf16 product: the outputs' own bf16 rounding dominates.)
 #include <type_traits>
 
 #include "sdpa_device.hpp"
@@ -48,19 +50,24 @@ namespace {
 constexpr int kBwdWaves = 4;
 constexpr int kBwdThreads = 64 * kBwdWaves;
 
+// dK / dV workgroups: 8 waves (two per SIMD), 32 keys each.
+constexpr int kDkvWaves = 8;
+constexpr int kDkvThreads = 64 * kDkvWaves;
+constexpr int kDkvKeys = 32 * kDkvWaves;
+
 // A 64-row tile of a [rows, D] 16-bit matrix in LDS: unpadded rows whose
 // 16-byte chunks are XOR-swizzled by the row (period 16 rows), filled by
-// direct buffer -> LDS loads: wave w writes 1 KiB lines w, w + 4, ...
-template <int D>
+// direct buffer -> LDS loads of NW waves: wave w writes 1 KiB lines w, w + NW, ...
+template <int D, int NW = kBwdWaves>
 struct Tile64 {
   static constexpr int ROWS = 64;
   static constexpr int RB = D * 2;                      // row bytes
   static constexpr int NCH = D / 8;                     // 16-byte chunks per row
   static constexpr int BYTES = ROWS * RB;
   static constexpr int LINES = BYTES / 1024;
-  static constexpr int LPW = LINES / kBwdWaves;         // lines per wave
-  static constexpr int STEP_ROWS = kBwdWaves * 64 / NCH;  // rows between a wave's lines
-  static_assert(LINES % kBwdWaves == 0 && STEP_ROWS % 16 == 0, "tile lines");
+  static constexpr int LPW = LINES / NW;                // lines per wave
+  static constexpr int STEP_ROWS = NW * 64 / NCH;       // rows between a wave's lines
+  static_assert(LINES % NW == 0 && STEP_ROWS % 16 == 0, "tile lines");
   __device__ static constexpr int swz(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & 7); }
 };
 
@@ -82,9 +89,9 @@ struct BwdParams {
 
 // Per-lane source offset of the direct loads of a Tile64: the 16 bytes that
 // land in LDS row r, chunk c come from logical chunk c ^ swz(r) of row r.
-template <int D>
+template <int D, int NW = kBwdWaves>
 __device__ inline uint32_t tile_lane_off(int wave, int lane, int64_t row_stride_elems) {
-  using L = Tile64<D>;
+  using L = Tile64<D, NW>;
   const int pos = wave * 64 + lane;
   const int row = pos / L::NCH, pch = pos % L::NCH;
   return (uint32_t)(row * row_stride_elems * 2 + (pch ^ L::swz(row)) * 16);
@@ -92,17 +99,17 @@ __device__ inline uint32_t tile_lane_off(int wave, int lane, int64_t row_stride_
 
 // Issue this wave's direct loads of rows [r0, r0 + 64) of a matrix (rows >=
 // nrows read as zero) into the Tile64 whose LDS byte address is `lds`.
-template <int D>
+template <int D, int NW = kBwdWaves>
 __device__ inline void tile_issue(const uint16_t* base, int64_t rs, int r0, int nrows, uint32_t off,
                                   uint32_t lds, int wave) {
-  using L = Tile64<D>;
+  using L = Tile64<D, NW>;
   const uint16_t* tb = base + (int64_t)r0 * rs;
   const int rows = nrows - r0;
   const uint32_t rowb = (uint32_t)(rs * 2);
   const uint32_t nb = rows >= 64 ? 0xffffffffu : (uint32_t)(rows - 1) * rowb + L::RB;
 #pragma unroll
   for (int i = 0; i < L::LPW; ++i)
-    dma16(tb, nb, lds + (wave + kBwdWaves * i) * 1024, off, i * L::STEP_ROWS * rowb);
+    dma16(tb, nb, lds + (wave + NW * i) * 1024, off, i * L::STEP_ROWS * rowb);
 }
 
 // Matrix-core A operand from a Tile64, row-major: A[m = row rb + lane%32][k =
@@ -137,17 +144,6 @@ __device__ inline u32x4 pack_b(const f32x16& x, int u) {
                cvt_pk(T{}, x[8 * u + 4], x[8 * u + 5]), cvt_pk(T{}, x[8 * u + 6], x[8 * u + 7])};
 }
 
-// registers 8u .. 8u+7 as bf16 hi + lo pairs (about 16 significant bits)
-__device__ inline void pack_b_split(const f32x16& x, int u, u32x4& hi, u32x4& lo) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    uint32_t h, l;
-    TBF16::split2(x[8 * u + 2 * e], x[8 * u + 2 * e + 1], h, l);
-    hi[e] = h;
-    lo[e] = l;
-  }
-}
-
 // ---- the LSE in log2 units ------------------------------------------------
 __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams bp) {
   const AttnParams& p = bp.f;
@@ -162,7 +158,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams bp) {
 
 // ---- dQ ---------------------------------------------------------------------
 template <class T, int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams bp) {
+__global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdParams bp) {
   const AttnParams& p = bp.f;
   using L = Tile64<D>;
   constexpr int NQ = D / 16, NMB = D / 32, NKB = 2;
@@ -279,30 +275,23 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams bp) {
     lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
     if (t + 1 < ntiles) issue(t + 1);
     const uint8_t* Ks = smem + (t & 1) * 2 * L::BYTES;
-    constexpr bool BF = std::is_same<T, TBF16>::value;
-    u32x4 dsp[NKB][2], dsl[NKB][2];
+    u32x4 dsp[NKB][2];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       f32x16 pr, dpt, ds;
       scores(Ks, Ks + L::BYTES, t, kb, t >= n_int, pr, dpt);
 #pragma unroll
       for (int r = 0; r < 16; ++r) ds[r] = pr[r] * (dpt[r] - dval);
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        if constexpr (BF) pack_b_split(ds, u, dsp[kb][u], dsl[kb][u]);
-        else dsp[kb][u] = pack_b<T>(ds, u);
-      }
+      dsp[kb][0] = pack_b<T>(ds, 0);
+      dsp[kb][1] = pack_b<T>(ds, 1);
     }
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          const u32x4 ka = tile_cols<D>(Ks, 32 * kb + 16 * u, mb, lane);
-          acc[mb] = mma32(T{}, ka, dsp[kb][u], acc[mb]);
-          if constexpr (BF) acc[mb] = mma32(T{}, ka, dsl[kb][u], acc[mb]);
-        }
+        for (int mb = 0; mb < NMB; ++mb)
+          acc[mb] = mma32(T{}, tile_cols<D>(Ks, 32 * kb + 16 * u, mb, lane), dsp[kb][u], acc[mb]);
   }
 
   if (my_i < p.Lq) {
@@ -321,13 +310,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_kernel(BwdParams bp) {
 
 // ---- dK, dV -------------------------------------------------------------------
 template <class T, int D, bool CAUSAL, bool MASK>
-__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
+__global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   const AttnParams& p = bp.f;
-  using L = Tile64<D>;
+  using L = Tile64<D, kDkvWaves>;
   constexpr int NQ = D / 16, NMB = D / 32;
   constexpr int STAGE = 2 * L::BYTES + 2048;  // Q, dO, LSE line, D line
+  constexpr int VBYTES = kDkvKeys * L::RB;     // the workgroup's value rows
   using S = uint16_t;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + VBYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -341,14 +331,17 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   const int lq = batch_len(p.seqlens_q, b, p.Lq);
   const int lk = batch_len(p.seqlens_k, b, p.Lk);
   const int coff = lk - lq;
-  const int k0 = kt * 128;
+  const int k0 = kt * kDkvKeys;
   const int kw0 = k0 + 32 * wave;
   const int my_j = kw0 + l32;
   const bool kok = my_j < lk;
   const float c = p.scale_log2;
 
-  // this lane's key and value rows as B operands (zero past the batch's keys)
-  u32x4 kreg[NQ], vreg[NQ];
+  // this lane's key row as B operands in registers and its value row, in the
+  // same operand order, in this wave's own LDS rows (each lane reads back only
+  // what it wrote); both zero past the batch's keys
+  u32x4 kreg[NQ];
+  uint8_t* const Vw = smem + 2 * STAGE + 32 * wave * L::RB;
   {
     const int jj = kok ? my_j : 0;
     const S* kr = (const S*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)jj * p.ks[2];
@@ -357,7 +350,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
     for (int s = 0; s < NQ; ++s) {
       const u32x4 a = ldg16_cached(kr + (2 * s + g) * 8), d = ldg16_cached(vr + (2 * s + g) * 8);
       kreg[s] = kok ? a : u32x4{0, 0, 0, 0};
-      vreg[s] = kok ? d : u32x4{0, 0, 0, 0};
+      lds_write16(Vw + l32 * L::RB + (((2 * s + g) ^ L::swz(l32)) * 16), kok ? d : u32x4{0, 0, 0, 0});
     }
   }
 
@@ -368,8 +361,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   const int per_head = max(0, nqt - qt0);
   const int ntiles = per_head * p.group;
 
-  const uint32_t qoff = tile_lane_off<D>(wave, lane, p.qs[2]);
-  const uint32_t dooff = tile_lane_off<D>(wave, lane, bp.dos[2]);
+  const uint32_t qoff = tile_lane_off<D, kDkvWaves>(wave, lane, p.qs[2]);
+  const uint32_t dooff = tile_lane_off<D, kDkvWaves>(wave, lane, bp.dos[2]);
   const uint32_t lds0 = lds_addr(smem);
   auto issue = [&](int t) {
     const int hq = hk * p.group + t / per_head;
@@ -377,8 +370,8 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
     const uint32_t st = lds0 + (t & 1) * STAGE;
     const S* qb = (const S*)p.q + b * p.qs[0] + hq * p.qs[1];
     const S* db = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1];
-    tile_issue<D>(qb, p.qs[2], q0, lq, qoff, st, wave);
-    tile_issue<D>(db, bp.dos[2], q0, lq, dooff, st + L::BYTES, wave);
+    tile_issue<D, kDkvWaves>(qb, p.qs[2], q0, lq, qoff, st, wave);
+    tile_issue<D, kDkvWaves>(db, bp.dos[2], q0, lq, dooff, st + L::BYTES, wave);
     if (wave == 0) {
       const int64_t r0 = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
       const uint32_t nb = (uint32_t)min(64, p.Lq - q0) * 4;
@@ -408,10 +401,14 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16 s_ = f32x16{}, dp = f32x16{};
+      // operand reads run at most two k-steps ahead of the products (a fence
+      // every second step), which keeps the wave inside half the register file
 #pragma unroll
       for (int s = 0; s < NQ; ++s) {
         s_ = mma32(T{}, tile_rows<D>(Qs, 32 * qb, s, l32, g), kreg[s], s_);
-        dp = mma32(T{}, tile_rows<D>(Ds, 32 * qb, s, l32, g), vreg[s], dp);
+        dp = mma32(T{}, tile_rows<D>(Ds, 32 * qb, s, l32, g),
+                   lds_read16(Vw + l32 * L::RB + (((2 * s + g) ^ L::swz(l32)) * 16)), dp);
+        if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
       }
       f32x16 pr, ds;
 #pragma unroll
@@ -440,17 +437,12 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        constexpr bool BF = std::is_same<T, TBF16>::value;
-        const u32x4 pb = pack_b<T>(pr, u);
-        u32x4 db, dl;
-        if constexpr (BF) pack_b_split(ds, u, db, dl);
-        else db = pack_b<T>(ds, u);
+        const u32x4 pb = pack_b<T>(pr, u), db = pack_b<T>(ds, u);
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
           dv[mb] = mma32(T{}, tile_cols<D>(Ds, 32 * qb + 16 * u, mb, lane), pb, dv[mb]);
-          const u32x4 qa = tile_cols<D>(Qs, 32 * qb + 16 * u, mb, lane);
-          dk[mb] = mma32(T{}, qa, db, dk[mb]);
-          if constexpr (BF) dk[mb] = mma32(T{}, qa, dl, dk[mb]);
+          dk[mb] = mma32(T{}, tile_cols<D>(Qs, 32 * qb + 16 * u, mb, lane), db, dk[mb]);
+          if (mb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -501,8 +493,8 @@ hipError_t launch_main(const BwdParams& bp, hipStream_t s) {
                      block, 0, s, bp);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, MASK>), dim3((unsigned)((p.Lk + 127) / 128 * p.B * p.Hkv)),
-                     block, 0, s, bp);
+  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, MASK>),
+                     dim3((unsigned)((p.Lk + kDkvKeys - 1) / kDkvKeys * p.B * p.Hkv)), dim3(kDkvThreads), 0, s, bp);
   return hipGetLastError();
 }
 

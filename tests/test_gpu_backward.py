@@ -131,3 +131,24 @@ def test_backward_rejects_unsupported():
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.prefill_backward(x["q"], x["k"], x["v"], o, lse, o)
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
+
+
+@pytest.mark.timeout(600)
+def test_causal_full_size_sampled_heads():
+    """The causal bf16 workload (B1 H32 L4096 D128) at full size, in the launch
+    configuration bench.py times; heads 0 and 31 (independent problems, one KV
+    head each) against the oracle, every element of dQ, dK, dV."""
+    import workloads
+    w = workloads.CAUSAL_BWD
+    say("backward full size", w)
+    x = workloads.make_inputs(w)
+    d = to_dev(x)
+    o, lse = sdpa.prefill(d["q"], d["k"], d["v"], scale=w.scale, causal=True, return_lse=True)
+    dq, dk, dv = sdpa.prefill_backward(d["q"], d["k"], d["v"], o, lse, d["dout"], scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    for h in (0, 31):
+        sl = slice(h, h + 1)
+        rq, rk, rv, _ = sdpa_backward_reference(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], x["dout"][:, sl],
+                                                scale=w.scale, causal=True)
+        _check_all([(dq[:, sl], rq, f"dq head {h}"), (dk[:, sl], rk, f"dk head {h}"),
+                    (dv[:, sl], rv, f"dv head {h}")])

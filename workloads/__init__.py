@@ -17,7 +17,9 @@ Recipe (the same for every tensor):
   * the long-context decode mask is float32 [B, 1, 1, Lk]: 0 for the leading
     keys and -inf for the trailing floor(Lk / 10) keys of every batch;
   * ragged KV-cache fill levels (per-batch key counts) are uniform integers
-    in [Lk / 8, Lk] from ``default_rng([0, cfg, 4])``.
+    in [Lk / 8, Lk] from ``default_rng([0, cfg, 4])``;
+  * the upstream gradient dO of a gradient workload is drawn like q with
+    tensor id 5.
 
 Seed 0 follows the reproducer script on the "Add D512 support to Metal vector
 attention" page (its ``SEED``); the shapes follow the pages' workloads (the
@@ -34,7 +36,7 @@ from typing import Dict, Optional, Tuple
 import numpy as np
 import torch
 
-TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_SINKS, TENSOR_FILL = 0, 1, 2, 3, 4
+TENSOR_Q, TENSOR_K, TENSOR_V, TENSOR_SINKS, TENSOR_FILL, TENSOR_DOUT = 0, 1, 2, 3, 4, 5
 
 DTYPES = {
     "fp32": torch.float32,
@@ -63,6 +65,7 @@ class Workload:
     lse: bool = False
     decode: bool = False           # run through sdpa_decode (always so when Lq == 1)
     fill: Optional[str] = None     # None | "ragged" (per-batch KV-cache fill levels)
+    grad: bool = False             # time the gradients (sdpa_prefill_backward) instead
 
     @property
     def is_decode(self) -> bool:
@@ -120,9 +123,12 @@ MQ_DECODE = Workload("mq4_gqa8_decode_b1_lk32768_fp16", 6, B=1, Hq=32, Hkv=4, Lq
 KVCACHE_DECODE = Workload("kvcache_ragged_decode_bf16", 7, B=8, Hq=32, Hkv=8, Lq=1, Lk=131072,
                           D=128, dtype="bf16", fill="ragged")
 
+# Gradients of the causal prefill (next-row extension): same inputs, plus dO.
+CAUSAL_BWD = CAUSAL.with_(name="causal_bf16_bwd", grad=True)
+
 ALL: Dict[str, Workload] = {w.name: w for w in
                             [TINY, DIT_FP16, DIT_FP32, CAUSAL, LONG_DECODE, *GQA_DECODE, MQ_DECODE,
-                             KVCACHE_DECODE]}
+                             KVCACHE_DECODE, CAUSAL_BWD]}
 
 
 # ---- generators --------------------------------------------------------------
@@ -174,6 +180,8 @@ def make_inputs(w: Workload, device="cpu") -> Dict[str, Optional[torch.Tensor]]:
     fill = w.seqlens_k()
     if fill is not None:
         out["seqlens_k"] = torch.from_numpy(fill).to(device)
+    if w.grad:
+        out["dout"] = tensor_normal(w.cfg_id, TENSOR_DOUT, w.B, w.Hq, w.Lq, w.D, dt, device)
     return out
 
 
