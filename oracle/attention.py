@@ -60,6 +60,15 @@ def _f64(x) -> np.ndarray:
     return np.asarray(x, dtype=np.float64)
 
 
+def _mask64(mask) -> np.ndarray:
+    """An additive mask in float64; a boolean mask (True = the key takes part,
+    the MLX convention) becomes 0 where True and -inf where False."""
+    m = mask.detach().cpu().numpy() if hasattr(mask, "detach") else np.asarray(mask)
+    if m.dtype == np.bool_:
+        return np.where(m, 0.0, -np.inf)
+    return np.asarray(m, dtype=np.float64)
+
+
 def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
                    mask=None, sinks=None, rows: Optional[Sequence[int]] = None,
                    heads: Optional[Sequence[Tuple[int, int]]] = None,
@@ -68,7 +77,8 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
     """Naive attention in fp64.
 
     q: [B, Hq, Lq, D]; k, v: [B, Hkv, Lk, D]; mask: anything broadcastable to
-    [B, Hq, Lq, Lk] (additive, may hold -inf); sinks: [Hq] or None;
+    [B, Hq, Lq, Lk], additive (may hold -inf) or boolean (False hides the
+    key); sinks: [Hq] or None;
     seqlens_q, seqlens_k: per-batch valid lengths [B] or None (= Lq, Lk).
     Padding entries of q, k and v are never read, so they may hold anything.
 
@@ -88,7 +98,7 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
-    M = None if mask is None else np.broadcast_to(_f64(mask), (B, Hq, Lq, Lk))
+    M = None if mask is None else np.broadcast_to(_mask64(mask), (B, Hq, Lq, Lk))
     S_ = None if sinks is None else _f64(sinks).reshape(Hq)
     row_idx = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     pairs = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)

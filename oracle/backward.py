@@ -35,7 +35,7 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from .attention import _f64, sdpa_reference
+from .attention import _f64, _mask64, sdpa_reference
 
 
 def sdpa_backward_reference(q, k, v, dout, *, scale: float, causal: bool = False,
@@ -48,7 +48,7 @@ def sdpa_backward_reference(q, k, v, dout, *, scale: float, causal: bool = False
     B, Hq, Lq, D = Q.shape
     Hkv, Lk = K.shape[1], K.shape[2]
     G = Hq // Hkv
-    M = None if mask is None else np.broadcast_to(_f64(mask), (B, Hq, Lq, Lk))
+    M = None if mask is None else np.broadcast_to(_mask64(mask), (B, Hq, Lq, Lk))
     SK = None if sinks is None else _f64(sinks).reshape(Hq)
     # the forward: O and LSE of the same definition
     O, LSE = sdpa_reference(q, k, v, scale=scale, causal=causal, mask=mask, sinks=sinks,

@@ -27,7 +27,12 @@ def brute_attention(q, k, v, scale, causal=False, mask=None, sinks=None, dps=50,
     B, Hq, Lq, D = Q.shape
     Hkv, Lk = K.shape[1], K.shape[2]
     group = Hq // Hkv
-    M = None if mask is None else np.broadcast_to(_np(mask), (B, Hq, Lq, Lk))
+    if mask is not None and str(getattr(mask, "dtype", "")).endswith("bool"):
+        # a boolean mask lists the keys that take part
+        keep = np.broadcast_to(np.asarray(mask.cpu() if hasattr(mask, "cpu") else mask), (B, Hq, Lq, Lk))
+        M = np.where(keep, 0.0, -math.inf)
+    else:
+        M = None if mask is None else np.broadcast_to(_np(mask), (B, Hq, Lq, Lk))
     SK = _np(sinks)
     O = np.zeros((B, Hq, Lq, D))
     LSE = np.zeros((B, Hq, Lq))

@@ -334,9 +334,24 @@ def pin_seqlens(ref):
     _close(L2, L, 0, "full lengths LSE")
 
 
+def pin_bool_mask(ref):
+    """A boolean mask (True = the key takes part) against the brute force,
+    which enumerates the listed keys, with causal masking and sinks, and a
+    row whose keys are all hidden."""
+    for n, (causal, sinks) in enumerate(((False, False), (True, True))):
+        x = random_case(170 + n, 2, 4, 2, 5, 7, 3, "fp32", sinks=sinks, sink_scale=2.0)
+        keep = np.random.default_rng(180 + n).random((2, 1, 5, 7)) < 0.6
+        keep[0, 0, 2, :] = False
+        mb = torch.from_numpy(keep)
+        O, L = ref(x["q"], x["k"], x["v"], scale=0.7, causal=causal, mask=mb, sinks=x["sinks"])
+        Ob, Lb = brute_attention(x["q"], x["k"], x["v"], 0.7, causal, mb, x["sinks"])
+        _close(O, Ob, 1e-12, f"bool mask {n} O")
+        _close(L, Lb, 1e-12, f"bool mask {n} LSE")
+
+
 PINS = [pin_hand_examples, pin_brute_force, pin_torch_sdpa, pin_torch_lse,
         pin_probabilities, pin_invariants, pin_gqa_equals_repeat, pin_split_merge,
-        pin_seqlens]
+        pin_seqlens, pin_bool_mask]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -380,6 +395,7 @@ MUTANTS = {
     "causal_on_tensor_extents": ("(row_idx[:, None] + (lk - lq))", "(row_idx[:, None] + (Lk - Lq))"),
     "padding_rows_see_keys": ("real = row_idx < lq ", "real = row_idx < Lq "),
     "padding_keys_seen": ("int(_f64(seqlens_k)[b])", "int(_f64(seqlens_k)[b]) + 1"),
+    "bool_mask_inverted": ("np.where(m, 0.0, -np.inf)", "np.where(m, -np.inf, 0.0)"),
     "sink_not_in_denominator": ("den = den + np.exp(S_[hq] - m_safe)", "den = den"),
     "sink_not_in_max": ("m = np.maximum(m, S_[hq])", "m = m"),
     "head_map_modulo": ("        g = hq // G ", "        g = hq % Hkv "),
