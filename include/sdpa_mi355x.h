@@ -28,7 +28,8 @@
  * Semantics (the same for both entry points):
  *   - query head hq reads KV head hq / (Hq / Hkv)   (Hq % Hkv must be 0);
  *   - S[i,j] = scale * (q_i . k_j) computed from the dtype inputs with fp32
- *     products and fp32 accumulation, then + mask[b,hq,i,j] (fp32);
+ *     products and fp32 accumulation, then + mask[b,hq,i,j] (fp32), or -inf
+ *     where a boolean mask is 0;
  *   - causal (bottom-right): key j is visible to query i iff
  *     j <= i + (Lk - Lq); for Lq == 1 every key is visible;
  *   - sinks[hq] (fp32, not multiplied by scale) adds exp(sinks[hq]) to the
@@ -63,9 +64,11 @@
  *     row (L) stride of k and v may be at most 8 MiB (SDPA_ERR_UNSUPPORTED
  *     above): key tiles are addressed with 32-bit offsets from their first
  *     row.
- *   - mask (optional, fp32) is indexed mask[b*s0 + hq*s1 + i*s2 + j*s3] with
+ *   - mask (optional) is indexed mask[b*s0 + hq*s1 + i*s2 + j*s3] with
  *     mask_stride[0..3] in elements; a stride of 0 broadcasts that dim (a
- *     [B,1,1,Lk] mask passes strides {Lk, 0, 0, 1}).  4-byte aligned.
+ *     [B,1,1,Lk] mask passes strides {Lk, 0, 0, 1}).  mask_kind selects
+ *     additive fp32 entries (4-byte aligned) or boolean uint8 entries
+ *     (nonzero = visible; a hidden key is the same as an additive -inf).
  *   - sinks (optional) is fp32 [Hq], contiguous (the cuDNN path on the mlx
  *     page converts sinks to float32 in prepare_sdpa_sinks).
  *   - lse (optional output) is fp32 [B, Hq, Lq], contiguous.
@@ -116,6 +119,15 @@ typedef enum sdpa_status {
   SDPA_ERR_HIP = 7          /* the HIP runtime rejected a launch                   */
 } sdpa_status;
 
+/* How `mask` is read: additive fp32 values, or a boolean (one byte per
+ * entry, nonzero = the key is visible, 0 = hidden; the boolean masks of the
+ * MLX SDPA API, which the CUDA backend on the mlx 0.30.7 page reports as
+ * unsupported, supports_bool_mask). */
+typedef enum sdpa_mask_kind {
+  SDPA_MASK_ADD_F32 = 0,
+  SDPA_MASK_BOOL = 1
+} sdpa_mask_kind;
+
 typedef struct sdpa_args {
   int64_t B;        /* batch                                   */
   int64_t Hq;       /* query heads                             */
@@ -126,7 +138,7 @@ typedef struct sdpa_args {
   int32_t dtype;    /* sdpa_dtype of q, k, v and o             */
   int32_t causal;   /* 0 or 1, bottom-right aligned            */
   float scale;      /* multiplies q.k; must be finite          */
-  int32_t reserved; /* must be 0                               */
+  int32_t mask_kind; /* sdpa_mask_kind of mask (ignored without) */
   const void *q;    int64_t q_stride[3];   /* [B, Hq,  Lq, D] */
   const void *k;    int64_t k_stride[3];   /* [B, Hkv, Lk, D] */
   const void *v;    int64_t v_stride[3];   /* [B, Hkv, Lk, D] */

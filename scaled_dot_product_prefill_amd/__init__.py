@@ -14,7 +14,8 @@ the library is missing, every entry point raises -- there is no CPU path.
     attention(q, k, v, ...)   autograd-aware prefill (forward + backward kernels)
 
 q: [B, Hq, Lq, D], k / v: [B, Hkv, Lk, D] (float32, float16 or bfloat16),
-mask: additive float tensor broadcastable to [B, Hq, Lq, Lk], sinks: [Hq],
+mask: broadcastable to [B, Hq, Lq, Lk], additive float or bool (True = the
+key takes part), sinks: [Hq],
 seqlens_q / seqlens_k: per-batch real query rows / keys [B] (padding masks).
 Returns O ([B, Hq, Lq, D], dtype of q) or (O, LSE) with LSE fp32 [B, Hq, Lq].
 """
@@ -34,6 +35,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "lib", "libsdpa_mi355x.so")
 
 F32, F16, BF16 = 0, 1, 2
+MASK_ADD_F32, MASK_BOOL = 0, 1
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
 
@@ -55,7 +57,7 @@ class SdpaArgs(ctypes.Structure):
         ("B", ctypes.c_int64), ("Hq", ctypes.c_int64), ("Hkv", ctypes.c_int64),
         ("Lq", ctypes.c_int64), ("Lk", ctypes.c_int64), ("D", ctypes.c_int64),
         ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
-        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("mask_kind", ctypes.c_int32),
         ("q", ctypes.c_void_p), ("q_stride", ctypes.c_int64 * 3),
         ("k", ctypes.c_void_p), ("k_stride", ctypes.c_int64 * 3),
         ("v", ctypes.c_void_p), ("v_stride", ctypes.c_int64 * 3),
@@ -157,7 +159,7 @@ def _make_args(q, k, v, o, scale, causal, mask, sinks, lse, seqlens_q=None, seql
     a.dtype = _DTYPE_CODE[q.dtype]
     a.causal = 1 if causal else 0
     a.scale = float(scale)
-    a.reserved = 0
+    a.mask_kind = MASK_BOOL if (mask is not None and mask.dtype == torch.bool) else MASK_ADD_F32
     for n, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         _fill(a, n, t)
     if mask is not None:
@@ -196,8 +198,8 @@ def _common(q, k, v, scale, mask, sinks, Lq_expected=None):
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     if mask is not None:
-        if mask.dtype != torch.float32:
-            mask = mask.to(torch.float32)
+        if mask.dtype != torch.float32 and mask.dtype != torch.bool:
+            mask = mask.to(torch.float32)                   # additive; bool masks stay one byte
         mask = mask.to(q.device).expand(B, Hq, Lq, Lk)     # broadcast dims get stride 0
     if sinks is not None:
         sinks = sinks.to(device=q.device, dtype=torch.float32).reshape(Hq).contiguous()

@@ -77,7 +77,8 @@ int check_sizes(const sdpa_args* a) {
   if (a->dtype != SDPA_F32 && a->dtype != SDPA_F16 && a->dtype != SDPA_BF16)
     return fail(SDPA_ERR_UNSUPPORTED, "dtype %d is not one of SDPA_F32, SDPA_F16, SDPA_BF16", a->dtype);
   if (a->causal != 0 && a->causal != 1) return fail(SDPA_ERR_ARG, "causal must be 0 or 1");
-  if (a->reserved != 0) return fail(SDPA_ERR_ARG, "reserved field must be 0");
+  if (a->mask_kind != SDPA_MASK_ADD_F32 && a->mask_kind != SDPA_MASK_BOOL)
+    return fail(SDPA_ERR_ARG, "mask_kind must be SDPA_MASK_ADD_F32 or SDPA_MASK_BOOL");
   if (!std::isfinite(a->scale)) return fail(SDPA_ERR_ARG, "scale must be finite");
   return SDPA_OK;
 }
@@ -104,8 +105,9 @@ int check_common(const sdpa_args* a) {
   // key/value tiles are addressed with 32-bit byte offsets from the tile's first row
   if (a->k_stride[2] * es > kMaxRowBytes || a->v_stride[2] * es > kMaxRowBytes)
     return fail(SDPA_ERR_UNSUPPORTED, "k/v row stride above %lld bytes", (long long)kMaxRowBytes);
+  const int mask_es = a->mask_kind == SDPA_MASK_BOOL ? 1 : 4;
   if (a->mask) {
-    if ((uintptr_t)a->mask % 4 != 0) return fail(SDPA_ERR_ALIGN, "mask is not 4-byte aligned");
+    if ((uintptr_t)a->mask % mask_es != 0) return fail(SDPA_ERR_ALIGN, "mask is not 4-byte aligned");
     for (int d = 0; d < 4; ++d)
       if (a->mask_stride[d] < 0) return fail(SDPA_ERR_ARG, "mask stride %d is negative", d);
   }
@@ -126,7 +128,7 @@ int check_common(const sdpa_args* a) {
     const int64_t last = (a->B - 1) * a->mask_stride[0] + (a->Hq - 1) * a->mask_stride[1] +
                          (a->Lq - 1) * a->mask_stride[2] + (a->Lk - 1) * a->mask_stride[3] + 1;
     em.lo = (uintptr_t)a->mask;
-    em.hi = em.lo + (uintptr_t)(last * 4);
+    em.hi = em.lo + (uintptr_t)(last * mask_es);
     em.valid = true;
   }
   Extent es_, el, esq, esk;
@@ -285,7 +287,8 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
   if (a->mask) {
     const int64_t last = (a->B - 1) * a->mask_stride[0] + (a->Hq - 1) * a->mask_stride[1] +
                          (a->Lq - 1) * a->mask_stride[2] + (a->Lk - 1) * a->mask_stride[3] + 1;
-    Extent e; e.lo = (uintptr_t)a->mask; e.hi = e.lo + (uintptr_t)(last * 4); e.valid = true; ins[n++] = e;
+    const int mes = a->mask_kind == SDPA_MASK_BOOL ? 1 : 4;
+    Extent e; e.lo = (uintptr_t)a->mask; e.hi = e.lo + (uintptr_t)(last * mes); e.valid = true; ins[n++] = e;
   }
   if (a->sinks) { Extent e; e.lo = (uintptr_t)a->sinks; e.hi = e.lo + a->Hq * 4; e.valid = true; ins[n++] = e; }
   if (a->seqlens_q) { Extent e; e.lo = (uintptr_t)a->seqlens_q; e.hi = e.lo + a->B * 4; e.valid = true; ins[n++] = e; }
@@ -321,6 +324,7 @@ AttnParams make_params(const sdpa_args& a) {
     p.vs[d] = a.v_stride[d]; p.os[d] = a.o_stride[d];
   }
   p.mask = a.mask;
+  p.mask_bool = a.mask_kind == SDPA_MASK_BOOL;
   for (int d = 0; d < 4; ++d) p.ms[d] = a.mask_stride[d];
   p.sinks = a.sinks;
   p.lse = a.lse;

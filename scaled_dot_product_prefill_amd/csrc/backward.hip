@@ -36,9 +36,12 @@
 //                     group's heads add up in registers (no atomics);
 //   bwd_dsink_kernel  the sink gradient, one workgroup per query head.
 // The matrix products are 32x32x16 MFMAs with fp32 accumulation; P and dS
-// enter the second products rounded to the input type.  (With D formed from
-// P and dP, bf16 dS fed as hi + lo pairs measured no more accurate than one
-// bf16 product: the outputs' own bf16 rounding dominates.)
+// enter the second products rounded to the input type.  bf16 P (8
+// significant bits) goes into dV as hi + lo pairs on tiles whose rows may see
+// few keys (at most 256, or any row under a mask): there single probabilities
+// are large and their rounding shows in dV, as in the forward's P.V.  (With D
+// formed from P and dP, bf16 dS fed as hi + lo measured no more accurate than
+// one bf16 product: the outputs' own bf16 rounding dominates.)
 #include <type_traits>
 
 #include "sdpa_device.hpp"
@@ -135,6 +138,17 @@ __device__ inline u32x4 tile_cols(const uint8_t* t, int rb, int mb, int lane) {
   const uint8_t* p1 = t + (vr + 8) * L::RB + ((ch ^ L::swz(vr + 8)) * 16) + (r16 & 1) * 8;
   const u32x2 a0 = lds_read_tr16(p0), a1 = lds_read_tr16(p1);
   return u32x4{a0[0], a0[1], a1[0], a1[1]};
+}
+
+// registers 8u .. 8u+7 as bf16 hi + lo pairs (about 16 significant bits)
+__device__ inline void pack_b_split(const f32x16& x, int u, u32x4& hi, u32x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    uint32_t h, l;
+    TBF16::split2(x[8 * u + 2 * e], x[8 * u + 2 * e + 1], h, l);
+    hi[e] = h;
+    lo[e] = l;
+  }
 }
 
 // registers 8u .. 8u+7 of an accumulator as a packed B operand
@@ -234,7 +248,8 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
         const int j = 64 * t + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
         if (MASK) {
           const int ii = ok ? my_i : 0, jj = j < lk ? j : lk - 1;
-          x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]];
+          x += kLog2e * mask_val(p.mask, p.mask_bool,
+                                 b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
         }
         const bool vis = j < lk && (!CAUSAL || j <= my_i + coff);
         x = vis ? x : kNegInf;
@@ -364,9 +379,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   const uint32_t qoff = tile_lane_off<D, kDkvWaves>(wave, lane, p.qs[2]);
   const uint32_t dooff = tile_lane_off<D, kDkvWaves>(wave, lane, bp.dos[2]);
   const uint32_t lds0 = lds_addr(smem);
+  // tile t = (query tile qt0 + t / G, query head hk * G + t % G)
   auto issue = [&](int t) {
-    const int hq = hk * p.group + t / per_head;
-    const int q0 = 64 * (qt0 + t % per_head);
+    const int hq = hk * p.group + t % p.group;
+    const int q0 = 64 * (qt0 + t / p.group);
     const uint32_t st = lds0 + (t & 1) * STAGE;
     const S* qb = (const S*)p.q + b * p.qs[0] + hq * p.qs[1];
     const S* db = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1];
@@ -384,69 +400,97 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) dk[mb] = dv[mb] = f32x16{};
 
-  if (ntiles > 0) issue(0);
-  for (int t = 0; t < ntiles; ++t) {
-    wait_vmcnt<0>();
-    lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
-    if (t + 1 < ntiles) issue(t + 1);
-    const int hq = hk * p.group + t / per_head;
-    const int q0 = 64 * (qt0 + t % per_head);
-    // nothing of this wave's keys is visible to the tile's rows
-    if (kw0 >= lk || (CAUSAL && kw0 > q0 + 63 + coff)) continue;
-    const bool edge = MASK || q0 + 64 > lq || kw0 + 32 > lk || (CAUSAL && kw0 + 31 > q0 + coff);
-    const uint8_t* Qs = smem + (t & 1) * STAGE;
-    const uint8_t* Ds = Qs + L::BYTES;
-    const float* Ls = (const float*)(Qs + 2 * L::BYTES);
-    const float* Dv = Ls + 256;
+  // bf16 P (8 significant bits) goes into dV as hi + lo pairs on tiles whose
+  // rows may see few keys (at most 256, or any row under a mask): there single
+  // probabilities are large and their rounding shows in dV, as in the
+  // forward's P.V.  Under causal masking rows see more keys the later the
+  // tile, so those tiles are a prefix of the loop and run in a loop of their
+  // own (one instantiation each keeps the common loop's registers unchanged).
+  int n_split = 0;
+  if (std::is_same<T, TBF16>::value) {
+    if (MASK) {
+      n_split = ntiles;
+    } else {
+      // query tiles qt0 .. qs - 1 hold a row that sees at most 256 keys
+      const int qs = CAUSAL ? (lk <= 256 ? nqt : min(nqt, max(qt0, (256 - coff) / 64 + 1))) : (lk <= 256 ? nqt : qt0);
+      n_split = (qs - qt0) * p.group;
+    }
+  }
+  auto run = [&](int t_begin, int t_end, auto split_tag) {
+    constexpr bool SPLIT = decltype(split_tag)::value;
+    for (int t = t_begin; t < t_end; ++t) {
+      wait_vmcnt<0>();
+      lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
+      if (t + 1 < ntiles) issue(t + 1);
+      const int hq = hk * p.group + t % p.group;
+      const int q0 = 64 * (qt0 + t / p.group);
+      // nothing of this wave's keys is visible to the tile's rows
+      if (kw0 >= lk || (CAUSAL && kw0 > q0 + 63 + coff)) continue;
+      const bool edge = MASK || q0 + 64 > lq || kw0 + 32 > lk || (CAUSAL && kw0 + 31 > q0 + coff);
+      const uint8_t* Qs = smem + (t & 1) * STAGE;
+      const uint8_t* Ds = Qs + L::BYTES;
+      const float* Ls = (const float*)(Qs + 2 * L::BYTES);
+      const float* Dv = Ls + 256;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s_ = f32x16{}, dp = f32x16{};
-      // operand reads run at most two k-steps ahead of the products (a fence
-      // every second step), which keeps the wave inside half the register file
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 s_ = f32x16{}, dp = f32x16{};
+        // operand reads run at most two k-steps ahead of the products (a
+        // fence every second step), which keeps the wave inside half the
+        // register file
 #pragma unroll
-      for (int s = 0; s < NQ; ++s) {
-        s_ = mma32(T{}, tile_rows<D>(Qs, 32 * qb, s, l32, g), kreg[s], s_);
-        dp = mma32(T{}, tile_rows<D>(Ds, 32 * qb, s, l32, g),
-                   lds_read16(Vw + l32 * L::RB + (((2 * s + g) ^ L::swz(l32)) * 16)), dp);
-        if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
-      }
-      f32x16 pr, ds;
-#pragma unroll
-      for (int rh = 0; rh < 4; ++rh) {
-        // rows 32 qb + 8 rh + 4 g + (0..3) of the tile
-        const int ib = 32 * qb + 8 * rh + 4 * g;
-        const f32x4 l4 = *(const f32x4*)(Ls + ib);
-        const f32x4 d4 = *(const f32x4*)(Dv + ib);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * rh + e;
-          float x = s_[r] * c;
-          if (edge) {
-            const int i = q0 + ib + e;
-            if (MASK) {
-              const int ii = i < lq ? i : lq - 1, jj = kok ? my_j : lk - 1;
-              x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]];
-            }
-            const bool vis = kok && i < lq && (!CAUSAL || my_j <= i + coff);
-            x = vis ? x : kNegInf;
-          }
-          const float pv = fast_exp2(x - l4[e]);
-          pr[r] = pv;
-          ds[r] = pv * (dp[r] - d4[e]);
+        for (int s = 0; s < NQ; ++s) {
+          s_ = mma32(T{}, tile_rows<D>(Qs, 32 * qb, s, l32, g), kreg[s], s_);
+          dp = mma32(T{}, tile_rows<D>(Ds, 32 * qb, s, l32, g),
+                     lds_read16(Vw + l32 * L::RB + (((2 * s + g) ^ L::swz(l32)) * 16)), dp);
+          if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
-      }
+        f32x16 pr, ds;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pb = pack_b<T>(pr, u), db = pack_b<T>(ds, u);
+        for (int rh = 0; rh < 4; ++rh) {
+          // rows 32 qb + 8 rh + 4 g + (0..3) of the tile
+          const int ib = 32 * qb + 8 * rh + 4 * g;
+          const f32x4 l4 = *(const f32x4*)(Ls + ib);
+          const f32x4 d4 = *(const f32x4*)(Dv + ib);
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) {
-          dv[mb] = mma32(T{}, tile_cols<D>(Ds, 32 * qb + 16 * u, mb, lane), pb, dv[mb]);
-          dk[mb] = mma32(T{}, tile_cols<D>(Qs, 32 * qb + 16 * u, mb, lane), db, dk[mb]);
-          if (mb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * rh + e;
+            float x = s_[r] * c;
+            if (edge) {
+              const int i = q0 + ib + e;
+              if (MASK) {
+                const int ii = i < lq ? i : lq - 1, jj = kok ? my_j : lk - 1;
+                x += kLog2e * mask_val(p.mask, p.mask_bool,
+                                       b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
+              }
+              const bool vis = kok && i < lq && (!CAUSAL || my_j <= i + coff);
+              x = vis ? x : kNegInf;
+            }
+            const float pv = fast_exp2(x - l4[e]);
+            pr[r] = pv;
+            ds[r] = pv * (dp[r] - d4[e]);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 db = pack_b<T>(ds, u);
+          u32x4 pb, pl;
+          if constexpr (SPLIT) pack_b_split(pr, u, pb, pl);
+          else pb = pack_b<T>(pr, u);
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            const u32x4 da = tile_cols<D>(Ds, 32 * qb + 16 * u, mb, lane);
+            dv[mb] = mma32(T{}, da, pb, dv[mb]);
+            if constexpr (SPLIT) dv[mb] = mma32(T{}, da, pl, dv[mb]);
+            dk[mb] = mma32(T{}, tile_cols<D>(Qs, 32 * qb + 16 * u, mb, lane), db, dk[mb]);
+            if (mb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
     }
-  }
+  };
+  if (ntiles > 0) issue(0);
+  if constexpr (std::is_same<T, TBF16>::value) run(0, n_split, std::true_type{});
+  run(n_split, ntiles, std::false_type{});
 
   if (my_j < p.Lk) {
     S* kr = (S*)bp.dk + b * bp.dks[0] + hk * bp.dks[1] + (int64_t)my_j * bp.dks[2];

@@ -147,8 +147,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   }
 
   // mask row of this lane's head: four consecutive keys per 16-key block
-  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] + (int64_t)qi * p.ms[2] : nullptr;
-  const bool mask_vec = MASK && p.ms[3] == 1 && (((uintptr_t)mrow) & 15) == 0;
+  const int64_t mbase = MASK ? b * p.ms[0] + (int64_t)hq * p.ms[1] + (int64_t)qi * p.ms[2] : 0;
+  const float* mrow = (const float*)p.mask + mbase;  // read as such only for fp32 masks
+  const bool mask_vec = MASK && !p.mask_bool && p.ms[3] == 1 && (((uintptr_t)mrow) & 15) == 0;
 
   f32x4 acc[C::NOB];
 #pragma unroll
@@ -258,7 +259,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
           mk = __builtin_bit_cast(f32x4, buf_load16(rm, 0));
         } else {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mk[r] = p.mask[(mrow - p.mask) + (int64_t)min(jb + r, kend - 1) * p.ms[3]];
+          for (int r = 0; r < 4; ++r)
+            mk[r] = mask_val(p.mask, p.mask_bool, mbase + (int64_t)min(jb + r, kend - 1) * p.ms[3]);
         }
       }
 #pragma unroll
@@ -475,7 +477,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
       qreg[s] = head_ok ? v : u32x4{0, 0, 0, 0};
     }
   }
-  const float* mrow = MASK ? p.mask + b * p.ms[0] + (int64_t)hq * p.ms[1] + (int64_t)qi * p.ms[2] : nullptr;
+  const int64_t mbase = MASK ? b * p.ms[0] + (int64_t)hq * p.ms[1] + (int64_t)qi * p.ms[2] : 0;
+  const float* mrow = (const float*)p.mask + mbase;  // read as such only for fp32 masks
 
   // ---- per-lane direct-load offsets (fixed across tiles): wave w issues
   //      lines w, w + 4, ...; lines [0, LINES) are K, the rest V
@@ -525,11 +528,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
     for (int blk = 0; blk < C::NBLK; ++blk) {
       const int jb = kbeg + t * C::TK + 16 * blk + 4 * g4;
       const float* mp = mrow + (int64_t)jb * p.ms[3];
-      if (p.ms[3] == 1 && jb + 3 < kend && (((uintptr_t)mp) & 15) == 0) {
+      if (!p.mask_bool && p.ms[3] == 1 && jb + 3 < kend && (((uintptr_t)mp) & 15) == 0) {
         mk[blk] = *(const f32x4*)mp;
       } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) mk[blk][r] = mrow[(int64_t)max(kbeg, min(jb + r, kend - 1)) * p.ms[3]];
+        for (int r = 0; r < 4; ++r)
+          mk[blk][r] = mask_val(p.mask, p.mask_bool, mbase + (int64_t)max(kbeg, min(jb + r, kend - 1)) * p.ms[3]);
       }
     }
   };

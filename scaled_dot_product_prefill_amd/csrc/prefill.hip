@@ -230,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
         if (MASK) {
           const int ii = my_i < lq ? my_i : lq - 1;
           const int jj = j < lk ? j : lk - 1;
-          x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] +
-                               (int64_t)jj * p.ms[3]];
+          x += kLog2e * mask_val(p.mask, p.mask_bool,
+                                 b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
         }
         if (edge) {
           const bool vis = (j < lk) && (!CAUSAL || j <= my_i + coff);
@@ -545,7 +545,8 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
           float x = sc[kb][r] * c;
           if (MASK) {
             const int jj = j < lk ? j : lk - 1;
-            x += kLog2e * p.mask[b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]];
+            x += kLog2e * mask_val(p.mask, p.mask_bool,
+                                 b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
           }
           const bool vis = (j < lk) && (!CAUSAL || j <= my_i + coff);
           x = vis ? x : kNegInf;

@@ -149,6 +149,13 @@ __device__ inline u32x4 ldg16(const void* p) {
 }
 __device__ inline u32x4 ldg16_cached(const void* p) { return *(const u32x4*)p; }
 
+// Mask entry idx (element index from the caller's strides) as an additive
+// term: the fp32 value, or 0 / -inf for a boolean (uint8) mask.
+__device__ inline float mask_val(const void* mask, int is_bool, int64_t idx) {
+  if (is_bool) return ((const uint8_t*)mask)[idx] ? 0.f : kNegInf;
+  return ((const float*)mask)[idx];
+}
+
 // Real rows of batch b along an extent of L rows: lens[b] clamped to [0, L],
 // or L when there is no per-batch length array.
 __device__ inline int batch_len(const int32_t* lens, int b, int L) {

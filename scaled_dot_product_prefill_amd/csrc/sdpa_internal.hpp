@@ -15,8 +15,9 @@ struct AttnParams {
   const void* v;
   void* o;
   int64_t qs[3], ks[3], vs[3], os[3];
-  const float* mask;
+  const void* mask;  // fp32 additive, or uint8 boolean when mask_bool
   int64_t ms[4];
+  int mask_bool;
   const float* sinks;
   float* lse;
   int B, Hq, Hkv, Lq, Lk, D;

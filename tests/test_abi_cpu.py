@@ -53,7 +53,7 @@ def test_struct_layout_matches_c():
 #define F(f) printf("%s %zu\n", #f, offsetof(sdpa_args, f));
 int main(void) {
   printf("sizeof %zu\n", sizeof(sdpa_args));
-  F(B) F(Hq) F(Hkv) F(Lq) F(Lk) F(D) F(dtype) F(causal) F(scale) F(reserved)
+  F(B) F(Hq) F(Hkv) F(Lq) F(Lk) F(D) F(dtype) F(causal) F(scale) F(mask_kind)
   F(q) F(q_stride) F(k) F(k_stride) F(v) F(v_stride) F(o) F(o_stride)
   F(mask) F(mask_stride) F(sinks) F(lse) F(seqlens_q) F(seqlens_k)
   return 0;
@@ -74,7 +74,7 @@ int main(void) {
 def _args(**kw):
     a = sdpa.SdpaArgs()
     a.B, a.Hq, a.Hkv, a.Lq, a.Lk, a.D = 2, 8, 2, 64, 64, 128
-    a.dtype, a.causal, a.scale, a.reserved = sdpa.BF16, 0, 0.125, 0
+    a.dtype, a.causal, a.scale, a.mask_kind = sdpa.BF16, 0, 0.125, 0
     # fake, aligned, non-overlapping host addresses: validation never dereferences them
     base = 1 << 40
     for i, n in enumerate(("q", "k", "v", "o")):
@@ -121,7 +121,9 @@ def test_prefill_validation(lib):
     assert _prefill(lib, scale=float("nan")) == S.ERR_ARG
     assert _prefill(lib, scale=float("inf")) == S.ERR_ARG
     assert _prefill(lib, causal=2) == S.ERR_ARG
-    assert _prefill(lib, reserved=1) == S.ERR_ARG
+    assert _prefill(lib, mask_kind=2) == S.ERR_ARG
+    assert _prefill(lib, mask=(1 << 45) + 1, mask_kind=1, mask_stride=(0, 0, 64, 1)) == S.OK   # bytes
+    assert _prefill(lib, mask=(1 << 45) + 1, mask_kind=0, mask_stride=(0, 0, 64, 1)) == S.ERR_ALIGN
     assert _prefill(lib, o=(1 << 40) + 4096) == S.ERR_ARG     # o overlaps q
     assert _prefill(lib, mask=(1 << 45) + 2) == S.ERR_ALIGN
     assert _prefill(lib, mask=1 << 45, mask_stride=(0, 0, -1, 1)) == S.ERR_ARG

@@ -152,3 +152,17 @@ def test_causal_full_size_sampled_heads():
                                                 scale=w.scale, causal=True)
         _check_all([(dq[:, sl], rq, f"dq head {h}"), (dk[:, sl], rk, f"dk head {h}"),
                     (dv[:, sl], rv, f"dv head {h}")])
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_backward_bool_mask(dtype):
+    B, Hq, Hkv, Lq, Lk, D = 1, 4, 2, 200, 190, 128
+    x = random_case(5400, B, Hq, Hkv, Lq, Lk, D, dtype, sinks=True, sink_scale=2.0)
+    keep = np.random.default_rng(5400).random((B, Hq, Lq, Lk)) < 0.7
+    keep[0, 1, 7, :] = False
+    x["mask"] = torch.from_numpy(keep)
+    dout = _dout(5400, x["q"].shape, dtype)
+    (dq, dk, dv, ds), sc = _run(x, dout, dtype, True, want_dsinks=True)
+    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+                                             mask=x["mask"], sinks=x["sinks"])
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")])

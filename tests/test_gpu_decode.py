@@ -177,3 +177,18 @@ def test_multi_query_full_size():
     out, l = sdpa.decode(d["q"], d["k"], d["v"], scale=w.scale, causal=w.causal, return_lse=True)
     torch.cuda.synchronize()
     compare_full(out, l, x, w.scale, w.dtype, f"{w.name} auto", causal=w.causal)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_bool_mask(dtype, num_splits):
+    """Boolean [B,1,1,Lk] mask (the trailing tenth hidden, plus scattered
+    holes) through the single-pass and split-K decode kernels."""
+    B, Hq, Hkv, Lk, D = 2, 16, 2, 3000, 128
+    x = random_case(2400, B, Hq, Hkv, 1, Lk, D, dtype, sinks=True)
+    keep = np.random.default_rng(2400).random((B, 1, 1, Lk)) < 0.9
+    keep[..., Lk - Lk // 10:] = False
+    x["mask"] = torch.from_numpy(keep)
+    d = to_dev(x)
+    out, l = _decode(d, 1 / math.sqrt(D), num_splits)
+    compare_full(out, l, x, 1 / math.sqrt(D), dtype, f"decode bool mask splits={num_splits}")

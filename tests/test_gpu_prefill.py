@@ -190,3 +190,18 @@ def test_rejects_unsupported():
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.prefill(x["q"], x["k"], x["v"])
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bool_mask(dtype, causal):
+    """Boolean mask (one byte per entry, True = the key takes part), broadcast
+    over heads, with rows whose keys are all hidden."""
+    B, Hq, Hkv, Lq, Lk, D = 2, 4, 2, 150, 211, 128 if dtype != "fp32" else 64
+    x = random_case(2300 + causal, B, Hq, Hkv, Lq, Lk, D, dtype, sinks=causal, sink_scale=2.0)
+    keep = np.random.default_rng(2300).random((B, 1, Lq, Lk)) < 0.7
+    keep[0, 0, 5, :] = False
+    keep[1, 0, 100:110, :] = False
+    x["mask"] = torch.from_numpy(keep)
+    out, l, sc = _run(x, dtype, causal=causal)
+    compare_full(out, l, x, sc, dtype, f"bool mask {dtype} causal={causal}", causal=causal)
