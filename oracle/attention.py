@@ -76,7 +76,8 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
                    ) -> Tuple[np.ndarray, np.ndarray]:
     """Naive attention in fp64.
 
-    q: [B, Hq, Lq, D]; k, v: [B, Hkv, Lk, D]; mask: anything broadcastable to
+    q: [B, Hq, Lq, D]; k: [B, Hkv, Lk, D]; v: [B, Hkv, Lk, Dv] (Dv may differ
+    from D; O then has head dim Dv); mask: anything broadcastable to
     [B, Hq, Lq, Lk], additive (may hold -inf) or boolean (False hides the
     key); sinks: [Hq] or None;
     seqlens_q, seqlens_k: per-batch valid lengths [B] or None (= Lq, Lk).
@@ -86,14 +87,15 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
     head); ``heads`` restricts it to those (b, hq) pairs.  The result then has
     the restricted shape [len(heads) or B*Hq ..., len(rows), D] -- see below.
 
-    Returns (O, LSE) in float64 with shapes [B, Hq, Lq', D] and [B, Hq, Lq']
+    Returns (O, LSE) in float64 with shapes [B, Hq, Lq', Dv] and [B, Hq, Lq']
     (Lq' = len(rows) when ``rows`` is given).  With ``heads`` the leading two
     dims are replaced by one dim over the listed pairs: [n, Lq', D], [n, Lq'].
     """
     Q, K, V = _f64(q), _f64(k), _f64(v)
     B, Hq, Lq, D = Q.shape
     Bk, Hkv, Lk, Dk = K.shape
-    if Bk != B or Dk != D or V.shape != K.shape:
+    Dv = V.shape[3]                                  # value / output head dim (may differ from D)
+    if Bk != B or Dk != D or V.shape[:3] != K.shape[:3]:
         raise ValueError("q/k/v shapes disagree")
     if Hq % Hkv != 0:
         raise ValueError("Hq must be a multiple of Hkv")
@@ -103,7 +105,7 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
     row_idx = np.arange(Lq) if rows is None else np.asarray(rows, dtype=np.int64)
     pairs = [(b, h) for b in range(B) for h in range(Hq)] if heads is None else list(heads)
 
-    O = np.zeros((len(pairs), len(row_idx), D))
+    O = np.zeros((len(pairs), len(row_idx), Dv))
     LSE = np.full((len(pairs), len(row_idx)), -np.inf)
 
     def lengths(b):
@@ -139,13 +141,13 @@ def sdpa_reference(q, k, v, *, scale: float, causal: bool = False,
         if S_ is not None:
             den = den + np.exp(S_[hq] - m_safe)
         # step 5: normalise; empty rows stay O = 0, LSE = -inf
-        Vb = V[b, g, :lk] if lk > 0 else np.zeros((1, D))
+        Vb = V[b, g, :lk] if lk > 0 else np.zeros((1, Dv))
         with np.errstate(divide="ignore", invalid="ignore"):
             O[n] = np.where(live[:, None], (e @ Vb) / den[:, None], 0.0)
             LSE[n] = np.where(live, m_safe + np.log(den), -np.inf)
 
     if heads is None:
-        O = O.reshape(B, Hq, len(row_idx), D)
+        O = O.reshape(B, Hq, len(row_idx), Dv)
         LSE = LSE.reshape(B, Hq, len(row_idx))
     return O, LSE
 

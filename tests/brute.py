@@ -34,7 +34,8 @@ def brute_attention(q, k, v, scale, causal=False, mask=None, sinks=None, dps=50,
     else:
         M = None if mask is None else np.broadcast_to(_np(mask), (B, Hq, Lq, Lk))
     SK = _np(sinks)
-    O = np.zeros((B, Hq, Lq, D))
+    Dv = V.shape[3]
+    O = np.zeros((B, Hq, Lq, Dv))
     LSE = np.zeros((B, Hq, Lq))
     sc = mp.mpf(float(scale))
     for b in range(B):
@@ -65,7 +66,7 @@ def brute_attention(q, k, v, scale, causal=False, mask=None, sinks=None, dps=50,
                 if den == 0:
                     LSE[b, h, i] = -math.inf
                     continue
-                for d in range(D):
+                for d in range(Dv):
                     O[b, h, i, d] = float(mp.fsum(w * mp.mpf(float(V[b, kv, j, d]))
                                                   for j, w in weights) / den)
                 LSE[b, h, i] = float(mp.log(den))

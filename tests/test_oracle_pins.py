@@ -349,9 +349,23 @@ def pin_bool_mask(ref):
         _close(L, Lb, 1e-12, f"bool mask {n} LSE")
 
 
+def pin_value_head_dim(ref):
+    """Values with a head dim other than the keys' (D_v != D_qk): brute force,
+    and the output columns are those of V alone (splitting V by columns
+    splits O the same way)."""
+    x = random_case(190, 2, 4, 2, 4, 6, 3, "fp32", sinks=True, sink_scale=1.5)
+    v5 = torch.from_numpy(np.random.default_rng(191).standard_normal((2, 2, 6, 5)).astype(np.float32))
+    O, L = ref(x["q"], x["k"], v5, scale=0.8, causal=True, sinks=x["sinks"])
+    Ob, Lb = brute_attention(x["q"], x["k"], v5, 0.8, True, None, x["sinks"])
+    _close(O, Ob, 1e-12, "Dv != D O")
+    _close(L, Lb, 1e-12, "Dv != D LSE")
+    O2, _ = ref(x["q"], x["k"], v5[..., 1:4], scale=0.8, causal=True, sinks=x["sinks"])
+    _close(O[..., 1:4], O2, 1e-14, "value columns")
+
+
 PINS = [pin_hand_examples, pin_brute_force, pin_torch_sdpa, pin_torch_lse,
         pin_probabilities, pin_invariants, pin_gqa_equals_repeat, pin_split_merge,
-        pin_seqlens, pin_bool_mask]
+        pin_seqlens, pin_bool_mask, pin_value_head_dim]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
