@@ -56,8 +56,12 @@
  *     only enqueues kernels on `stream` (a hipStream_t; NULL = the null
  *     stream) and returns; execution errors surface at the caller's next
  *     synchronisation.
- *   - q, k, v, o are 4-D [B, H, L, D] tensors whose last dim (D) is
- *     contiguous; *_stride[0..2] are ELEMENT strides of the B, H and L dims.
+ *   - q, k are 4-D [B, H, L, D] and v, o [B, H, L, Dv] tensors (Dv = D
+ *     unless set; the cuDNN path on the mlx page takes D_qk and D_v
+ *     separately) whose last dim is contiguous; *_stride[0..2] are ELEMENT
+ *     strides of the B, H and L dims.  D and Dv are multiples of 8; the
+ *     kernels run at the next of 64, 128, 256, 512 above both ("kernel head
+ *     dim" below) with the extra columns zero.
  *     Base pointers must be 16-byte aligned and every stride * element size
  *     a multiple of 16 bytes (the input preparation rule of prepare_sdpa_input
  *     on the mlx 0.30.7 page: unit last-dim stride, aligned pointer).  The
@@ -134,7 +138,7 @@ typedef struct sdpa_args {
   int64_t Hkv;      /* key/value heads (Hq % Hkv == 0)         */
   int64_t Lq;       /* queries per head                        */
   int64_t Lk;       /* keys per head                           */
-  int64_t D;        /* head dim (q, k and v share it)          */
+  int64_t D;        /* head dim of q and k (v, o: Dv below)    */
   int32_t dtype;    /* sdpa_dtype of q, k, v and o             */
   int32_t causal;   /* 0 or 1, bottom-right aligned            */
   float scale;      /* multiplies q.k; must be finite          */
@@ -148,10 +152,12 @@ typedef struct sdpa_args {
   float *lse;                                /* optional [B, Hq, Lq] fp32 out */
   const int32_t *seqlens_q;                  /* optional [B] real query rows  */
   const int32_t *seqlens_k;                  /* optional [B] real keys        */
+  int64_t Dv;       /* head dim of v and o; 0 means D          */
 } sdpa_args;
 
 /* Prefill / full self-attention, any Lq >= 1, Lk >= 1.
- * Supported: D in {64, 128} for F32, F16 and BF16; D = 256 for F16 and BF16.
+ * Supported: kernel head dim 64 or 128 for F32, F16 and BF16; 256 for F16 and
+ * BF16 (so any D, Dv that are multiples of 8 up to 128, or 256).
  * One kernel launch. */
 SDPA_API int sdpa_prefill(const sdpa_args *args, void *stream);
 
@@ -163,7 +169,8 @@ SDPA_API int sdpa_prefill_check(const sdpa_args *args);
  * whose keys stream once per KV head.  The Lq query rows and the Hq / Hkv
  * query heads sharing a KV head are processed together; causal is
  * bottom-right within the query block (it has no effect for Lq == 1).
- * Supported: D in {64, 128, 256, 512}; dtype F32, F16, BF16; any Hq / Hkv.
+ * Supported: head dims that are multiples of 8 up to 512 (kernel head dim
+ * 64, 128, 256, 512); dtype F32, F16, BF16; any Hq / Hkv.
  * num_splits = 0 picks the split count automatically; 1 forces the
  * single-pass kernel; n >= 2 forces the two-pass split-K kernel pair with n
  * splits of the key range (n <= Lk).  The two-pass form needs a workspace of
@@ -183,7 +190,7 @@ SDPA_API int sdpa_decode_num_splits(const sdpa_args *args, int num_splits);
 
 /* Workspace bytes sdpa_decode needs for this request and num_splits
  * (0 when the single-pass kernel is used or the request is invalid):
- * B * Hq * Lq * splits * (D + 2) * 4. */
+ * B * Hq * Lq * splits * (kernel head dim + 2) * 4. */
 SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_splits);
 
 /* ---- gradients ------------------------------------------------------------
@@ -207,7 +214,7 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_split
  * dK and dV of a KV head sum over the
  * Hq / Hkv query heads that read it.  The mask is a constant (no gradient).
  * Padding rows (past seqlens_q[b]) get dQ = 0, padding keys dK = dV = 0.
- * Supported: dtype F16 or BF16, D in {64, 128}.  dq, dk, dv are written in
+ * Supported: dtype F16 or BF16, D = Dv in {64, 128}.  dq, dk, dv are written in
  * the input dtype with the layout rules of q, k, v (last dim contiguous,
  * 16-byte aligned pointers and strides); dsinks (optional, used only with
  * sinks) is fp32 [Hq].  The workspace (device memory, 16-byte aligned,

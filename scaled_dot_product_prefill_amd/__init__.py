@@ -67,6 +67,7 @@ class SdpaArgs(ctypes.Structure):
         ("lse", ctypes.c_void_p),
         ("seqlens_q", ctypes.c_void_p),
         ("seqlens_k", ctypes.c_void_p),
+        ("Dv", ctypes.c_int64),
     ]
 
 
@@ -156,6 +157,7 @@ def _make_args(q, k, v, o, scale, causal, mask, sinks, lse, seqlens_q=None, seql
     a = SdpaArgs()
     a.B, a.Hq, a.Lq, a.D = B, Hq, Lq, D
     a.Hkv, a.Lk = k.shape[1], k.shape[2]
+    a.Dv = v.shape[3]
     a.dtype = _DTYPE_CODE[q.dtype]
     a.causal = 1 if causal else 0
     a.scale = float(scale)
@@ -192,7 +194,7 @@ def _common(q, k, v, scale, mask, sinks, Lq_expected=None):
         raise ValueError("q, k and v must be GPU tensors (there is no CPU path)")
     q, k, v = _prep(q, "q"), _prep(k, "k"), _prep(v, "v")
     B, Hq, Lq, D = q.shape
-    if k.shape != v.shape or k.shape[0] != B or k.shape[3] != D:
+    if k.shape[:3] != v.shape[:3] or k.shape[0] != B or k.shape[3] != D:
         raise ValueError(f"shape mismatch q {tuple(q.shape)} k {tuple(k.shape)} v {tuple(v.shape)}")
     Lk = k.shape[2]
     if scale is None:
@@ -216,7 +218,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     lib = library()
     q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    o = torch.empty((B, Hq, Lq, v.shape[3]), dtype=q.dtype, device=q.device) if out is None else out
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
     sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
     sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
@@ -236,19 +238,20 @@ def _decode_args(q, k, v, scale, mask, sinks):
 def decode_num_splits(q, k, v, *, num_splits: int = 0) -> int:
     """Splits of the key range sdpa_decode would use (1 = single pass)."""
     lib = library()
-    return int(lib.sdpa_decode_num_splits(ctypes.byref(_size_args(q, k)), int(num_splits)))
+    return int(lib.sdpa_decode_num_splits(ctypes.byref(_size_args(q, k, v)), int(num_splits)))
 
 
 def decode_workspace_bytes(q, k, v, *, num_splits: int = 0) -> int:
     lib = library()
-    return int(lib.sdpa_decode_workspace_bytes(ctypes.byref(_size_args(q, k)), int(num_splits)))
+    return int(lib.sdpa_decode_workspace_bytes(ctypes.byref(_size_args(q, k, v)), int(num_splits)))
 
 
-def _size_args(q, k) -> SdpaArgs:
+def _size_args(q, k, v=None) -> SdpaArgs:
     """Sizes-only argument block for the split / workspace queries."""
     a = SdpaArgs()
     a.B, a.Hq, a.Lq, a.D = q.shape
     a.Hkv, a.Lk = k.shape[1], k.shape[2]
+    a.Dv = v.shape[3] if v is not None else 0
     a.dtype = _DTYPE_CODE[q.dtype]
     a.scale = 1.0
     return a
@@ -267,7 +270,7 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
     lib = library()
     q, k, v, scale, mask, sinks = _decode_args(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
-    o = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    o = torch.empty((B, Hq, Lq, v.shape[3]), dtype=q.dtype, device=q.device) if out is None else out
     lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
     sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
     sk = _lengths(seqlens_k, B, q.device, "seqlens_k")

@@ -62,6 +62,19 @@ bool overlaps(const Extent& a, const Extent& b) {
   return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi;
 }
 
+// Head dim of v and o (0 in the argument block means the q / k head dim).
+int64_t dv_of(const sdpa_args* a) { return a->Dv ? a->Dv : a->D; }
+
+// The kernels' head dim: the real dims rounded up to 64, 128, 256 or 512
+// (0 beyond 512).  Chunks past the real dims are zero-filled on load and not
+// stored.
+int kernel_dim(const sdpa_args* a) {
+  const int64_t d = a->D > dv_of(a) ? a->D : dv_of(a);
+  for (int k : {64, 128, 256, 512})
+    if (d <= k) return k;
+  return 0;
+}
+
 // Size and scalar checks (no pointers examined).
 int check_sizes(const sdpa_args* a) {
   if (!a) return fail(SDPA_ERR_NULL, "args is NULL");
@@ -72,6 +85,10 @@ int check_sizes(const sdpa_args* a) {
   if (a->Hq % a->Hkv != 0)
     return fail(SDPA_ERR_SHAPE, "Hq (%lld) must be a multiple of Hkv (%lld)", (long long)a->Hq,
                 (long long)a->Hkv);
+  if (a->Dv < 0) return fail(SDPA_ERR_SHAPE, "Dv must be >= 0 (0 = D), got %lld", (long long)a->Dv);
+  if (a->D % 8 != 0 || dv_of(a) % 8 != 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "head dims must be multiples of 8, got D=%lld Dv=%lld", (long long)a->D,
+                (long long)dv_of(a));
   if (a->Lq > kMaxInt / 2 || a->Lk > kMaxInt / 2 || a->B * a->Hq > kMaxInt / 2)
     return fail(SDPA_ERR_UNSUPPORTED, "sizes beyond the 32-bit index range of the kernels");
   if (a->dtype != SDPA_F32 && a->dtype != SDPA_F16 && a->dtype != SDPA_BF16)
@@ -101,7 +118,7 @@ int check_common(const sdpa_args* a) {
                     names[t], d, (long long)strides[t][d]);
     }
   }
-  if (a->o_stride[2] < a->D) return fail(SDPA_ERR_ARG, "o rows overlap (o_stride[2] < D)");
+  if (a->o_stride[2] < dv_of(a)) return fail(SDPA_ERR_ARG, "o rows overlap (o_stride[2] < Dv)");
   // key/value tiles are addressed with 32-bit byte offsets from the tile's first row
   if (a->k_stride[2] * es > kMaxRowBytes || a->v_stride[2] * es > kMaxRowBytes)
     return fail(SDPA_ERR_UNSUPPORTED, "k/v row stride above %lld bytes", (long long)kMaxRowBytes);
@@ -119,10 +136,10 @@ int check_common(const sdpa_args* a) {
   if (a->lse && (uintptr_t)a->lse % 4 != 0) return fail(SDPA_ERR_ALIGN, "lse is not 4-byte aligned");
 
   // the output must not overlap any input or the other output
-  const Extent eo = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, a->D, es);
+  const Extent eo = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, dv_of(a), es);
   const Extent eq = tensor_extent(a->q, a->q_stride, a->B, a->Hq, a->Lq, a->D, es);
   const Extent ek = tensor_extent(a->k, a->k_stride, a->B, a->Hkv, a->Lk, a->D, es);
-  const Extent ev = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, a->D, es);
+  const Extent ev = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, dv_of(a), es);
   Extent em;
   if (a->mask) {
     const int64_t last = (a->B - 1) * a->mask_stride[0] + (a->Hq - 1) * a->mask_stride[1] +
@@ -148,9 +165,11 @@ int check_common(const sdpa_args* a) {
 int check_prefill(const sdpa_args* a) {
   int st = check_common(a);
   if (st != SDPA_OK) return st;
-  if (a->D != 64 && a->D != 128 && !(a->D == 256 && a->dtype != SDPA_F32))
-    return fail(SDPA_ERR_UNSUPPORTED, "prefill supports D in {64, 128} (and 256 for fp16/bf16), got %lld",
-                (long long)a->D);
+  const int kd = kernel_dim(a);
+  if (kd == 0 || kd > (a->dtype == SDPA_F32 ? 128 : 256))
+    return fail(SDPA_ERR_UNSUPPORTED,
+                "prefill supports head dims up to 128 (fp32) or 256 (fp16/bf16), got D=%lld Dv=%lld",
+                (long long)a->D, (long long)dv_of(a));
   const int64_t grid = ((a->Lq + 127) / 128) * a->B * a->Hq;
   if (grid > kMaxInt) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
   return SDPA_OK;
@@ -188,7 +207,7 @@ SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
   if (num_splits >= 2) {
     len = (Lk + num_splits - 1) / num_splits;
   } else {
-    const int64_t tk = decode_tile_keys(a->dtype, (int)a->D);
+    const int64_t tk = decode_tile_keys(a->dtype, kernel_dim(a));
     const int64_t tiles = (Lk + tk - 1) / tk;
     const int64_t units = a->B * a->Hkv * decode_chunks(a);
     int64_t ns = (kDecodeCUs + units - 1) / units;
@@ -205,7 +224,7 @@ SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
 
 size_t workspace_for(const sdpa_args* a, const SplitPlan& sp) {
   if (sp.nsplit <= 1) return 0;
-  return (size_t)a->B * a->Hq * a->Lq * sp.nsplit * (a->D + 2) * sizeof(float);
+  return (size_t)a->B * a->Hq * a->Lq * sp.nsplit * (kernel_dim(a) + 2) * sizeof(float);
 }
 
 int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_bytes, SplitPlan* out) {
@@ -213,8 +232,9 @@ int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_b
   if (st != SDPA_OK) return st;
   if (a->Lq > kMaxDecodeLq)
     return fail(SDPA_ERR_UNSUPPORTED, "decode supports 1 <= Lq <= %d, got %lld", kMaxDecodeLq, (long long)a->Lq);
-  if (a->D != 64 && a->D != 128 && a->D != 256 && a->D != 512)
-    return fail(SDPA_ERR_UNSUPPORTED, "decode supports D in {64, 128, 256, 512}, got %lld", (long long)a->D);
+  if (kernel_dim(a) == 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "decode supports head dims up to 512, got D=%lld Dv=%lld", (long long)a->D,
+                (long long)dv_of(a));
   if (num_splits < 0 || num_splits > a->Lk)
     return fail(SDPA_ERR_ARG, "num_splits must be in [0, Lk], got %d", num_splits);
   SplitPlan sp = plan_splits(a, num_splits);
@@ -240,8 +260,9 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
   if (st != SDPA_OK) return st;
   if (!g) return fail(SDPA_ERR_NULL, "gradient arguments are NULL");
   if (a->dtype == SDPA_F32) return fail(SDPA_ERR_UNSUPPORTED, "backward supports F16 and BF16 inputs");
-  if (a->D != 64 && a->D != 128)
-    return fail(SDPA_ERR_UNSUPPORTED, "backward supports D in {64, 128}, got %lld", (long long)a->D);
+  if ((a->D != 64 && a->D != 128) || dv_of(a) != a->D)
+    return fail(SDPA_ERR_UNSUPPORTED, "backward supports D = Dv in {64, 128}, got D=%lld Dv=%lld", (long long)a->D,
+                (long long)dv_of(a));
   if (!a->lse) return fail(SDPA_ERR_NULL, "backward needs the forward's lse");
   if (!g->dout || !g->dq || !g->dk || !g->dv) return fail(SDPA_ERR_NULL, "dout, dq, dk and dv must be non-NULL");
   const void* ptrs[4] = {g->dout, g->dq, g->dk, g->dv};
@@ -329,7 +350,10 @@ AttnParams make_params(const sdpa_args& a) {
   p.sinks = a.sinks;
   p.lse = a.lse;
   p.B = (int)a.B; p.Hq = (int)a.Hq; p.Hkv = (int)a.Hkv;
-  p.Lq = (int)a.Lq; p.Lk = (int)a.Lk; p.D = (int)a.D;
+  p.Lq = (int)a.Lq; p.Lk = (int)a.Lk;
+  p.D = kernel_dim(&a);
+  p.Dqk = (int)a.D;
+  p.Dv = (int)dv_of(&a);
   p.group = (int)(a.Hq / a.Hkv);
   p.causal = a.causal;
   p.seqlens_q = a.seqlens_q;
@@ -385,7 +409,7 @@ int sdpa_decode(const sdpa_args* args, int num_splits, void* workspace, size_t w
   if (sp.nsplit > 1) {
     float* ws = (float*)workspace;
     p.part_o = ws;
-    p.part_ml = ws + (size_t)args->B * args->Hq * args->Lq * sp.nsplit * args->D;
+    p.part_ml = ws + (size_t)args->B * args->Hq * args->Lq * sp.nsplit * sdpa::kernel_dim(args);
   }
   return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
 }

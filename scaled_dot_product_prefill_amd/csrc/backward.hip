@@ -187,8 +187,8 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
   int qt, bh;
   prefill_tile((int)blockIdx.x, (int)gridDim.x, nqt, p.B * p.Hq, CAUSAL, qt, bh);
   const int b = bh / p.Hq, hq = bh % p.Hq, hk = hq / p.group;
-  const int lq = batch_len(p.seqlens_q, b, p.Lq);
-  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
+  const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
   const int coff = lk - lq;
   const int i0 = qt * 128;
   const int my_i = i0 + 32 * wave + l32;
@@ -343,8 +343,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   const int nbh = p.B * p.Hkv;
   const int kt = (int)blockIdx.x / nbh, bhk = (int)blockIdx.x % nbh;
   const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
-  const int lq = batch_len(p.seqlens_q, b, p.Lq);
-  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
+  const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
   const int coff = lk - lq;
   const int k0 = kt * kDkvKeys;
   const int kw0 = k0 + 32 * wave;

@@ -139,10 +139,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   {
     const int s0 = wave < C::QSPLIT ? wave * C::NSW : 0;
     const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1] + (int64_t)qi * p.qs[2];
+    const int nqk = p.Dqk / C::VEC;  // real chunks of a q / k row; the rest is zero
 #pragma unroll
     for (int s = 0; s < C::NSW; ++s) {
-      u32x4 v = ldg16_cached(row + (4 * (s0 + s) + g4) * C::VEC);
-      qreg[s] = head_ok ? v : u32x4{0, 0, 0, 0};
+      const int ch = 4 * (s0 + s) + g4;
+      u32x4 v = ldg16_cached(row + min(ch, nqk - 1) * C::VEC);
+      qreg[s] = head_ok && ch < nqk ? v : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -157,20 +159,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   float m_run = kNegInf;
   float l_run = 0.f;
 
-  // ---- tile loads (buffer resources zero-fill keys at or past kend)
-  auto valid_bytes = [&](int j0, int64_t stride) -> uint32_t {
-    const int64_t nb = (int64_t)(kend - j0 - 1) * stride * C::ES + D * C::ES;
-    return nb > 0xffffffffLL ? 0xffffffffu : (uint32_t)nb;
+  // ---- tile loads (buffer resources zero-fill keys at or past kend, and
+  //      chunks past the real head dims, whose offset is set to the tile's
+  //      byte count)
+  auto valid_bytes = [&](int j0, int64_t stride, int real_d) -> uint32_t {
+    return (uint32_t)((int64_t)(min(kend - j0, C::TK) - 1) * stride * C::ES + real_d * C::ES);
   };
   u32x4 kpre[C::K_IT];
   u32x4 vpre[C::V_IT][C::F32 ? 4 : 1];
   auto prefetch = [&](int j0) {
-    const auto rk = make_rsrc(kp + (int64_t)j0 * p.ks[2], valid_bytes(j0, p.ks[2]));
-    const auto rv = make_rsrc(vp + (int64_t)j0 * p.vs[2], valid_bytes(j0, p.vs[2]));
+    const uint32_t nk = valid_bytes(j0, p.ks[2], p.Dqk), nv = valid_bytes(j0, p.vs[2], p.Dv);
+    const auto rk = make_rsrc(kp + (int64_t)j0 * p.ks[2], nk);
+    const auto rv = make_rsrc(vp + (int64_t)j0 * p.vs[2], nv);
 #pragma unroll
     for (int it = 0; it < C::K_IT; ++it) {
       const int u = tid + kThreads * it;
-      kpre[it] = buf_load16(rk, (uint32_t)((u / C::NCH) * p.ks[2] * C::ES + (u % C::NCH) * 16));
+      const int c = u % C::NCH;
+      kpre[it] = buf_load16(rk, c * C::VEC < p.Dqk ? (uint32_t)((u / C::NCH) * p.ks[2] * C::ES + c * 16) : kNoLoad);
     }
 #pragma unroll
     for (int it = 0; it < C::V_IT; ++it) {
@@ -179,9 +184,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
         const int kg = u / C::NCH, c = u % C::NCH;
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          vpre[it][r] = buf_load16(rv, (uint32_t)((4 * kg + r) * p.vs[2] * C::ES + c * 16));
+          vpre[it][r] =
+              buf_load16(rv, c * C::VEC < p.Dv ? (uint32_t)((4 * kg + r) * p.vs[2] * C::ES + c * 16) : kNoLoad);
       } else {
-        vpre[it][0] = buf_load16(rv, (uint32_t)((u / C::NCH) * p.vs[2] * C::ES + (u % C::NCH) * 16));
+        const int c = u % C::NCH;
+        vpre[it][0] =
+            buf_load16(rv, c * C::VEC < p.Dv ? (uint32_t)((u / C::NCH) * p.vs[2] * C::ES + c * 16) : kNoLoad);
       }
     }
   };
@@ -399,7 +407,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < C::NOB; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) orow[out_d(i, r)] = T::from_f32(acc[i][r] * so);
+        for (int r = 0; r < 4; ++r)
+          if (out_d(i, r) < p.Dv) orow[out_d(i, r)] = T::from_f32(acc[i][r] * so);
       if (p.lse && wave == 0 && g4 == 0) p.lse[bh] = lse;
     }
   }
@@ -471,10 +480,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   u32x4 qreg[C::NQ];
   {
     const S* row = (const S*)p.q + b * p.qs[0] + (int64_t)hq * p.qs[1] + (int64_t)qi * p.qs[2];
+    const int nqk = p.Dqk / 8;  // real chunks of a q / k row; the rest is zero
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
-      const u32x4 v = ldg16_cached(row + (4 * s + g4) * 8);
-      qreg[s] = head_ok ? v : u32x4{0, 0, 0, 0};
+      const u32x4 v = ldg16_cached(row + min(4 * s + g4, nqk - 1) * 8);
+      qreg[s] = head_ok && 4 * s + g4 < nqk ? v : u32x4{0, 0, 0, 0};
     }
   }
   const int64_t mbase = MASK ? b * p.ms[0] + (int64_t)hq * p.ms[1] + (int64_t)qi * p.ms[2] : 0;
@@ -482,6 +492,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
 
   // ---- per-lane direct-load offsets (fixed across tiles): wave w issues
   //      lines w, w + 4, ...; lines [0, LINES) are K, the rest V
+  //      (a chunk past the real head dim loads nothing: kNoLoad)
   uint32_t voff[C::LPW];
 #pragma unroll
   for (int i = 0; i < C::LPW; ++i) {
@@ -489,19 +500,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
     const int pos = ln * 64 + lane;                 // 16-byte slot within the tile
     const int row = pos / C::NCH, pch = pos % C::NCH;
     const int lch = pch ^ chunk_swz<C::NCH>(row);
-    const int64_t stride = (wave + kWaves * i) < C::LINES ? p.ks[2] : p.vs[2];
-    voff[i] = (uint32_t)(row * stride * 2 + lch * 16);
+    const bool is_k = (wave + kWaves * i) < C::LINES;
+    const int64_t stride = is_k ? p.ks[2] : p.vs[2];
+    voff[i] = lch * 8 < (is_k ? p.Dqk : p.Dv) ? (uint32_t)(row * stride * 2 + lch * 16) : kNoLoad;
   }
-  auto valid_bytes = [&](int j0, int64_t stride) -> uint32_t {
-    const int64_t nb = (int64_t)(kend - j0 - 1) * stride * 2 + D * 2;
-    return nb > 0xffffffffLL ? 0xffffffffu : (uint32_t)nb;
+  auto valid_bytes = [&](int j0, int64_t stride, int real_d) -> uint32_t {
+    return (uint32_t)((int64_t)(min(kend - j0, C::TK) - 1) * stride * 2 + real_d * 2);
   };
   auto issue = [&](int t) {
     if (t >= ntiles) return;
     const int j0 = kbeg + t * C::TK;
     const S* tk = kp + (int64_t)j0 * p.ks[2];
     const S* tv = vp + (int64_t)j0 * p.vs[2];
-    const uint32_t nk = valid_bytes(j0, p.ks[2]), nv = valid_bytes(j0, p.vs[2]);
+    const uint32_t nk = valid_bytes(j0, p.ks[2], p.Dqk), nv = valid_bytes(j0, p.vs[2], p.Dv);
     const uint32_t st = lds_addr(ring) + (t % C::NST) * C::STAGE;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) {
@@ -665,8 +676,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < C::NOB; ++i) {
         const f32x4 o = acc[i] * so;
-        *(u32x2*)(orow + 16 * (wave * C::NOB + i) + 4 * g4) =
-            u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
+        if (16 * (wave * C::NOB + i) + 4 * g4 < p.Dv)
+          *(u32x2*)(orow + 16 * (wave * C::NOB + i) + 4 * g4) = u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
       }
       if (p.lse && wave == 0 && g4 == 0) p.lse[bh] = lse;
     }
@@ -736,8 +747,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
     for (int g = 1; g < NSG; ++g) o += part[g][dq];
     const float inv = live ? 1.f / L : 0.f;
     S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)qi * p.os[2] + d0 + 4 * dq;
+    if (d0 + 4 * dq < p.Dv)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) orow[e] = T::from_f32(o[e] * inv);
+      for (int e = 0; e < 4; ++e) orow[e] = T::from_f32(o[e] * inv);
     if (p.lse && blockIdx.x % nslice == 0 && dq == 0)
       p.lse[bh] = live ? (M + fast_log2(L)) * kLn2 : kNegInf;
   }

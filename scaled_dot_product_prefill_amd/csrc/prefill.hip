@@ -99,8 +99,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
   const int iw = i0 + 32 * wave;      // first query row of this wave
   const int my_i = iw + l32;          // this lane's query row
   // real query rows and keys of this batch; bottom-right causal offset
-  const int lq = batch_len(p.seqlens_q, b, p.Lq);
-  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
+  const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
   const int coff = lk - lq;
 
   const S* qp = (const S*)p.q + b * p.qs[0] + hq * p.qs[1];
@@ -112,10 +112,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
   {
     const bool ok = my_i < lq;
     const S* row = qp + (int64_t)(ok ? my_i : 0) * p.qs[2];
+    const int nqk = p.Dqk / C::VEC;  // real chunks of a q / k row; the rest is zero
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
-      u32x4 v = ldg16_cached(row + (2 * s + g) * C::VEC);
-      qreg[s] = ok ? v : u32x4{0, 0, 0, 0};
+      u32x4 v = ldg16_cached(row + min(2 * s + g, nqk - 1) * C::VEC);
+      qreg[s] = ok && 2 * s + g < nqk ? v : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -144,8 +145,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
       const int u = tid + kThreads * it;
       const int key = u / C::NCH, c = u % C::NCH;
       const int j = j0 + key;
-      kpre[it] = j < lk ? ldg16_cached(kp + (int64_t)j * p.ks[2] + c * C::VEC)
-                          : u32x4{0, 0, 0, 0};
+      kpre[it] = j < lk && c * C::VEC < p.Dqk ? ldg16_cached(kp + (int64_t)j * p.ks[2] + c * C::VEC)
+                                              : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int it = 0; it < C::V_IT; ++it) {
@@ -154,8 +155,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = j0 + 4 * kg + r;
-        vpre[it][r] = j < lk ? ldg16_cached(vp + (int64_t)j * p.vs[2] + c * C::VEC)
-                               : u32x4{0, 0, 0, 0};
+        vpre[it][r] = j < lk && c * C::VEC < p.Dv ? ldg16_cached(vp + (int64_t)j * p.vs[2] + c * C::VEC)
+                                                  : u32x4{0, 0, 0, 0};
       }
     }
   };
@@ -335,7 +336,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_f32_kernel(AttnParams p) 
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rho = 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
-        orow[vt_row_to_d<C::NCH, C::VEC>(rho)] = T::from_f32(acc[mb][r] * scale_o);
+        const int d = vt_row_to_d<C::NCH, C::VEC>(rho);
+        if (d < p.Dv) orow[d] = T::from_f32(acc[mb][r] * scale_o);
       }
     }
     if (p.lse && g == 0) p.lse[((int64_t)b * p.Hq + hq) * p.Lq + my_i] = lse;
@@ -425,8 +427,8 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   const int iw = i0 + 32 * wave;
   const int my_i = iw + l32;
   // real query rows and keys of this batch; bottom-right causal offset
-  const int lq = batch_len(p.seqlens_q, b, p.Lq);
-  const int lk = batch_len(p.seqlens_k, b, p.Lk);
+  const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
+  const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
   const int coff = lk - lq;
 
   // exponent scale c = |scale| log2(e); a negative scale is moved into Q
@@ -436,11 +438,12 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   {
     const bool ok = my_i < lq;
     const S* row = (const S*)p.q + b * p.qs[0] + hq * p.qs[1] + (int64_t)(ok ? my_i : 0) * p.qs[2];
+    const int nqk = p.Dqk / 8;  // real 16-byte chunks of a q / k row; the rest is zero
 #pragma unroll
     for (int s = 0; s < C::NQ; ++s) {
-      u32x4 v = ldg16_cached(row + (2 * s + g) * 8);
+      u32x4 v = ldg16_cached(row + min(2 * s + g, nqk - 1) * 8);
       v ^= qflip;
-      qreg[s] = ok ? v : u32x4{0, 0, 0, 0};
+      qreg[s] = ok && 2 * s + g < nqk ? v : u32x4{0, 0, 0, 0};
     }
   }
 
@@ -467,6 +470,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // swizzles repeat every 16 rows: one per-lane offset plus a uniform step.
   const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
   const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
+  // A lane whose chunk lies past the real head dim loads nothing (kNoLoad).
   uint32_t koff[C::KVAR], voff;
   {
     const int pos = wave * 64 + lane;  // 16-byte slot of line 0
@@ -474,28 +478,32 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
 #pragma unroll
     for (int k = 0; k < C::KVAR; ++k) {
       const int rk = row + k * C::STEP_ROWS;  // a line KVAR steps further repeats it
-      koff[k] = (uint32_t)(row * p.ks[2] * 2 + (pch ^ swz_k<C::NCH>(rk)) * 16);
+      const int lch = pch ^ swz_k<C::NCH>(rk);
+      koff[k] = lch * 8 < p.Dqk ? (uint32_t)(row * p.ks[2] * 2 + lch * 16) : kNoLoad;
     }
-    voff = (uint32_t)(row * p.vs[2] * 2 + (pch ^ swz_v<C::NCH>(row)) * 16);
+    const int lch = pch ^ swz_v<C::NCH>(row);
+    voff = lch * 8 < p.Dv ? (uint32_t)(row * p.vs[2] * 2 + lch * 16) : kNoLoad;
   }
   const uint32_t krow = (uint32_t)(p.ks[2] * 2), vrow = (uint32_t)(p.vs[2] * 2);
   const uint32_t kstep = C::STEP_ROWS * krow, vstep = C::STEP_ROWS * vrow;
-  // bytes of a tile that hold real keys (rows from lk on read as zero)
-  auto tile_bytes = [&](int j0, uint32_t rowb) -> uint32_t {
-    const int rows = lk - j0;
-    return rows >= C::BN ? 0xffffffffu : (uint32_t)(rows - 1) * rowb + C::RB;
+  // bytes of a tile that hold real keys: rows from lk on (and, since the row
+  // stride is at least the real row, everything past the last real row) read
+  // as zero
+  auto tile_bytes = [&](int j0, uint32_t rowb, uint32_t real_rb) -> uint32_t {
+    const int rows = min(lk - j0, C::BN);
+    return (uint32_t)(rows - 1) * rowb + real_rb;
   };
-  auto issue = [&](const S* base, int64_t rs, uint32_t rowb, const uint32_t* off, int noff, uint32_t step,
-                   uint8_t* st, int t) {
+  auto issue = [&](const S* base, int64_t rs, uint32_t rowb, uint32_t real_rb, const uint32_t* off, int noff,
+                   uint32_t step, uint8_t* st, int t) {
     const int j0 = t * C::BN;
     const S* tb = base + (int64_t)j0 * rs;
-    const uint32_t nb = tile_bytes(j0, rowb);
+    const uint32_t nb = tile_bytes(j0, rowb, real_rb);
     const uint32_t la = lds_addr(st) + wave * 1024;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) dma16(tb, nb, la + NW * i * 1024, off[i % noff], i * step);
   };
-  auto issue_k = [&](int t, uint8_t* st) { issue(kbase, p.ks[2], krow, koff, C::KVAR, kstep, st, t); };
-  auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, &voff, 1, vstep, st, t); };
+  auto issue_k = [&](int t, uint8_t* st) { issue(kbase, p.ks[2], krow, 2 * p.Dqk, koff, C::KVAR, kstep, st, t); };
+  auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, 2 * p.Dv, &voff, 1, vstep, st, t); };
 
   // ---- per-lane LDS read offsets
   const uint32_t k_lane = l32 * C::RB;                 // + (32 kb) rows
@@ -809,7 +817,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
         // rows 8*q4 + 4g + (0..3) of block mb: four consecutive head-dim elements
         const u32x2 w = {cvt_pk(T{}, acc[mb][4 * q4] * scale_o, acc[mb][4 * q4 + 1] * scale_o),
                          cvt_pk(T{}, acc[mb][4 * q4 + 2] * scale_o, acc[mb][4 * q4 + 3] * scale_o)};
-        *(u32x2*)(orow + 32 * mb + 8 * q4 + 4 * g) = w;
+        if (32 * mb + 8 * q4 + 4 * g < p.Dv) *(u32x2*)(orow + 32 * mb + 8 * q4 + 4 * g) = w;
       }
     if (p.lse && g == 0) p.lse[((int64_t)b * p.Hq + hq) * p.Lq + my_i] = lse;
   }

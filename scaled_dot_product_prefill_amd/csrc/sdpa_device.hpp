@@ -162,6 +162,12 @@ __device__ inline int batch_len(const int32_t* lens, int b, int L) {
   return lens ? min(max(lens[b], 0), L) : L;
 }
 
+// Per-lane offset of a direct load that must read nothing (a chunk past the
+// real head dim): 1 GiB, above every tile's byte count (at most 64 rows of
+// 8 MiB), so the range check returns zero; with a tile's scalar offset added
+// it stays below 2^31.
+constexpr uint32_t kNoLoad = 0x40000000u;
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
@@ -186,12 +192,20 @@ __device__ inline void buf_load16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint3
 // The descriptor is built by hand (base, stride 0, num_records, the same
 // format word as make_rsrc); M0 holds the wave-uniform LDS destination, set
 // at least one wait state before the load.
+// base, bytes, soff and lds_addr are wave-uniform; they are pinned to scalar
+// registers (readfirstlane) so the "s" operands never see a vector register.
+// A vector instruction that writes a scalar register needs five wait states
+// before a buffer instruction reads it, and the compiler does not see inside
+// the asm, so it opens with s_nop 4 (which also covers the M0 write).
 __device__ inline void dma16(const void* base, uint32_t bytes, uint32_t lds_addr, uint32_t voff,
                              uint32_t soff) {
   const uint64_t a = (uint64_t)base;
-  const u32x4 rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+  const u32x4 rsrc = {(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a),
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+                      (uint32_t)__builtin_amdgcn_readfirstlane(bytes), 0x00020000u};
+  soff = (uint32_t)__builtin_amdgcn_readfirstlane(soff);
   asm volatile(
-      "s_nop 0\n\t"
+      "s_nop 4\n\t"
       "buffer_load_dwordx4 %0, %1, %2 offen lds"
       :
       : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr));

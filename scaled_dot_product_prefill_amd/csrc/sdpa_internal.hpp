@@ -20,7 +20,8 @@ struct AttnParams {
   int mask_bool;
   const float* sinks;
   float* lse;
-  int B, Hq, Hkv, Lq, Lk, D;
+  int B, Hq, Hkv, Lq, Lk, D;  // D: the kernel's head dim (the real dims rounded up)
+  int Dqk, Dv;                  // real head dims of q / k and of v / o (multiples of 8)
   int group;         // Hq / Hkv
   int causal;        // bottom-right causal masking (decode; prefill has it as a template flag)
   const int32_t* seqlens_q;  // optional [B] real query rows per batch

@@ -55,7 +55,7 @@ int main(void) {
   printf("sizeof %zu\n", sizeof(sdpa_args));
   F(B) F(Hq) F(Hkv) F(Lq) F(Lk) F(D) F(dtype) F(causal) F(scale) F(mask_kind)
   F(q) F(q_stride) F(k) F(k_stride) F(v) F(v_stride) F(o) F(o_stride)
-  F(mask) F(mask_stride) F(sinks) F(lse) F(seqlens_q) F(seqlens_k)
+  F(mask) F(mask_stride) F(sinks) F(lse) F(seqlens_q) F(seqlens_k) F(Dv)
   return 0;
 }
 """
@@ -114,7 +114,14 @@ def test_prefill_validation(lib):
     assert _prefill(lib, q=None) == S.ERR_NULL
     assert _prefill(lib, Lq=0) == S.ERR_SHAPE
     assert _prefill(lib, Hq=7) == S.ERR_SHAPE                 # not a multiple of Hkv
-    assert _prefill(lib, D=96) == S.ERR_UNSUPPORTED
+    assert _prefill(lib, D=96) == S.OK                          # runs in the D = 128 kernel
+    assert _prefill(lib, D=100) == S.ERR_UNSUPPORTED            # not a multiple of 8
+    assert _prefill(lib, Dv=64) == S.OK
+    assert _prefill(lib, Dv=-8) == S.ERR_SHAPE
+    assert _prefill(lib, D=64, Dv=136) == S.ERR_ARG             # o rows (stride 128) overlap
+    assert _prefill(lib, dtype=sdpa.F32, D=136, q_stride=(8 * 64 * 136, 64 * 136, 136),
+                    k_stride=(2 * 64 * 136, 64 * 136, 136), v_stride=(2 * 64 * 136, 64 * 136, 136),
+                    o_stride=(8 * 64 * 136, 64 * 136, 136)) == S.ERR_UNSUPPORTED
     assert _prefill(lib, dtype=7) == S.ERR_UNSUPPORTED
     assert _prefill(lib, q=(1 << 40) + 8) == S.ERR_ALIGN
     assert _prefill(lib, k_stride=(2 * 64 * 128, 64 * 128, 100)) == S.ERR_ALIGN
@@ -140,14 +147,15 @@ def test_prefill_validation(lib):
 
     msg = lib.sdpa_last_error()
     assert msg == b""
-    _prefill(lib, D=96)
-    assert b"D in {64, 128}" in lib.sdpa_last_error()
+    _prefill(lib, D=100)
+    assert b"multiples of 8" in lib.sdpa_last_error()
 
 
 def test_decode_validation(lib):
     assert _decode(lib) == S.OK
     assert _decode(lib, Lq=17) == S.ERR_UNSUPPORTED           # multi-query decode: Lq <= 16
-    assert _decode(lib, D=96) == S.ERR_UNSUPPORTED
+    assert _decode(lib, D=96) == S.OK
+    assert _decode(lib, D=100) == S.ERR_UNSUPPORTED
     assert _decode(lib, num_splits=-1) == S.ERR_ARG
     assert _decode(lib, num_splits=65) == S.ERR_ARG           # more splits than keys
     assert _decode(lib, num_splits=4, ws=None) == S.ERR_WORKSPACE
@@ -257,6 +265,7 @@ def test_backward_validation(lib):
     assert _bwd(lib) == S.OK
     assert _bwd(lib, dtype=sdpa.F32) == S.ERR_UNSUPPORTED
     assert _bwd(lib, D=96) == S.ERR_UNSUPPORTED
+    assert _bwd(lib, Dv=64) == S.ERR_UNSUPPORTED
     assert _bwd(lib, lse=None) == S.ERR_NULL
     assert _bwd(lib, gkw={"dq": None}) == S.ERR_NULL
     assert _bwd(lib, gkw={"dk": (1 << 41) + 8}) == S.ERR_ALIGN

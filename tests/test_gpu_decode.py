@@ -116,9 +116,9 @@ def test_decode_errors():
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.decode(x["q"], x["k"], x["v"])                # Lq = 17 > 16
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
-    x = to_dev(random_case(3401, 1, 4, 2, 1, 64, 96, "fp16"))
+    x = to_dev(random_case(3401, 1, 4, 2, 1, 64, 520, "fp16"))
     with pytest.raises(sdpa.SdpaError) as e:
-        sdpa.decode(x["q"], x["k"], x["v"])                # D = 96
+        sdpa.decode(x["q"], x["k"], x["v"])                # D = 520 > 512
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
 
 
@@ -192,3 +192,18 @@ def test_bool_mask(dtype, num_splits):
     d = to_dev(x)
     out, l = _decode(d, 1 / math.sqrt(D), num_splits)
     compare_full(out, l, x, 1 / math.sqrt(D), dtype, f"decode bool mask splits={num_splits}")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("dims", [(8, 8), (80, 80), (96, 64), (192, 128), (320, 320), (512, 448)],
+                         ids=lambda d: f"{d[0]}x{d[1]}")
+def test_head_dims(dtype, dims):
+    """Head dims that are multiples of 8 (D_v may differ from D_qk), single
+    pass and split-K."""
+    D, Dv = dims
+    x = random_case(2600 + D + Dv, 2, 16, 4, 1, 1500, D, dtype, Dv=Dv, sinks=True)
+    d = to_dev(x)
+    for ns in (0, 1):
+        out, l = _decode(d, 1 / math.sqrt(D), ns)
+        assert out.shape[-1] == Dv
+        compare_full(out, l, x, 1 / math.sqrt(D), dtype, f"decode head dims {D}x{Dv} splits={ns}")

@@ -182,11 +182,11 @@ def test_gqa_equals_repeated_kv():
 
 
 def test_rejects_unsupported():
-    x = to_dev(random_case(2008, 1, 2, 2, 8, 8, 96, "fp16"))
+    x = to_dev(random_case(2008, 1, 2, 2, 8, 8, 264, "fp16"))   # D = 264 > 256
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.prefill(x["q"], x["k"], x["v"])
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
-    x = to_dev(random_case(2009, 1, 2, 2, 8, 8, 256, "fp32"))   # D = 256 is 16-bit only
+    x = to_dev(random_case(2009, 1, 2, 2, 8, 8, 136, "fp32"))   # fp32 runs head dims up to 128
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.prefill(x["q"], x["k"], x["v"])
     assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
@@ -205,3 +205,22 @@ def test_bool_mask(dtype, causal):
     x["mask"] = torch.from_numpy(keep)
     out, l, sc = _run(x, dtype, causal=causal)
     compare_full(out, l, x, sc, dtype, f"bool mask {dtype} causal={causal}", causal=causal)
+
+
+# (D, Dv): head dims that are multiples of 8, run in the next kernel size up
+HEAD_DIMS = [(8, 8), (40, 40), (80, 80), (96, 96), (112, 64), (64, 120), (128, 96)]
+HEAD_DIMS_16 = [(160, 160), (192, 128), (256, 200)]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
+@pytest.mark.parametrize("dims", HEAD_DIMS + HEAD_DIMS_16, ids=lambda d: f"{d[0]}x{d[1]}")
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dims(dtype, dims, causal):
+    D, Dv = dims
+    if dtype == "fp32" and max(D, Dv) > 128:
+        pytest.skip("fp32 prefill runs head dims up to 128")
+    say(f"prefill head dims {dtype} D={D} Dv={Dv} causal={causal}")
+    x = random_case(2500 + D + Dv, 2, 4, 2, 150, 211, D, dtype, Dv=Dv, sinks=causal, sink_scale=2.0)
+    out, l, sc = _run(x, dtype, causal=causal)
+    assert out.shape[-1] == Dv
+    compare_full(out, l, x, sc, dtype, f"head dims {D}x{Dv}", causal=causal)

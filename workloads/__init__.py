@@ -188,15 +188,16 @@ def make_inputs(w: Workload, device="cpu") -> Dict[str, Optional[torch.Tensor]]:
 def random_case(seed: int, B: int, Hq: int, Hkv: int, Lq: int, Lk: int, D: int,
                 dtype: str = "fp32", *, mask: bool = False, sinks: bool = False,
                 sink_scale: float = 1.0, mask_neg_inf_frac: float = 0.0,
-                mask_shape: Tuple[int, int, int, int] | None = None
+                mask_shape: Tuple[int, int, int, int] | None = None, Dv: Optional[int] = None
                 ) -> Dict[str, Optional[torch.Tensor]]:
-    """Small seeded case for tests: N(0,1) q/k/v, optional N(0,1) additive mask
-    (a fraction of entries set to -inf) and optional sinks."""
+    """Small seeded case for tests: N(0,1) q/k/v (v with head dim Dv when
+    given), optional N(0,1) additive mask (a fraction of entries set to -inf)
+    and optional sinks."""
     rng = np.random.default_rng([1, seed])
     dt = DTYPES[dtype]
     q = _round_to(rng.standard_normal((B, Hq, Lq, D), dtype=np.float32), dt)
     k = _round_to(rng.standard_normal((B, Hkv, Lk, D), dtype=np.float32), dt)
-    v = _round_to(rng.standard_normal((B, Hkv, Lk, D), dtype=np.float32), dt)
+    v = _round_to(rng.standard_normal((B, Hkv, Lk, Dv or D), dtype=np.float32), dt)
     m = None
     if mask:
         shp = mask_shape or (B, Hq, Lq, Lk)
