@@ -431,8 +431,18 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
   const int coff = lk - lq;
 
-  // exponent scale c = |scale| log2(e); a negative scale is moved into Q
+  // exponent scale c = |scale| log2(e); a negative scale is moved into Q.
+  // fp16 with c <= 1: Q is multiplied by c once (it cannot overflow; each
+  // element takes one more rounding, 2^-11 relative), so the matrix cores
+  // deliver c S itself and the steady loop, which also starts its score
+  // accumulators at -m, feeds the exponential without any per-score
+  // arithmetic.  (bf16 would round c Q to 8 bits, which shows in rows that
+  // average few keys, so bf16 keeps one multiply-add per score.)  cs is the
+  // factor the scores still owe.
+  constexpr bool kRel = std::is_same<T, TF16>::value;
   const float c = fabsf(p.scale_log2);
+  const bool pre = kRel && c <= 1.f;
+  const float cs = pre ? 1.f : c;
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   u32x4 qreg[C::NQ];
   {
@@ -443,6 +453,13 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     for (int s = 0; s < C::NQ; ++s) {
       u32x4 v = ldg16_cached(row + min(2 * s + g, nqk - 1) * 8);
       v ^= qflip;
+      if (pre) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w = v[e];
+          v[e] = cvt_pk(T{}, T::to_f32((uint16_t)(w & 0xffffu)) * c, T::to_f32((uint16_t)(w >> 16)) * c);
+        }
+      }
       qreg[s] = ok && 2 * s + g < nqk ? v : u32x4{0, 0, 0, 0};
     }
   }
@@ -540,7 +557,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       for (int kb = 0; kb < C::NKB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-      mx = max_xor32(mx) * c;
+      mx = max_xor32(mx) * cs;
     } else {
       const int j0 = t * C::BN;
       const int ii = my_i < lq ? my_i : lq - 1;
@@ -550,7 +567,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          float x = sc[kb][r] * c;
+          float x = sc[kb][r] * cs;
           if (MASK) {
             const int jj = j < lk ? j : lk - 1;
             x += kLog2e * mask_val(p.mask, p.mask_bool,
@@ -576,7 +593,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       m_run = m_new;
     }
   };
-  // P = exp2(S c - m) (interior) or exp2(S - m) (edge, already scaled), packed
+  // P = exp2(S cs - m) (interior) or exp2(S - m) (edge, already scaled), packed
   // as the B operands of P.V: k-step u of block kb <-> accumulator rows 8u..8u+7.
   // Without the split the row sum adds the packed (rounded) probabilities,
   // the values P.V multiplies.
@@ -589,7 +606,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     for (int kb = 0; kb < C::NKB; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        sc[kb][r] = EDGE ? fast_exp2(sc[kb][r] - m_use) : fast_exp2(fmaf(sc[kb][r], c, -m_use));
+        sc[kb][r] = EDGE ? fast_exp2(sc[kb][r] - m_use) : fast_exp2(fmaf(sc[kb][r], cs, -m_use));
 #pragma unroll
       for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -628,16 +645,21 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       }
   };
 
-  // One steady-state tile as a fixed sequence of slots.  Slot i holds
+  // One steady-state tile as a fixed sequence of slots.  fp16 holds scores
+  // relative to the reference max: S'(t) = c S(t) - m, the accumulators of
+  // S(t+1) starting at -m (mneg), so P(t) = exp2(S'(t)); bf16 holds the raw
+  // S(t) and P(t) = exp2(c S(t) - m).  Slot i holds
   //   - the LDS operand read of matrix-core op i + W (W ops of lead time),
   //   - matrix-core op i: ops [0, NQK) form S(t+1) = K(t+1).Q^T (kb-major),
-  //     the rest O^T += V(t)^T.P(t)^T in (kb, u) groups of NMB (+1 row-sum op),
+  //     the rest O^T += V(t)^T.P(t)^T in (kb, u) groups of NMB,
   //   - its share of the VALU work: "EC" items (two probabilities of P(t),
   //     exponentials, packing, row sum) before the P.V ops that consume them,
-  //     then "X" items (row max of S(t+1), two scores each) once S(t+1) exists.
+  //     then "X" items (row max of S(t+1), two scores each) once it exists.
+  // Returns the row max of c S(t+1): relative to m for fp16, absolute for bf16.
   // A full scheduling fence closes every slot.  A wave whose matrix ops are
   // spaced by a few VALU ops lets both units run at once; a run of
   // back-to-back matrix ops stalls the VALU of the other wave on the SIMD.
+  f32x16 mneg;
   auto steady_slots = [&](const uint8_t* Kst, const uint8_t* Vst, f32x16* cur, f32x16* nxt) -> float {
     constexpr int NQK = C::NKB * C::NQ;
     constexpr int GOPS = C::NMB;
@@ -669,26 +691,29 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     auto do_op = [&](int i) {
       if (i < NQK) {
         const int kb = i / C::NQ, s = i % C::NQ;
-        nxt[kb] = mma32(T{}, opnd[i], qreg[s], s == 0 ? f32x16{} : nxt[kb]);
+        nxt[kb] = mma32(T{}, opnd[i], qreg[s], s == 0 ? (kRel ? mneg : f32x16{}) : nxt[kb]);
       } else {
         const int j = i - NQK, grp = j / GOPS, w = j % GOPS;
         const int kb = grp / 2, u = grp % 2;
         acc[w] = mma32(T{}, opnd[i], hi[kb][u], acc[w]);
       }
     };
-    // EC item = two probabilities: (a) scaled score minus max, (b) exp2,
-    // (c) pack + row sum.  The stages of one item run in consecutive slots
-    // (a two slots ahead of c), so each slot mixes independent work of three
-    // items instead of one dependent chain.
+    // EC item = two probabilities: (a) bf16 only: scaled score minus max,
+    // (b) exp2, (c) pack + row sum.  The stages of one item run in consecutive
+    // slots (a two slots ahead of c), so each slot mixes independent work of
+    // several items instead of one dependent chain.
     float xs[NEC][2], ps[NEC][2];
     auto ec_a = [&](int it) {
-      const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
-      xs[it][0] = fmaf(cur[kb][8 * u + 2 * e], c, -m_use);
-      xs[it][1] = fmaf(cur[kb][8 * u + 2 * e + 1], c, -m_use);
+      if constexpr (!kRel) {
+        const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
+        xs[it][0] = fmaf(cur[kb][8 * u + 2 * e], c, -m_use);
+        xs[it][1] = fmaf(cur[kb][8 * u + 2 * e + 1], c, -m_use);
+      }
     };
     auto ec_b = [&](int it) {
-      ps[it][0] = fast_exp2(xs[it][0]);
-      ps[it][1] = fast_exp2(xs[it][1]);
+      const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
+      ps[it][0] = fast_exp2(kRel ? cur[kb][8 * u + 2 * e] : xs[it][0]);
+      ps[it][1] = fast_exp2(kRel ? cur[kb][8 * u + 2 * e + 1] : xs[it][1]);
     };
     auto ec_c = [&](int it) {
       const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
@@ -732,7 +757,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       __builtin_amdgcn_sched_barrier(0);
     }
     const float mx = fmaxf(mx2[0], mx2[1]);
-    return max_xor32(mx) * c;
+    return kRel ? max_xor32(mx) : max_xor32(mx) * c;
   };
 
   // ---- pipeline.  Tile t lives in stage t & 1 of both rings.  Iteration t
@@ -757,7 +782,21 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     lds_barrier();
     issue_v(t + 1, Vring + (PAR ^ 1) * C::TILE);
     issue_k(t + 2, Kring + PAR * C::TILE);
-    update_max(steady_slots(Kring + (PAR ^ 1) * C::TILE, Vring + PAR * C::TILE, cur, nxt));
+    const float mx = steady_slots(Kring + (PAR ^ 1) * C::TILE, Vring + PAR * C::TILE, cur, nxt);
+    if constexpr (!kRel) {
+      update_max(mx);
+    } else if (__any(mx > kRescaleSlack)) {
+      // update_max in relative units; S'(t+1) follows the moved max
+      const float d = fmaxf(mx, 0.f);
+      const float corr = fast_exp2(-d);
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+      l_run *= corr;
+      m_run += d;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) nxt[kb] -= d;
+      mneg = -m_run;
+    }
   };
   auto general = [&](int t, auto edge_tag) {
     const int par = t & 1;
@@ -776,7 +815,13 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   };
   int t = 0;
   if constexpr (D <= 128) {
-    const int n_steady = split_p ? 0 : max(0, min(n_int - 1, ntiles - 2));
+    const int n_steady = split_p || (kRel && !pre) ? 0 : max(0, min(n_int - 1, ntiles - 2));
+    if (kRel && n_steady > 0) {
+      // tile 0 was interior, so m_run is finite
+      mneg = -m_run;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += mneg;
+    }
     for (; t + 1 < n_steady; t += 2) {
       steady(t, std::integral_constant<int, 0>{}, sa, sb);
       steady(t + 1, std::integral_constant<int, 1>{}, sb, sa);
@@ -786,6 +831,10 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
 #pragma unroll
       for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
       ++t;
+    }
+    if (kRel && n_steady > 0) {
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += m_run;
     }
   }
   for (; t < n_int; ++t) general(t, std::false_type{});

@@ -150,6 +150,42 @@ def test_dominant_logit_and_identical_keys(dtype):
     compare_full(out, l, x, sc, dtype, "dominant/identical")
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128])
+def test_running_max_moves(dtype, D):
+    # a score offset that grows along the keys (a shared direction in q and
+    # k) moves the reference max past the rescale slack again and again
+    # inside the steady loop, while tens of keys still share each row
+    x = random_case(2010 + D, 1, 2, 2, 256, 1024, D, dtype)
+    q, k = x["q"].float(), x["k"].float()
+    q[..., 0] = 8.0
+    k[..., 0] = torch.linspace(0.0, 25.0, 1024)
+    x["q"], x["k"] = q.to(x["v"].dtype), k.to(x["v"].dtype)
+    out, l, sc = _run(x, dtype)
+    compare_full(out, l, x, sc, dtype, f"moving max {dtype} D{D}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp16_scale_above_one_log2_unit(causal):
+    # |scale| log2(e) > 1: Q is not pre-multiplied and every tile takes the
+    # general path
+    x = random_case(2012, 1, 2, 2, 200, 700, 64, "fp16")
+    x["q"] = (x["q"].float() * 0.25).half()
+    out, l, sc = _run(x, "fp16", causal=causal, scale=1.5)
+    compare_full(out, l, x, sc, "fp16", f"scale 1.5 causal={causal}", causal=causal)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("tail", [1, 31, 33, 64, 65, 96, 97])
+def test_tail_workgroup_waves(dtype, tail):
+    # the last 128-row workgroup of each head holds `tail` real rows, so 0 to 3
+    # of its 32-row waves hold none (they still stream K / V with the others)
+    Lq = 256 + tail
+    x = random_case(2100 + tail, 2, 2, 1, Lq, 300, 64, dtype, sinks=True)
+    out, l, sc = _run(x, dtype, causal=tail % 2 == 1)
+    compare_full(out, l, x, sc, dtype, f"tail {tail}", causal=tail % 2 == 1)
+
+
 def test_non_contiguous_layouts():
     # q, k, v, o stored as [B, L, H, D] and viewed as [B, H, L, D]
     B, H, L, D = 2, 4, 150, 128
