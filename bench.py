@@ -22,7 +22,8 @@ on a bounded sample of the same workload on the host cores.
 Other workloads (for profiling): --workload dit_fp16|dit_fp32|causal_bf16|
 long_decode_bf16|<gqa8 decode name>|mq4_gqa8_decode_b1_lk32768_fp16 (multi-query decode)|
 kvcache_ragged_decode_bf16 (KV cache with per-batch fill levels; GB/s over the filled part)|
-causal_bf16_bwd (gradients of the causal prefill; 10*D flops per visible pair).
+causal_bf16_bwd (gradients of the causal prefill; 10*D flops per visible pair)|
+causal_gqa8_d512_bf16 (prefill at head dim 512, GQA-8).
 """
 from __future__ import annotations
 

@@ -156,9 +156,12 @@ typedef struct sdpa_args {
 } sdpa_args;
 
 /* Prefill / full self-attention, any Lq >= 1, Lk >= 1.
- * Supported: kernel head dim 64 or 128 for F32, F16 and BF16; 256 for F16 and
- * BF16 (so any D, Dv that are multiples of 8 up to 128, or 256).
- * One kernel launch. */
+ * Supported: D, Dv multiples of 8 up to 512 (kernel head dim 64, 128, 256,
+ * 512), dtypes F32, F16, BF16.  Kernel head dim 64 or 128 (any dtype) and 256
+ * (F16, BF16) run on 128-row tiles; 512, and 256 in F32, run 16 columns
+ * (query rows x the query heads of a KV head) per workgroup, the kernel the
+ * decode path uses, in a single pass over the keys.
+ * One kernel launch; no workspace. */
 SDPA_API int sdpa_prefill(const sdpa_args *args, void *stream);
 
 /* Host-only validation of a prefill request (no GPU work, no HIP calls).

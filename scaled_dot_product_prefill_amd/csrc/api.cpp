@@ -162,25 +162,35 @@ int check_common(const sdpa_args* a) {
   return SDPA_OK;
 }
 
+// Decode: the Lq query rows times the G heads of a KV head are the columns of
+// 16-wide matrix tiles; each chunk of 16 columns is one workgroup per key split.
+int64_t decode_chunks(const sdpa_args* a) { return (a->Lq * (a->Hq / a->Hkv) + 15) / 16; }
+
+// Prefill head dims the 128-row prefill kernels do not hold (kernel head dim
+// 512, or above 128 in fp32: a 32-row wave's O accumulator alone would fill
+// the register file) run on the 16-column kernels of the decode path, one
+// pass over the keys per workgroup.
+bool prefill_narrow(const sdpa_args* a) {
+  const int kd = kernel_dim(a);
+  return kd == 512 || (a->dtype == SDPA_F32 && kd > 128);
+}
+
 int check_prefill(const sdpa_args* a) {
   int st = check_common(a);
   if (st != SDPA_OK) return st;
-  const int kd = kernel_dim(a);
-  if (kd == 0 || kd > (a->dtype == SDPA_F32 ? 128 : 256))
-    return fail(SDPA_ERR_UNSUPPORTED,
-                "prefill supports head dims up to 128 (fp32) or 256 (fp16/bf16), got D=%lld Dv=%lld",
+  if (kernel_dim(a) == 0)
+    return fail(SDPA_ERR_UNSUPPORTED, "prefill supports head dims up to 512, got D=%lld Dv=%lld",
                 (long long)a->D, (long long)dv_of(a));
-  const int64_t grid = ((a->Lq + 127) / 128) * a->B * a->Hq;
+  const int64_t grid = prefill_narrow(a) ? decode_chunks(a) * a->B * a->Hkv : ((a->Lq + 127) / 128) * a->B * a->Hq;
   if (grid > kMaxInt) return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
   return SDPA_OK;
 }
 
 // Decode: the Lq query rows times the G heads of a KV head are the columns of
 // 16-wide matrix tiles (multi-query decode, e.g. speculative or chunked
-// decoding); each chunk of 16 columns is one workgroup per key split.
+// decoding); each chunk of 16 columns is one workgroup per key split
+// (decode_chunks).
 constexpr int kMaxDecodeLq = 16;
-int64_t decode_chunks(const sdpa_args* a) { return (a->Lq * (a->Hq / a->Hkv) + 15) / 16; }
-
 struct SplitPlan {
   int nsplit = 1;
   int split_len = 0;
@@ -378,6 +388,12 @@ int sdpa_prefill(const sdpa_args* args, void* stream) {
   int st = sdpa::check_prefill(args);
   if (st != SDPA_OK) return st;
   sdpa::AttnParams p = sdpa::make_params(*args);
+  if (sdpa::prefill_narrow(args)) {
+    p.nsplit = 1;
+    p.split_len = (int)args->Lk;
+    p.nchunk = (int)sdpa::decode_chunks(args);
+    return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
+  }
   return sdpa::launch_status(sdpa::launch_prefill(p, args->dtype, args->causal != 0, (hipStream_t)stream));
 }
 

@@ -44,6 +44,7 @@ struct DecodeUnit {
   int hq, qi;     // its query head and query row (0 for padding columns)
   int lk;         // real keys of the batch
   int last_key;   // last visible key of that row (-1: none)
+  int key_end;    // one past the last key any real row of the workgroup sees
 };
 __device__ inline DecodeUnit decode_unit(const AttnParams& p, int n) {
   DecodeUnit u;
@@ -61,6 +62,11 @@ __device__ inline DecodeUnit decode_unit(const AttnParams& p, int n) {
   const int lq = batch_len(p.seqlens_q, u.b, p.Lq);
   u.lk = batch_len(p.seqlens_k, u.b, p.Lk);
   u.last_key = u.qi >= lq ? -1 : (p.causal ? u.lk - lq + u.qi : u.lk);
+  // the workgroup's rows run from (16 chunk) / G to (16 chunk + 15) / G; under
+  // bottom-right causal masking its last real row sees the most keys
+  const int qfirst = 16 * chunk / p.group;
+  const int qlast = min(min(16 * chunk + 15, p.Lq * p.group - 1) / p.group, lq - 1);
+  u.key_end = qfirst >= lq ? 0 : (p.causal ? max(0, u.lk - lq + qlast + 1) : u.lk);
   return u;
 }
 
@@ -128,7 +134,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
   const bool head_ok = u.ok;
 
   const int kbeg = split * p.split_len;
-  const int kend = min(u.lk, kbeg + p.split_len);
+  const int kend = min(u.key_end, kbeg + p.split_len);
   const int ntiles = kend > kbeg ? (kend - kbeg + C::TK - 1) / C::TK : 0;
 
   const S* kp = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
@@ -470,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   const bool head_ok = u.ok;
 
   const int kbeg = split * p.split_len;
-  const int kend = min(u.lk, kbeg + p.split_len);
+  const int kend = min(u.key_end, kbeg + p.split_len);
   const int ntiles = kend > kbeg ? (kend - kbeg + C::TK - 1) / C::TK : 0;
 
   const S* kp = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];

@@ -121,7 +121,10 @@ def test_prefill_validation(lib):
     assert _prefill(lib, D=64, Dv=136) == S.ERR_ARG             # o rows (stride 128) overlap
     assert _prefill(lib, dtype=sdpa.F32, D=136, q_stride=(8 * 64 * 136, 64 * 136, 136),
                     k_stride=(2 * 64 * 136, 64 * 136, 136), v_stride=(2 * 64 * 136, 64 * 136, 136),
-                    o_stride=(8 * 64 * 136, 64 * 136, 136)) == S.ERR_UNSUPPORTED
+                    o_stride=(8 * 64 * 136, 64 * 136, 136)) == S.OK   # 16-column kernel
+    assert _prefill(lib, D=520, q_stride=(8 * 64 * 520, 64 * 520, 520),
+                    k_stride=(2 * 64 * 520, 64 * 520, 520), v_stride=(2 * 64 * 520, 64 * 520, 520),
+                    o_stride=(8 * 64 * 520, 64 * 520, 520)) == S.ERR_UNSUPPORTED   # above 512
     assert _prefill(lib, dtype=7) == S.ERR_UNSUPPORTED
     assert _prefill(lib, q=(1 << 40) + 8) == S.ERR_ALIGN
     assert _prefill(lib, k_stride=(2 * 64 * 128, 64 * 128, 100)) == S.ERR_ALIGN

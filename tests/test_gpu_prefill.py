@@ -218,14 +218,11 @@ def test_gqa_equals_repeated_kv():
 
 
 def test_rejects_unsupported():
-    x = to_dev(random_case(2008, 1, 2, 2, 8, 8, 264, "fp16"))   # D = 264 > 256
-    with pytest.raises(sdpa.SdpaError) as e:
-        sdpa.prefill(x["q"], x["k"], x["v"])
-    assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
-    x = to_dev(random_case(2009, 1, 2, 2, 8, 8, 136, "fp32"))   # fp32 runs head dims up to 128
-    with pytest.raises(sdpa.SdpaError) as e:
-        sdpa.prefill(x["q"], x["k"], x["v"])
-    assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
+    for dt in ("fp16", "fp32"):
+        x = to_dev(random_case(2008, 1, 2, 2, 8, 8, 520, dt))   # D = 520 > 512
+        with pytest.raises(sdpa.SdpaError) as e:
+            sdpa.prefill(x["q"], x["k"], x["v"])
+        assert e.value.status == sdpa.Status.ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
@@ -246,17 +243,27 @@ def test_bool_mask(dtype, causal):
 # (D, Dv): head dims that are multiples of 8, run in the next kernel size up
 HEAD_DIMS = [(8, 8), (40, 40), (80, 80), (96, 96), (112, 64), (64, 120), (128, 96)]
 HEAD_DIMS_16 = [(160, 160), (192, 128), (256, 200)]
+# kernel head dim 512 (and 256 in fp32): 16 columns per workgroup
+HEAD_DIMS_WIDE = [(512, 512), (264, 512), (512, 320), (136, 136)]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
-@pytest.mark.parametrize("dims", HEAD_DIMS + HEAD_DIMS_16, ids=lambda d: f"{d[0]}x{d[1]}")
+@pytest.mark.parametrize("dims", HEAD_DIMS + HEAD_DIMS_16 + HEAD_DIMS_WIDE, ids=lambda d: f"{d[0]}x{d[1]}")
 @pytest.mark.parametrize("causal", [False, True])
 def test_head_dims(dtype, dims, causal):
     D, Dv = dims
-    if dtype == "fp32" and max(D, Dv) > 128:
-        pytest.skip("fp32 prefill runs head dims up to 128")
     say(f"prefill head dims {dtype} D={D} Dv={Dv} causal={causal}")
     x = random_case(2500 + D + Dv, 2, 4, 2, 150, 211, D, dtype, Dv=Dv, sinks=causal, sink_scale=2.0)
     out, l, sc = _run(x, dtype, causal=causal)
     assert out.shape[-1] == Dv
     compare_full(out, l, x, sc, dtype, f"head dims {D}x{Dv}", causal=causal)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16", "fp32"])
+def test_d512_gqa_causal_sampled(dtype):
+    """Head dim 512 with GQA-8 (the decode workload's heads) over 2048 causal
+    rows: 16 columns = 2 query rows x 8 heads per workgroup; LSE and sinks."""
+    w = workloads.CAUSAL.with_(name=f"causal_{dtype}_d512", B=1, Hq=16, Hkv=2, Lq=2048, Lk=2048, D=512,
+                               dtype=dtype, sinks=True)
+    _full_size(w, heads=[(0, 0), (0, 7), (0, 8), (0, 15)], rows=[0, 1, 2, 15, 16, 1000, 2046, 2047])
+

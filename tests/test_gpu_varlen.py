@@ -37,11 +37,9 @@ PREFILL_CASES = [
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
-@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("D", [64, 128, 256, 512])
 @pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
 def test_prefill_seqlens(dtype, D, case):
-    if dtype == "fp32" and D == 256:
-        pytest.skip("prefill D = 256 is 16-bit only")
     Hq, Hkv, Lq, Lk, sq, sk, causal, mask, sinks = PREFILL_CASES[case]
     say(f"prefill seqlens {dtype} D={D} case={PREFILL_CASES[case]}")
     x = random_case(4000 + 10 * case + D, 3, Hq, Hkv, Lq, Lk, D, dtype, mask=mask, sinks=sinks,

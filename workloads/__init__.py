@@ -126,9 +126,13 @@ KVCACHE_DECODE = Workload("kvcache_ragged_decode_bf16", 7, B=8, Hq=32, Hkv=8, Lq
 # Gradients of the causal prefill (next-row extension): same inputs, plus dO.
 CAUSAL_BWD = CAUSAL.with_(name="causal_bf16_bwd", grad=True)
 
+# Prefill at head dim 512 (next-row extension): the GQA-8 D512 heads of the
+# decode family over a 4096-token causal prompt.
+PREFILL_D512 = CAUSAL.with_(name="causal_gqa8_d512_bf16", Hq=32, Hkv=4, D=512)
+
 ALL: Dict[str, Workload] = {w.name: w for w in
                             [TINY, DIT_FP16, DIT_FP32, CAUSAL, LONG_DECODE, *GQA_DECODE, MQ_DECODE,
-                             KVCACHE_DECODE, CAUSAL_BWD]}
+                             KVCACHE_DECODE, CAUSAL_BWD, PREFILL_D512]}
 
 
 # ---- generators --------------------------------------------------------------
