@@ -690,21 +690,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   }
 }
 
-// Merge pass.  Workgroup (b, hq, 64-element slice of the head dim): the
-// reference max M and the total L are reduced over the splits by all 256
-// threads, then thread (split group sg, element quad dq) sums its splits'
-// weighted partial O for four head-dim elements and the 16 split groups are
-// combined in LDS.
+// Merge pass.  Workgroup (b, hq, 64-element slice of the head dim); thread
+// (split group sg, element quad dq) takes splits sg, sg + NSG, ...  A thread
+// fetches the (m_s, l_s, O~_s) of several splits at once (no load waits on a
+// reduction, so the partials cost one memory round trip) and folds them into
+// its own (m, l, O~) by the same rescaling as the online softmax; the NSG
+// split groups are then combined in LDS with the sink:
+//   M = max(max_g m_g, sink),  L = sum_g l_g 2^(m_g - M) + 2^(sink - M),
+//   O = sum_g O~_g 2^(m_g - M) / L.  Splits with m_s = -inf weigh 0.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeCols = 64;  // head-dim elements per workgroup
+constexpr int kMergeUnroll = 4; // splits a thread fetches together
 
 template <class T, int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   using S = typename T::storage;
   constexpr int NDQ = (D < kMergeCols ? D : kMergeCols) / 4;  // float4 columns per workgroup
   constexpr int NSG = kMergeThreads / NDQ;                      // split groups
-  __shared__ float red[kMergeThreads / 64];
   __shared__ f32x4 part[NSG][NDQ];
+  __shared__ float gm[NSG], gl[NSG];
   const int tid = threadIdx.x;
   const int nslice = D / (NDQ * 4);
   const int64_t bh = blockIdx.x / nslice;  // ((b * Hq + hq) * Lq + qi)
@@ -714,48 +718,58 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   const int b = (int)(bh / p.Lq / p.Hq);
   const float* pml = p.part_ml + bh * p.nsplit * 2;
   const float* po = p.part_o + bh * p.nsplit * D;
-  const float sk = p.sinks ? p.sinks[hq] * kLog2e : kNegInf;
-
-  // M = max(max_s m_s, sink)
-  float M = kNegInf;
-  for (int s = tid; s < p.nsplit; s += kMergeThreads) M = fmaxf(M, pml[2 * s]);
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  M = fmaxf(M, sk);
-  __syncthreads();
-  // L = sum_s l_s 2^(m_s - M) + 2^(sink - M); splits with m_s = -inf weigh 0
-  float L = 0.f;
-  if (M != kNegInf)
-    for (int s = tid; s < p.nsplit; s += kMergeThreads) {
-      const float ms = pml[2 * s];
-      if (ms != kNegInf) L += pml[2 * s + 1] * fast_exp2(ms - M);
-    }
-  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = L;
-  __syncthreads();
-  L = red[0] + red[1] + red[2] + red[3];
-  if (p.sinks && M != kNegInf) L += fast_exp2(sk - M);
-  const bool live = M != kNegInf && L > 0.f;
-
-  // weighted partial numerators
   const int dq = tid % NDQ, sg = tid / NDQ;
+
+  float m = kNegInf, l = 0.f;
   f32x4 o = f32x4{};
-  if (live)
-    for (int s = sg; s < p.nsplit; s += NSG) {
-      const float ms = pml[2 * s];
-      if (ms != kNegInf) o += fast_exp2(ms - M) * *(const f32x4*)(po + (int64_t)s * D + d0 + 4 * dq);
+  for (int s0 = sg; s0 < p.nsplit; s0 += kMergeUnroll * NSG) {
+    float ms[kMergeUnroll], ls[kMergeUnroll];
+    f32x4 os[kMergeUnroll];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int sp = s0 + u * NSG;
+      const bool in = sp < p.nsplit;
+      ms[u] = in ? pml[2 * sp] : kNegInf;
+      ls[u] = in ? pml[2 * sp + 1] : 0.f;
+      os[u] = in ? *(const f32x4*)(po + (int64_t)sp * D + d0 + 4 * dq) : f32x4{};
     }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      if (ms[u] == kNegInf) continue;
+      const float mn = fmaxf(m, ms[u]);
+      const float a = fast_exp2(m - mn), w = fast_exp2(ms[u] - mn);  // m = -inf: a = 0
+      l = l * a + ls[u] * w;
+      o = o * a + os[u] * w;
+      m = mn;
+    }
+  }
   part[sg][dq] = o;
+  if (dq == 0) {
+    gm[sg] = m;
+    gl[sg] = l;
+  }
   __syncthreads();
   if (sg == 0) {
-    for (int g = 1; g < NSG; ++g) o += part[g][dq];
+    const float sk = p.sinks ? p.sinks[hq] * kLog2e : kNegInf;
+    float M = sk;
+    for (int g = 0; g < NSG; ++g) M = fmaxf(M, gm[g]);
+    float L = 0.f;
+    f32x4 acc = f32x4{};
+    if (M != kNegInf) {
+      for (int g = 0; g < NSG; ++g) {
+        if (gm[g] == kNegInf) continue;
+        const float w = fast_exp2(gm[g] - M);
+        L += gl[g] * w;
+        acc += part[g][dq] * w;
+      }
+      if (p.sinks) L += fast_exp2(sk - M);
+    }
+    const bool live = M != kNegInf && L > 0.f;
     const float inv = live ? 1.f / L : 0.f;
     S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)qi * p.os[2] + d0 + 4 * dq;
     if (d0 + 4 * dq < p.Dv)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) orow[e] = T::from_f32(o[e] * inv);
+      for (int e = 0; e < 4; ++e) orow[e] = T::from_f32(acc[e] * inv);
     if (p.lse && blockIdx.x % nslice == 0 && dq == 0)
       p.lse[bh] = live ? (M + fast_log2(L)) * kLn2 : kNegInf;
   }
