@@ -46,15 +46,31 @@ struct DecodeUnit {
   int last_key;   // last visible key of that row (-1: none)
   int key_end;    // one past the last key any real row of the workgroup sees
 };
-__device__ inline DecodeUnit decode_unit(const AttnParams& p, int n) {
+// Workgroup columns: chunk holds columns [16 cpw chunk, 16 cpw (chunk + 1));
+// 16-column block w of them (w < cpw) belongs to wave w when cpw > 1.
+__device__ inline DecodeUnit decode_unit(const AttnParams& p, int n, int cpw = 1, int w = 0) {
   DecodeUnit u;
-  u.split = blockIdx.x % p.nsplit;
-  int r = blockIdx.x / p.nsplit;
-  const int chunk = r % p.nchunk;
-  r /= p.nchunk;
+  int chunk, r;
+  if (cpw == 1) {
+    // decode: (split, chunk, kv head, batch), split fastest
+    u.split = blockIdx.x % p.nsplit;
+    r = blockIdx.x / p.nsplit;
+    chunk = r % p.nchunk;
+    r /= p.nchunk;
+  } else {
+    // prefill, one split: (kv head, batch) fastest, so that the workgroups
+    // launched first are the heaviest chunks of every head under causal
+    // masking (later rows see more keys), and head h stays on XCD h % 8
+    // when B * Hkv is a multiple of 8
+    u.split = 0;
+    const int nbh = p.B * p.Hkv;
+    const int ci = blockIdx.x / nbh;
+    chunk = p.causal ? p.nchunk - 1 - ci : ci;
+    r = blockIdx.x % nbh;
+  }
   u.hk = r % p.Hkv;
   u.b = r / p.Hkv;
-  const int c = 16 * chunk + n;
+  const int c = 16 * (cpw * chunk + w) + n;
   u.ok = c < p.Lq * p.group;
   const int cc = u.ok ? c : 0;
   u.qi = cc / p.group;
@@ -62,10 +78,11 @@ __device__ inline DecodeUnit decode_unit(const AttnParams& p, int n) {
   const int lq = batch_len(p.seqlens_q, u.b, p.Lq);
   u.lk = batch_len(p.seqlens_k, u.b, p.Lk);
   u.last_key = u.qi >= lq ? -1 : (p.causal ? u.lk - lq + u.qi : u.lk);
-  // the workgroup's rows run from (16 chunk) / G to (16 chunk + 15) / G; under
-  // bottom-right causal masking its last real row sees the most keys
-  const int qfirst = 16 * chunk / p.group;
-  const int qlast = min(min(16 * chunk + 15, p.Lq * p.group - 1) / p.group, lq - 1);
+  // the workgroup's rows run from (16 cpw chunk) / G to (16 cpw chunk + 16 cpw
+  // - 1) / G; under bottom-right causal masking its last real row sees the
+  // most keys
+  const int qfirst = 16 * cpw * chunk / p.group;
+  const int qlast = min(min(16 * cpw * (chunk + 1) - 1, p.Lq * p.group - 1) / p.group, lq - 1);
   u.key_end = qfirst >= lq ? 0 : (p.causal ? max(0, u.lk - lq + qlast + 1) : u.lk);
   return u;
 }
@@ -438,11 +455,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
 #ifndef SDPA_DECODE16_STAGES_LARGE
 #define SDPA_DECODE16_STAGES_LARGE 2  // ring stages at D >= 256 (32 KiB stages)
 #endif
-template <int D>
+template <int D, int TKO = 0>
 struct Dec16 {
   static constexpr int RB = D * 2;                 // row bytes
   static constexpr int NCH = D / 8;                // 16-byte chunks per row
-  static constexpr int TK = D >= 512 ? 16 : (D >= 256 ? 32 : SDPA_DECODE16_TK128 * 128 / D);
+  static constexpr int TK = TKO ? TKO : (D >= 512 ? 16 : (D >= 256 ? 32 : SDPA_DECODE16_TK128 * 128 / D));
   static constexpr int TILE = TK * RB;             // bytes of the K (or V) tile
   static constexpr int NST = D >= 256 ? SDPA_DECODE16_STAGES_LARGE : SDPA_DECODE16_STAGES;
   static constexpr int STAGE = 2 * TILE;
@@ -459,10 +476,18 @@ struct Dec16 {
 template <int NCH>
 __device__ constexpr int chunk_swz(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & (NCH - 1)); }
 
-template <class T, int D, bool MASK, bool SPLIT>
+// CPW = 1 (decode): the four waves share 16 columns; each computes their
+// scores and owns a quarter of the O^T rows.  CPW = 4 (prefill at head dim
+// 512): each wave owns 16 columns of its own and all O^T rows, so the K / V
+// tiles in LDS serve 64 columns.
+// The CPW = 4 form takes 32-key tiles (128 KiB of LDS at D = 512) so that
+// P.V runs as 16x16x32 products, 32 keys per step, at the full matrix rate.
+template <class T, int D, bool MASK, bool SPLIT, int CPW = 1>
 __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
-  using C = Dec16<D>;
+  using C = Dec16<D, (CPW > 1 ? 32 : 0)>;
   using S = uint16_t;
+  static_assert(CPW == 1 || (CPW == kWaves && !SPLIT), "column blocks");
+  constexpr int NOB = CPW > 1 ? D / 16 : C::NOB;  // O^T row blocks per wave
   __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NST * C::STAGE];
 
   const int tid = threadIdx.x;
@@ -470,8 +495,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g4 = lane >> 4;
+  const int ob0 = CPW > 1 ? 0 : wave * NOB;  // first O^T row block of this wave
 
-  const DecodeUnit u = decode_unit(p, n);
+  const DecodeUnit u = decode_unit(p, n, CPW, CPW > 1 ? wave : 0);
   const int split = u.split, hk = u.hk, b = u.b, hq = u.hq, qi = u.qi;
   const bool head_ok = u.ok;
 
@@ -534,10 +560,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
   const int swv = chunk_swz<C::NCH>(vrow);
   const uint32_t vlane = vrow * C::RB + (n & 1) * 8;
 
-  f32x4 acc[C::NOB];
+  f32x4 acc[NOB];
 #pragma unroll
-  for (int i = 0; i < C::NOB; ++i) acc[i] = f32x4{};
+  for (int i = 0; i < NOB; ++i) acc[i] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
+  // bf16 P goes in as hi + lo: always in decode (the matrix cores have ample
+  // headroom in this bandwidth-bound kernel); in prefill where rows may see
+  // few keys (at most 256, or any row under a mask), as in the prefill kernel
+  const bool split_p = std::is_same<T, TBF16>::value && (CPW == 1 || MASK || kend - kbeg <= 256);
 
   // mask values for tile t, loaded one tile ahead
   auto load_mask = [&](int t, f32x4* mk) {
@@ -613,10 +643,47 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
       const float corr = m_new > m_run ? fast_exp2(m_run - m_new) : 1.f;
       l_run *= corr;
 #pragma unroll
-      for (int i = 0; i < C::NOB; ++i) acc[i] *= corr;
+      for (int i = 0; i < NOB; ++i) acc[i] *= corr;
       m_run = m_new;
     }
     const float m_use = m_run == kNegInf ? 0.f : m_run;
+    if constexpr (CPW > 1) {
+      // ---- O^T += V^T . P^T, 32 keys per step: k-slot 8 g4 + e <-> key
+      //      32 bp + 4 g4 + e (e < 4) or 32 bp + 16 + 4 g4 + e - 4 (e >= 4)
+#pragma unroll
+      for (int bp = 0; bp < C::NBLK / 2; ++bp) {
+        float pr[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          pr[r] = fast_exp2(sc[2 * bp + r / 4][r % 4] - m_use);
+          l_run += pr[r];
+        }
+        u32x4 hi, lo = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hi[e] = cvt_pk(T{}, pr[2 * e], pr[2 * e + 1]);
+        if constexpr (std::is_same<T, TBF16>::value) {
+          if (split_p) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              uint32_t h, l;
+              T::split2(pr[2 * e], pr[2 * e + 1], h, l);
+              hi[e] = h;
+              lo[e] = l;
+            }
+          }
+        }
+        const uint8_t* vb = Vs + 32 * bp * C::RB + vlane;
+#pragma unroll
+        for (int i = 0; i < NOB; ++i) {
+          const int lch = 2 * (ob0 + i) + ((n >> 1) & 1);
+          const u32x2 v0 = lds_read_tr16(vb + ((lch ^ swv) * 16));
+          const u32x2 v1 = lds_read_tr16(vb + 16 * C::RB + ((lch ^ swv) * 16));
+          const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+          acc[i] = mma16(T{}, va, hi, acc[i]);
+          if (split_p) acc[i] = mma16(T{}, va, lo, acc[i]);
+        }
+      }
+    } else {
     // ---- O^T += V^T . P^T, 16 keys per step (k-slot 4 g4 + e <-> key 4 g4 + e)
 #pragma unroll
     for (int blk = 0; blk < C::NBLK; ++blk) {
@@ -626,26 +693,26 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
         pr[r] = fast_exp2(sc[blk][r] - m_use);
         l_run += pr[r];
       }
-      u32x2 hi, lo;
+      u32x2 hi = u32x2{cvt_pk(T{}, pr[0], pr[1]), cvt_pk(T{}, pr[2], pr[3])}, lo = u32x2{0, 0};
       if constexpr (std::is_same<T, TBF16>::value) {
-        // bf16 P carries 8 significant bits: P = hi + lo (the matrix cores
-        // have ample headroom in this bandwidth-bound kernel)
-        uint32_t h0, l0, h1, l1;
-        T::split2(pr[0], pr[1], h0, l0);
-        T::split2(pr[2], pr[3], h1, l1);
-        hi = u32x2{h0, h1};
-        lo = u32x2{l0, l1};
-      } else {
-        hi = u32x2{cvt_pk(T{}, pr[0], pr[1]), cvt_pk(T{}, pr[2], pr[3])};
+        if (split_p) {
+          // bf16 P carries 8 significant bits: P = hi + lo
+          uint32_t h0, l0, h1, l1;
+          T::split2(pr[0], pr[1], h0, l0);
+          T::split2(pr[2], pr[3], h1, l1);
+          hi = u32x2{h0, h1};
+          lo = u32x2{l0, l1};
+        }
       }
       const uint8_t* vb = Vs + 16 * blk * C::RB + vlane;
 #pragma unroll
-      for (int i = 0; i < C::NOB; ++i) {
-        const int lch = 2 * (wave * C::NOB + i) + ((n >> 1) & 1);  // chunk of columns d0 + 4(n%4)
+      for (int i = 0; i < NOB; ++i) {
+        const int lch = 2 * (ob0 + i) + ((n >> 1) & 1);  // chunk of columns d0 + 4(n%4)
         const u32x2 va = lds_read_tr16(vb + ((lch ^ swv) * 16));
         acc[i] = mma16k16(T{}, va, hi, acc[i]);
-        if constexpr (std::is_same<T, TBF16>::value) acc[i] = mma16k16(T{}, va, lo, acc[i]);
+        if (split_p) acc[i] = mma16k16(T{}, va, lo, acc[i]);
       }
+    }
     }
   }
 
@@ -657,8 +724,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
     if (head_ok) {
       float* po = p.part_o + (bh * p.nsplit + split) * D;
 #pragma unroll
-      for (int i = 0; i < C::NOB; ++i)
-        *(f32x4*)(po + 16 * (wave * C::NOB + i) + 4 * g4) = acc[i];
+      for (int i = 0; i < NOB; ++i)
+        *(f32x4*)(po + 16 * (ob0 + i) + 4 * g4) = acc[i];
       if (wave == 0 && g4 == 0) {
         float* pml = p.part_ml + (bh * p.nsplit + split) * 2;
         pml[0] = m_run;
@@ -680,12 +747,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode16_kernel(AttnParams p) {
     if (head_ok) {
       S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)qi * p.os[2];
 #pragma unroll
-      for (int i = 0; i < C::NOB; ++i) {
+      for (int i = 0; i < NOB; ++i) {
         const f32x4 o = acc[i] * so;
-        if (16 * (wave * C::NOB + i) + 4 * g4 < p.Dv)
-          *(u32x2*)(orow + 16 * (wave * C::NOB + i) + 4 * g4) = u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
+        if (16 * (ob0 + i) + 4 * g4 < p.Dv)
+          *(u32x2*)(orow + 16 * (ob0 + i) + 4 * g4) = u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
       }
-      if (p.lse && wave == 0 && g4 == 0) p.lse[bh] = lse;
+      if (p.lse && (CPW > 1 || wave == 0) && g4 == 0) p.lse[bh] = lse;
     }
   }
 }
@@ -816,7 +883,20 @@ hipError_t launch_d(const AttnParams& p, hipStream_t s) {
   }
 }
 
+// Prefill at head dim 512 (16-bit): 64 columns per workgroup, one pass.
+template <class T>
+hipError_t launch_wide(const AttnParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)((int64_t)p.nchunk * p.Hkv * p.B));
+  if (p.mask) hipLaunchKernelGGL((decode16_kernel<T, 512, true, false, kWaves>), grid, dim3(kThreads), 0, s, p);
+  else hipLaunchKernelGGL((decode16_kernel<T, 512, false, false, kWaves>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_prefill_wide(const AttnParams& p, int dtype, hipStream_t s) {
+  return dtype == SDPA_F16 ? launch_wide<TF16>(p, s) : launch_wide<TBF16>(p, s);
+}
 
 int decode_tile_keys(int dtype, int D) {
   if (dtype == SDPA_F32) return D >= 256 ? 16 : SDPA_DECODE_TILE_BYTES / (8 * D);
