@@ -169,8 +169,8 @@ int64_t decode_chunks(const sdpa_args* a) { return (a->Lq * (a->Hq / a->Hkv) + 1
 // Prefill head dims the 128-row prefill kernels do not hold (kernel head dim
 // 512, or above 128 in fp32: a 32-row wave's O accumulator alone would fill
 // the register file) run on the 16-column kernels of the decode path, one
-// pass over the keys per workgroup: in 16-bit each of the four waves owns 16
-// columns (64 per workgroup), in fp32 the waves share 16.
+// pass over the keys per workgroup: in 16-bit each wave owns 16 columns of
+// its own, in fp32 the four waves share 16.
 bool prefill_narrow(const sdpa_args* a) {
   const int kd = kernel_dim(a);
   return kd == 512 || (a->dtype == SDPA_F32 && kd > 128);
@@ -392,11 +392,8 @@ int sdpa_prefill(const sdpa_args* args, void* stream) {
   if (sdpa::prefill_narrow(args)) {
     p.nsplit = 1;
     p.split_len = (int)args->Lk;
-    if (args->dtype != SDPA_F32) {
-      // 64 columns per workgroup
-      p.nchunk = (int)((args->Lq * (args->Hq / args->Hkv) + 63) / 64);
+    if (args->dtype != SDPA_F32)
       return sdpa::launch_status(sdpa::launch_prefill_wide(p, args->dtype, (hipStream_t)stream));
-    }
     p.nchunk = (int)sdpa::decode_chunks(args);
     return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
   }

@@ -40,7 +40,7 @@ AttnParams make_params(const sdpa_args& a);
 // Kernel launchers: return hipSuccess or the launch error.
 hipError_t launch_prefill(const AttnParams& p, int dtype, bool causal, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s);
-// 16-bit prefill at kernel head dim 512: nchunk = 64-column chunks, one pass
+// 16-bit prefill at kernel head dim 512 (sets its own column chunks), one pass
 hipError_t launch_prefill_wide(const AttnParams& p, int dtype, hipStream_t s);
 // Gradients: ws holds 2 * B * Hq * Lq floats (D_i, then the LSE in log2 units).
 hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float scale, float* ws, int dtype,

@@ -267,3 +267,18 @@ def test_d512_gqa_causal_sampled(dtype):
                                dtype=dtype, sinks=True)
     _full_size(w, heads=[(0, 0), (0, 7), (0, 8), (0, 15)], rows=[0, 1, 2, 15, 16, 1000, 2046, 2047])
 
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("mask", [False, True])
+def test_d512_eight_wave_workgroups_sampled(dtype, mask):
+    """Head dim 512 with a grid large enough for the 128-column (eight-wave)
+    workgroups: B=8, GQA-8 over 1024 causal rows; additive mask with -inf
+    entries broadcast over heads, and sinks."""
+    B, Hq, Hkv, Lq, Lk, D = 8, 16, 2, 1024, 1100, 512
+    x = random_case(2700 + mask, B, Hq, Hkv, Lq, Lk, D, dtype, mask=mask, sinks=True,
+                    mask_neg_inf_frac=0.05, mask_shape=(B, 1, Lq, Lk))
+    say(f"prefill d512 eight-wave {dtype} mask={mask}")
+    out, l, sc = _run(x, dtype, causal=True)
+    compare_sampled(out, l, x, sc, dtype, f"d512 w8 {dtype} mask={mask}",
+                    [(0, 0), (3, 9), (7, 15)], [0, 1, 127, 128, 500, 1023], causal=True)
