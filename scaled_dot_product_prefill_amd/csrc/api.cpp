@@ -164,7 +164,11 @@ int check_common(const sdpa_args* a) {
 
 // Decode: the Lq query rows times the G heads of a KV head are the columns of
 // 16-wide matrix tiles; each chunk of 16 columns is one workgroup per key split.
-int64_t decode_chunks(const sdpa_args* a) { return (a->Lq * (a->Hq / a->Hkv) + 15) / 16; }
+int64_t decode_chunks(const sdpa_args* a) {
+  const int64_t cols = a->Lq * (a->Hq / a->Hkv);
+  const int64_t w = 16 * decode_cpw(a->dtype, cols);
+  return (cols + w - 1) / w;
+}
 
 // Prefill head dims the 128-row prefill kernels do not hold (kernel head dim
 // 512, or above 128 in fp32: a 32-row wave's O accumulator alone would fill
@@ -218,7 +222,7 @@ SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
   if (num_splits >= 2) {
     len = (Lk + num_splits - 1) / num_splits;
   } else {
-    const int64_t tk = decode_tile_keys(a->dtype, kernel_dim(a));
+    const int64_t tk = decode_tile_keys(a->dtype, kernel_dim(a), decode_cpw(a->dtype, a->Lq * (a->Hq / a->Hkv)));
     const int64_t tiles = (Lk + tk - 1) / tk;
     const int64_t units = a->B * a->Hkv * decode_chunks(a);
     int64_t ns = (kDecodeCUs + units - 1) / units;

@@ -52,14 +52,14 @@ struct DecodeUnit {
 __device__ inline DecodeUnit decode_unit(const AttnParams& p, int n, int cpw = 1, int w = 0) {
   DecodeUnit u;
   int chunk, r;
-  if (cpw == 1) {
+  if (cpw == 1 || p.nsplit > 1) {
     // decode: (split, chunk, kv head, batch), split fastest
     u.split = blockIdx.x % p.nsplit;
     r = blockIdx.x / p.nsplit;
     chunk = r % p.nchunk;
     r /= p.nchunk;
   } else {
-    // prefill, one split: (kv head, batch) fastest, so that the workgroups
+    // one split (prefill): (kv head, batch) fastest, so that the workgroups
     // launched first are the heaviest chunks of every head under causal
     // masking (later rows see more keys), and head h stays on XCD h % 8
     // when B * Hkv is a multiple of 8
@@ -477,19 +477,22 @@ struct Dec16 {
 template <int NCH>
 __device__ constexpr int chunk_swz(int row) { return NCH >= 16 ? (row & 15) : ((row >> 1) & (NCH - 1)); }
 
-// CPW = 1 (decode): the four waves share 16 columns; each computes their
-// scores and owns a quarter of the O^T rows.  CPW > 1 (prefill at head dim
-// 512): CPW waves, each owning 16 columns of its own and all O^T rows, so the
-// K / V tiles in LDS serve 16 CPW columns.
-// The CPW = 4 form takes 32-key tiles (128 KiB of LDS at D = 512) so that
-// P.V runs as 16x16x32 products, 32 keys per step, at the full matrix rate.
+// CPW 16-column blocks per workgroup, NW = max(CPW, 4) waves, WPB = NW / CPW
+// waves per block.  The waves of a block each compute the block's scores and
+// own 1 / WPB of its O^T rows: CPW = 1 (decode, G * Lq <= 16) shares one
+// block among four waves; CPW = 2 and 4 (multi-query decode) let K / V stream
+// once for up to 64 columns; CPW = 4 and 8 (prefill at head dim 512) give
+// every wave its own 16 columns and all O^T rows.  With CPW > 1 the tiles are
+// a multiple of 32 keys (at D = 512: 32 keys, 128 KiB of LDS) and P.V runs as
+// 16x16x32 products, 32 keys per step, at the full matrix rate.
 template <class T, int D, bool MASK, bool SPLIT, int CPW = 1>
-__global__ __launch_bounds__(64 * (CPW > 1 ? CPW : kWaves), 1) void decode16_kernel(AttnParams p) {
-  constexpr int NW = CPW > 1 ? CPW : kWaves;  // waves per workgroup
-  using C = Dec16<D, (CPW > 1 ? 32 : 0), NW>;
+__global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode16_kernel(AttnParams p) {
+  constexpr int NW = CPW > kWaves ? CPW : kWaves;  // waves per workgroup
+  constexpr int WPB = NW / CPW;                     // waves per 16-column block
+  using C = Dec16<D, (CPW > 1 && D >= 512 ? 32 : 0), NW>;
   using S = uint16_t;
-  static_assert(CPW == 1 || !SPLIT, "column blocks");
-  constexpr int NOB = CPW > 1 ? D / 16 : C::NOB;  // O^T row blocks per wave
+  static_assert(CPW == 1 || C::NBLK % 2 == 0, "32-key products");
+  constexpr int NOB = D / 16 / WPB;  // O^T row blocks per wave
   __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NST * C::STAGE];
 
   const int tid = threadIdx.x;
@@ -497,9 +500,9 @@ __global__ __launch_bounds__(64 * (CPW > 1 ? CPW : kWaves), 1) void decode16_ker
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15;
   const int g4 = lane >> 4;
-  const int ob0 = CPW > 1 ? 0 : wave * NOB;  // first O^T row block of this wave
+  const int ob0 = (wave % WPB) * NOB;  // first O^T row block of this wave
 
-  const DecodeUnit u = decode_unit(p, n, CPW, CPW > 1 ? wave : 0);
+  const DecodeUnit u = decode_unit(p, n, CPW, wave / WPB);
   const int split = u.split, hk = u.hk, b = u.b, hq = u.hq, qi = u.qi;
   const bool head_ok = u.ok;
 
@@ -733,7 +736,7 @@ __global__ __launch_bounds__(64 * (CPW > 1 ? CPW : kWaves), 1) void decode16_ker
 #pragma unroll
       for (int i = 0; i < NOB; ++i)
         *(f32x4*)(po + 16 * (ob0 + i) + 4 * g4) = acc[i];
-      if (wave == 0 && g4 == 0) {
+      if (wave % WPB == 0 && g4 == 0) {
         float* pml = p.part_ml + (bh * p.nsplit + split) * 2;
         pml[0] = m_run;
         pml[1] = l_tot;
@@ -759,7 +762,7 @@ __global__ __launch_bounds__(64 * (CPW > 1 ? CPW : kWaves), 1) void decode16_ker
         if (16 * (ob0 + i) + 4 * g4 < p.Dv)
           *(u32x2*)(orow + 16 * (ob0 + i) + 4 * g4) = u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
       }
-      if (p.lse && (CPW > 1 || wave == 0) && g4 == 0) p.lse[bh] = lse;
+      if (p.lse && wave % WPB == 0 && g4 == 0) p.lse[bh] = lse;
     }
   }
 }
@@ -849,19 +852,37 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   }
 }
 
+template <class T, int D, bool SPLIT>
+void launch16(const AttnParams& p, int cpw, bool mask, dim3 grid, hipStream_t s) {
+  const dim3 block(kThreads);  // four waves for CPW <= 4
+  switch (cpw) {
+    case 1:
+      if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, SPLIT, 1>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode16_kernel<T, D, false, SPLIT, 1>), grid, block, 0, s, p);
+      break;
+    case 2:
+      if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, SPLIT, 2>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode16_kernel<T, D, false, SPLIT, 2>), grid, block, 0, s, p);
+      break;
+    default:
+      if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, SPLIT, 4>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((decode16_kernel<T, D, false, SPLIT, 4>), grid, block, 0, s, p);
+  }
+}
+
 template <class T, int D>
 hipError_t launch_t(const AttnParams& p, hipStream_t s) {
   const dim3 grid((unsigned)((int64_t)p.nsplit * p.nchunk * p.Hkv * p.B));
   const dim3 block(kThreads);
   const bool mask = p.mask != nullptr;
   constexpr bool F32 = std::is_same<T, TF32>::value;
+  const int cpw = decode_cpw(F32 ? SDPA_F32 : SDPA_F16, (int64_t)p.Lq * p.group);
   if (p.nsplit > 1) {
     if constexpr (F32) {
       if (mask) hipLaunchKernelGGL((decode_f32_kernel<T, D, true, true>), grid, block, 0, s, p);
       else hipLaunchKernelGGL((decode_f32_kernel<T, D, false, true>), grid, block, 0, s, p);
     } else {
-      if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((decode16_kernel<T, D, false, true>), grid, block, 0, s, p);
+      launch16<T, D, true>(p, cpw, mask, grid, s);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -873,8 +894,7 @@ hipError_t launch_t(const AttnParams& p, hipStream_t s) {
       if (mask) hipLaunchKernelGGL((decode_f32_kernel<T, D, true, false>), grid, block, 0, s, p);
       else hipLaunchKernelGGL((decode_f32_kernel<T, D, false, false>), grid, block, 0, s, p);
     } else {
-      if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, false>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((decode16_kernel<T, D, false, false>), grid, block, 0, s, p);
+      launch16<T, D, false>(p, cpw, mask, grid, s);
     }
   }
   return hipGetLastError();
@@ -916,13 +936,13 @@ hipError_t launch_prefill_wide(const AttnParams& p, int dtype, hipStream_t s) {
   return dtype == SDPA_F16 ? launch_wide<TF16>(p, s) : launch_wide<TBF16>(p, s);
 }
 
-int decode_tile_keys(int dtype, int D) {
+int decode_tile_keys(int dtype, int D, int cpw) {
   if (dtype == SDPA_F32) return D >= 256 ? 16 : SDPA_DECODE_TILE_BYTES / (8 * D);
   switch (D) {
     case 64: return Dec16<64>::TK;
     case 128: return Dec16<128>::TK;
     case 256: return Dec16<256>::TK;
-    default: return Dec16<512>::TK;
+    default: return cpw > 1 ? Dec16<512, 32>::TK : Dec16<512>::TK;
   }
 }
 

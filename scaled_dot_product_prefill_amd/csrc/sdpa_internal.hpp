@@ -46,7 +46,12 @@ hipError_t launch_prefill_wide(const AttnParams& p, int dtype, hipStream_t s);
 hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float scale, float* ws, int dtype,
                            bool causal, hipStream_t s);
 
-// Decode tiling shared by the host heuristics and the kernels.
-int decode_tile_keys(int dtype, int D);
+// Decode tiling shared by the host heuristics and the kernels.  The Lq * G
+// (query row, head) columns of a KV head form 16-column blocks; in 16-bit up
+// to four blocks share one pass over K / V (one workgroup per chunk and split).
+inline int decode_cpw(int dtype, int64_t cols) {
+  return dtype == SDPA_F32 ? 1 : (cols > 32 ? 4 : (cols > 16 ? 2 : 1));
+}
+int decode_tile_keys(int dtype, int D, int cpw);
 
 }  // namespace sdpa

@@ -123,10 +123,11 @@ def test_decode_errors():
 
 
 # Multi-query decode (Lq query rows per head, speculative / chunked decoding):
-# the rows and the G heads of a KV head share the 16 columns of the matrix
-# tiles, 16 columns per workgroup; causal is bottom-right within the block.
+# the rows and the G heads of a KV head are the columns of 16-column matrix
+# tiles, 16, 32 or 64 columns per workgroup (Lq * G of 16, 32, 51 and 64
+# below); causal is bottom-right within the block.
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
-@pytest.mark.parametrize("Lq,G", [(2, 8), (4, 8), (8, 4), (16, 1), (3, 17)])
+@pytest.mark.parametrize("Lq,G", [(2, 8), (4, 8), (8, 8), (8, 4), (16, 1), (3, 17)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_multi_query(dtype, Lq, G, causal):
     Hkv, D, Lk = 2, (512 if G == 8 else 128), 1500
