@@ -217,7 +217,8 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_split
  * dK and dV of a KV head sum over the
  * Hq / Hkv query heads that read it.  The mask is a constant (no gradient).
  * Padding rows (past seqlens_q[b]) get dQ = 0, padding keys dK = dV = 0.
- * Supported: dtype F16 or BF16, D = Dv in {64, 128}.  dq, dk, dv are written in
+ * Supported: dtype F16 or BF16; D (q, k, dq, dk) and Dv (v, o, dout, dv) any
+ * multiples of 8 up to 128, as in the forward.  dq, dk, dv are written in
  * the input dtype with the layout rules of q, k, v (last dim contiguous,
  * 16-byte aligned pointers and strides); dsinks (optional, used only with
  * sinks) is fp32 [Hq].  The workspace (device memory, 16-byte aligned,
@@ -226,10 +227,10 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_split
  * kernels are enqueued on `stream`; nothing is allocated or synchronised.
  * The outputs must not overlap each other, the inputs or the workspace. */
 typedef struct sdpa_bwd_args {
-  const void *dout; int64_t dout_stride[3];  /* [B, Hq,  Lq, D] upstream gradient */
-  void *dq;         int64_t dq_stride[3];    /* [B, Hq,  Lq, D] output            */
-  void *dk;         int64_t dk_stride[3];    /* [B, Hkv, Lk, D] output            */
-  void *dv;         int64_t dv_stride[3];    /* [B, Hkv, Lk, D] output            */
+  const void *dout; int64_t dout_stride[3];  /* [B, Hq,  Lq, Dv] upstream gradient */
+  void *dq;         int64_t dq_stride[3];    /* [B, Hq,  Lq, D]  output            */
+  void *dk;         int64_t dk_stride[3];    /* [B, Hkv, Lk, D]  output            */
+  void *dv;         int64_t dv_stride[3];    /* [B, Hkv, Lk, Dv] output            */
   float *dsinks;                             /* optional [Hq] fp32 output         */
 } sdpa_bwd_args;
 

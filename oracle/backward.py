@@ -43,7 +43,8 @@ def sdpa_backward_reference(q, k, v, dout, *, scale: float, causal: bool = False
                             ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, Optional[np.ndarray]]:
     """Gradients (dQ, dK, dV, dsinks) in float64; dsinks is None without sinks.
 
-    Shapes as in sdpa_reference; dout has the shape of q."""
+    Shapes as in sdpa_reference; dout has the shape of the output o,
+    [B, Hq, Lq, Dv] (Dv, the head dim of v, may differ from that of q, k)."""
     Q, K, V, dO = _f64(q), _f64(k), _f64(v), _f64(dout)
     B, Hq, Lq, D = Q.shape
     Hkv, Lk = K.shape[1], K.shape[2]

@@ -294,13 +294,15 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
                      want_dsinks: bool = False, workspace: Optional[torch.Tensor] = None):
     """Gradients of prefill(q, k, v, ...) = o (with log-sum-exp ``lse``) for the
     upstream gradient ``dout``: returns (dq, dk, dv) or, with ``want_dsinks``,
-    (dq, dk, dv, dsinks).  fp16 / bf16 inputs, D in {64, 128}."""
+    (dq, dk, dv, dsinks).  fp16 / bf16 inputs, head dims (D of q, k; Dv of v)
+    multiples of 8 up to 128."""
     lib = library()
     q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
     o, dout = _prep(o, "o"), _prep(dout, "dout")
     B, Hq, Lq, D = q.shape
-    if o.shape != q.shape or dout.shape != q.shape:
-        raise ValueError("o and dout must have the shape of q")
+    oshape = (B, Hq, Lq, v.shape[3])
+    if tuple(o.shape) != oshape or tuple(dout.shape) != oshape:
+        raise ValueError(f"o and dout must be [B, Hq, Lq, Dv] = {oshape}")
     lse = lse.to(torch.float32).contiguous()
     if lse.shape != (B, Hq, Lq):
         raise ValueError(f"lse must be [B, Hq, Lq] = {(B, Hq, Lq)}, got {tuple(lse.shape)}")

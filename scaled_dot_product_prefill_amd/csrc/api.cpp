@@ -275,8 +275,9 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
   if (st != SDPA_OK) return st;
   if (!g) return fail(SDPA_ERR_NULL, "gradient arguments are NULL");
   if (a->dtype == SDPA_F32) return fail(SDPA_ERR_UNSUPPORTED, "backward supports F16 and BF16 inputs");
-  if ((a->D != 64 && a->D != 128) || dv_of(a) != a->D)
-    return fail(SDPA_ERR_UNSUPPORTED, "backward supports D = Dv in {64, 128}, got D=%lld Dv=%lld", (long long)a->D,
+  const int kd = kernel_dim(a);
+  if (kd != 64 && kd != 128)
+    return fail(SDPA_ERR_UNSUPPORTED, "backward supports head dims up to 128, got D=%lld Dv=%lld", (long long)a->D,
                 (long long)dv_of(a));
   if (!a->lse) return fail(SDPA_ERR_NULL, "backward needs the forward's lse");
   if (!g->dout || !g->dq || !g->dk || !g->dv) return fail(SDPA_ERR_NULL, "dout, dq, dk and dv must be non-NULL");
@@ -296,8 +297,8 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
     return fail(SDPA_ERR_UNSUPPORTED, "dout row stride above %lld bytes", (long long)kMaxRowBytes);
   if (a->q_stride[2] * 2 > kMaxRowBytes)
     return fail(SDPA_ERR_UNSUPPORTED, "q row stride above %lld bytes", (long long)kMaxRowBytes);
-  if (g->dq_stride[2] < a->D || g->dk_stride[2] < a->D || g->dv_stride[2] < a->D)
-    return fail(SDPA_ERR_ARG, "gradient rows overlap (row stride < D)");
+  if (g->dq_stride[2] < a->D || g->dk_stride[2] < a->D || g->dv_stride[2] < dv_of(a))
+    return fail(SDPA_ERR_ARG, "gradient rows overlap (row stride below the head dim)");
   if (g->dsinks && (uintptr_t)g->dsinks % 4 != 0) return fail(SDPA_ERR_ALIGN, "dsinks is not 4-byte aligned");
   const size_t need = backward_workspace(a);
   if (!ws) return fail(SDPA_ERR_WORKSPACE, "backward needs a workspace of %zu bytes", need);
@@ -307,7 +308,7 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
   // outputs: disjoint from each other, from every input and from the workspace
   const Extent outs[4] = {tensor_extent(g->dq, g->dq_stride, a->B, a->Hq, a->Lq, a->D, 2),
                           tensor_extent(g->dk, g->dk_stride, a->B, a->Hkv, a->Lk, a->D, 2),
-                          tensor_extent(g->dv, g->dv_stride, a->B, a->Hkv, a->Lk, a->D, 2), Extent{}};
+                          tensor_extent(g->dv, g->dv_stride, a->B, a->Hkv, a->Lk, dv_of(a), 2), Extent{}};
   Extent eds;
   if (g->dsinks) { eds.lo = (uintptr_t)g->dsinks; eds.hi = eds.lo + a->Hq * 4; eds.valid = true; }
   Extent ews;
@@ -316,9 +317,9 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
   int n = 0;
   ins[n++] = tensor_extent(a->q, a->q_stride, a->B, a->Hq, a->Lq, a->D, 2);
   ins[n++] = tensor_extent(a->k, a->k_stride, a->B, a->Hkv, a->Lk, a->D, 2);
-  ins[n++] = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, a->D, 2);
-  ins[n++] = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, a->D, 2);
-  ins[n++] = tensor_extent(g->dout, g->dout_stride, a->B, a->Hq, a->Lq, a->D, 2);
+  ins[n++] = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, dv_of(a), 2);
+  ins[n++] = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, dv_of(a), 2);
+  ins[n++] = tensor_extent(g->dout, g->dout_stride, a->B, a->Hq, a->Lq, dv_of(a), 2);
   { Extent e; e.lo = (uintptr_t)a->lse; e.hi = e.lo + a->B * a->Hq * a->Lq * 4; e.valid = true; ins[n++] = e; }
   if (a->mask) {
     const int64_t last = (a->B - 1) * a->mask_stride[0] + (a->Hq - 1) * a->mask_stride[1] +

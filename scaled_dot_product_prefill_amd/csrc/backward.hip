@@ -1,4 +1,6 @@
-// Gradients of the prefill attention (fp16 / bf16 inputs, D in {64, 128}).
+// Gradients of the prefill attention (fp16 / bf16 inputs; head dims D of q, k
+// and Dv of v, o, any multiples of 8 up to 128, run at kernel dim 64 or 128
+// with the chunks past the real dims loaded as zero and never stored).
 //
 // The structure follows the two backward kernels of the rustytorch
 // "flash_attention.metal" page: one kernel per query block computes dQ
@@ -91,25 +93,29 @@ struct BwdParams {
 };
 
 // Per-lane source offset of the direct loads of a Tile64: the 16 bytes that
-// land in LDS row r, chunk c come from logical chunk c ^ swz(r) of row r.
+// land in LDS row r, chunk c come from logical chunk c ^ swz(r) of row r; a
+// chunk past the matrix's real head dim loads nothing (kNoLoad: beyond every
+// tile's byte count, so the range check returns zero).
 template <int D, int NW = kBwdWaves>
-__device__ inline uint32_t tile_lane_off(int wave, int lane, int64_t row_stride_elems) {
+__device__ inline uint32_t tile_lane_off(int wave, int lane, int64_t row_stride_elems, int real_d) {
   using L = Tile64<D, NW>;
   const int pos = wave * 64 + lane;
   const int row = pos / L::NCH, pch = pos % L::NCH;
-  return (uint32_t)(row * row_stride_elems * 2 + (pch ^ L::swz(row)) * 16);
+  const int lch = pch ^ L::swz(row);
+  return lch * 8 < real_d ? (uint32_t)(row * row_stride_elems * 2 + lch * 16) : kNoLoad;
 }
 
 // Issue this wave's direct loads of rows [r0, r0 + 64) of a matrix (rows >=
-// nrows read as zero) into the Tile64 whose LDS byte address is `lds`.
+// nrows read as zero) into the Tile64 whose LDS byte address is `lds`.  The
+// byte count ends at the real length (real_d elements) of the last real row.
 template <int D, int NW = kBwdWaves>
 __device__ inline void tile_issue(const uint16_t* base, int64_t rs, int r0, int nrows, uint32_t off,
-                                  uint32_t lds, int wave) {
+                                  uint32_t lds, int wave, int real_d) {
   using L = Tile64<D, NW>;
   const uint16_t* tb = base + (int64_t)r0 * rs;
-  const int rows = nrows - r0;
+  const int rows = min(nrows - r0, L::ROWS);
   const uint32_t rowb = (uint32_t)(rs * 2);
-  const uint32_t nb = rows >= 64 ? 0xffffffffu : (uint32_t)(rows - 1) * rowb + L::RB;
+  const uint32_t nb = (uint32_t)(rows - 1) * rowb + (uint32_t)real_d * 2;
 #pragma unroll
   for (int i = 0; i < L::LPW; ++i)
     dma16(tb, nb, lds + (wave + NW * i) * 1024, off, i * L::STEP_ROWS * rowb);
@@ -201,11 +207,13 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
     const int ii = ok ? my_i : 0;
     const S* qr = (const S*)p.q + b * p.qs[0] + hq * p.qs[1] + (int64_t)ii * p.qs[2];
     const S* dr = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1] + (int64_t)ii * bp.dos[2];
+    const int nq = p.Dqk / 8, nd = p.Dv / 8;  // real 16-byte chunks; the rest is zero
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
-      const u32x4 a = ldg16_cached(qr + (2 * s + g) * 8), d = ldg16_cached(dr + (2 * s + g) * 8);
-      qreg[s] = ok ? a : u32x4{0, 0, 0, 0};
-      doreg[s] = ok ? d : u32x4{0, 0, 0, 0};
+      const int ch = 2 * s + g;
+      const u32x4 a = ldg16_cached(qr + min(ch, nq - 1) * 8), d = ldg16_cached(dr + min(ch, nd - 1) * 8);
+      qreg[s] = ok && ch < nq ? a : u32x4{0, 0, 0, 0};
+      doreg[s] = ok && ch < nd ? d : u32x4{0, 0, 0, 0};
     }
   }
   const int64_t wrow = ((int64_t)b * p.Hq + hq) * p.Lq + (ok ? my_i : 0);
@@ -223,13 +231,13 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
 
   const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
   const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
-  const uint32_t koff = tile_lane_off<D>(wave, lane, p.ks[2]);
-  const uint32_t voff = tile_lane_off<D>(wave, lane, p.vs[2]);
+  const uint32_t koff = tile_lane_off<D>(wave, lane, p.ks[2], p.Dqk);
+  const uint32_t voff = tile_lane_off<D>(wave, lane, p.vs[2], p.Dv);
   const uint32_t lds0 = lds_addr(smem);
   auto issue = [&](int t) {
     const uint32_t st = lds0 + (t & 1) * 2 * L::BYTES;
-    tile_issue<D>(kbase, p.ks[2], 64 * t, lk, koff, st, wave);
-    tile_issue<D>(vbase, p.vs[2], 64 * t, lk, voff, st + L::BYTES, wave);
+    tile_issue<D>(kbase, p.ks[2], 64 * t, lk, koff, st, wave, p.Dqk);
+    tile_issue<D>(vbase, p.vs[2], 64 * t, lk, voff, st + L::BYTES, wave, p.Dv);
   };
 
   // S^T and dP^T of key block kb of tile t (stage Ks / Vs), and P^T
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
       for (int q4 = 0; q4 < 4; ++q4) {
         const u32x2 w = {cvt_pk(T{}, acc[mb][4 * q4] * sc, acc[mb][4 * q4 + 1] * sc),
                          cvt_pk(T{}, acc[mb][4 * q4 + 2] * sc, acc[mb][4 * q4 + 3] * sc)};
-        *(u32x2*)(orow + 32 * mb + 8 * q4 + 4 * g) = w;
+        if (32 * mb + 8 * q4 + 4 * g < p.Dqk) *(u32x2*)(orow + 32 * mb + 8 * q4 + 4 * g) = w;
       }
   }
 }
@@ -361,11 +369,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
     const int jj = kok ? my_j : 0;
     const S* kr = (const S*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)jj * p.ks[2];
     const S* vr = (const S*)p.v + b * p.vs[0] + hk * p.vs[1] + (int64_t)jj * p.vs[2];
+    const int nk = p.Dqk / 8, nv = p.Dv / 8;  // real 16-byte chunks; the rest is zero
 #pragma unroll
     for (int s = 0; s < NQ; ++s) {
-      const u32x4 a = ldg16_cached(kr + (2 * s + g) * 8), d = ldg16_cached(vr + (2 * s + g) * 8);
-      kreg[s] = kok ? a : u32x4{0, 0, 0, 0};
-      lds_write16(Vw + l32 * L::RB + (((2 * s + g) ^ L::swz(l32)) * 16), kok ? d : u32x4{0, 0, 0, 0});
+      const int ch = 2 * s + g;
+      const u32x4 a = ldg16_cached(kr + min(ch, nk - 1) * 8), d = ldg16_cached(vr + min(ch, nv - 1) * 8);
+      kreg[s] = kok && ch < nk ? a : u32x4{0, 0, 0, 0};
+      lds_write16(Vw + l32 * L::RB + ((ch ^ L::swz(l32)) * 16), kok && ch < nv ? d : u32x4{0, 0, 0, 0});
     }
   }
 
@@ -376,8 +386,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   const int per_head = max(0, nqt - qt0);
   const int ntiles = per_head * p.group;
 
-  const uint32_t qoff = tile_lane_off<D, kDkvWaves>(wave, lane, p.qs[2]);
-  const uint32_t dooff = tile_lane_off<D, kDkvWaves>(wave, lane, bp.dos[2]);
+  const uint32_t qoff = tile_lane_off<D, kDkvWaves>(wave, lane, p.qs[2], p.Dqk);
+  const uint32_t dooff = tile_lane_off<D, kDkvWaves>(wave, lane, bp.dos[2], p.Dv);
   const uint32_t lds0 = lds_addr(smem);
   // tile t = (query tile qt0 + t / G, query head hk * G + t % G)
   auto issue = [&](int t) {
@@ -386,8 +396,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
     const uint32_t st = lds0 + (t & 1) * STAGE;
     const S* qb = (const S*)p.q + b * p.qs[0] + hq * p.qs[1];
     const S* db = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1];
-    tile_issue<D, kDkvWaves>(qb, p.qs[2], q0, lq, qoff, st, wave);
-    tile_issue<D, kDkvWaves>(db, bp.dos[2], q0, lq, dooff, st + L::BYTES, wave);
+    tile_issue<D, kDkvWaves>(qb, p.qs[2], q0, lq, qoff, st, wave, p.Dqk);
+    tile_issue<D, kDkvWaves>(db, bp.dos[2], q0, lq, dooff, st + L::BYTES, wave, p.Dv);
     if (wave == 0) {
       const int64_t r0 = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
       const uint32_t nb = (uint32_t)min(64, p.Lq - q0) * 4;
@@ -504,8 +514,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
                           cvt_pk(T{}, dk[mb][4 * q4 + 2] * sc, dk[mb][4 * q4 + 3] * sc)};
         const u32x2 wv = {cvt_pk(T{}, dv[mb][4 * q4], dv[mb][4 * q4 + 1]),
                           cvt_pk(T{}, dv[mb][4 * q4 + 2], dv[mb][4 * q4 + 3])};
-        *(u32x2*)(kr + 32 * mb + 8 * q4 + 4 * g) = wk;
-        *(u32x2*)(vr + 32 * mb + 8 * q4 + 4 * g) = wv;
+        if (32 * mb + 8 * q4 + 4 * g < p.Dqk) *(u32x2*)(kr + 32 * mb + 8 * q4 + 4 * g) = wk;
+        if (32 * mb + 8 * q4 + 4 * g < p.Dv) *(u32x2*)(vr + 32 * mb + 8 * q4 + 4 * g) = wv;
       }
   }
 }

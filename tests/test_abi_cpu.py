@@ -267,8 +267,15 @@ def _bwd(lib, ws=1 << 45, ws_bytes=1 << 30, gkw=None, **kw):
 def test_backward_validation(lib):
     assert _bwd(lib) == S.OK
     assert _bwd(lib, dtype=sdpa.F32) == S.ERR_UNSUPPORTED
-    assert _bwd(lib, D=96) == S.ERR_UNSUPPORTED
-    assert _bwd(lib, Dv=64) == S.ERR_UNSUPPORTED
+    assert _bwd(lib, D=96) == S.OK                               # runs at kernel dim 128
+    assert _bwd(lib, Dv=64) == S.OK                              # D = 128, Dv = 64
+    assert _bwd(lib, D=100) == S.ERR_UNSUPPORTED                 # not a multiple of 8
+    assert _bwd(lib, D=136, q_stride=(8 * 64 * 136, 64 * 136, 136), k_stride=(2 * 64 * 136, 64 * 136, 136),
+                v_stride=(2 * 64 * 136, 64 * 136, 136), o_stride=(8 * 64 * 136, 64 * 136, 136),
+                gkw={"dq_stride": (8 * 64 * 136, 64 * 136, 136), "dk_stride": (2 * 64 * 136, 64 * 136, 136),
+                     "dv_stride": (2 * 64 * 136, 64 * 136, 136),
+                     "dout_stride": (8 * 64 * 136, 64 * 136, 136)}) == S.ERR_UNSUPPORTED   # above 128
+    assert _bwd(lib, Dv=64, gkw={"dv_stride": (2 * 64 * 56, 64 * 56, 56)}) == S.ERR_ARG  # dv rows overlap
     assert _bwd(lib, lse=None) == S.ERR_NULL
     assert _bwd(lib, gkw={"dq": None}) == S.ERR_NULL
     assert _bwd(lib, gkw={"dk": (1 << 41) + 8}) == S.ERR_ALIGN

@@ -2,7 +2,8 @@
 ABI) against the fp64 gradient oracle: a grid of small cases spanning several
 tiles with ragged tails (GQA, bottom-right causal with Lq != Lk, rows without
 keys, additive mask with -inf entries, sinks and their gradient, per-batch
-lengths with NaN in the padding) for fp16 / bf16 and D = 64 / 128, plus the
+lengths with NaN in the padding) for fp16 / bf16 and D = 64 / 128, head dims
+that are multiples of 8 up to 128 with Dv != D, plus the
 autograd wrapper.
 
 Tolerance: gradients are linear in dO, so the forward's elementwise bound
@@ -86,6 +87,30 @@ def test_backward_grid(dtype, D, case):
         pairs.append((ds, rs, "dsinks"))
     else:
         assert ds is None
+    _check_all(pairs)
+
+
+# (D, Dv): head dims that are multiples of 8 up to 128, run at kernel dim 64
+# or 128 with zero chunks past the real dims
+BWD_DIMS = [(8, 8), (40, 40), (96, 96), (112, 112), (128, 64), (64, 120)]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dims", BWD_DIMS, ids=lambda d: f"{d[0]}x{d[1]}")
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_head_dims(dtype, dims, causal):
+    D, Dv = dims
+    B, Hq, Hkv, Lq, Lk = 2, 4, 2, 150, 211
+    say(f"backward head dims {dtype} D={D} Dv={Dv} causal={causal}")
+    x = random_case(5300 + D + Dv, B, Hq, Hkv, Lq, Lk, D, dtype, Dv=Dv, sinks=causal, sink_scale=2.0)
+    dout = _dout(5300 + D, (B, Hq, Lq, Dv), dtype)
+    (dq, dk, dv, ds), sc = _run(x, dout, dtype, causal, want_dsinks=True)
+    assert dq.shape == x["q"].shape and dk.shape == x["k"].shape and dv.shape == x["v"].shape
+    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=causal,
+                                             sinks=x["sinks"])
+    pairs = [(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")]
+    if causal:
+        pairs.append((ds, rs, "dsinks"))
     _check_all(pairs)
 
 

@@ -34,11 +34,12 @@ def _close(a, b, tol, what):
 
 
 FD_CASES = [
-    # (B, Hq, Hkv, Lq, Lk, D, causal, mask, sinks, seqlens_q, seqlens_k)
-    (1, 2, 2, 3, 4, 3, False, False, False, None, None),
-    (2, 4, 2, 3, 5, 2, True, False, True, None, None),       # GQA, causal Lq < Lk, sinks
-    (1, 2, 1, 4, 3, 2, True, True, True, None, None),        # Lq > Lk, mask with -inf
-    (2, 2, 1, 3, 4, 2, True, False, True, [3, 2], [4, 1]),   # per-batch lengths
+    # (B, Hq, Hkv, Lq, Lk, D, causal, mask, sinks, seqlens_q, seqlens_k, Dv)
+    (1, 2, 2, 3, 4, 3, False, False, False, None, None, None),
+    (2, 4, 2, 3, 5, 2, True, False, True, None, None, None),       # GQA, causal Lq < Lk, sinks
+    (1, 2, 1, 4, 3, 2, True, True, True, None, None, None),        # Lq > Lk, mask with -inf
+    (2, 2, 1, 3, 4, 2, True, False, True, [3, 2], [4, 1], None),   # per-batch lengths
+    (1, 2, 1, 3, 4, 2, True, False, True, None, None, 3),          # value head dim 3 != 2
 ]
 
 
@@ -49,12 +50,12 @@ def _loss(q, k, v, dout, sinks, kw):
 
 def pin_finite_differences(ref):
     h = 1e-6
-    for n, (B, Hq, Hkv, Lq, Lk, D, causal, mask, sinks, sq, sk) in enumerate(FD_CASES):
+    for n, (B, Hq, Hkv, Lq, Lk, D, causal, mask, sinks, sq, sk, Dv) in enumerate(FD_CASES):
         x = random_case(500 + n, B, Hq, Hkv, Lq, Lk, D, "fp32", mask=mask, sinks=sinks,
-                        sink_scale=1.5, mask_neg_inf_frac=0.25)
+                        sink_scale=1.5, mask_neg_inf_frac=0.25, Dv=Dv)
         q, k, v = (x[t].double().numpy() for t in ("q", "k", "v"))
         s = None if x["sinks"] is None else x["sinks"].double().numpy()
-        dout = np.random.default_rng(600 + n).standard_normal(q.shape)
+        dout = np.random.default_rng(600 + n).standard_normal(q.shape[:3] + v.shape[3:])
         kw = dict(scale=0.9, causal=causal, mask=x["mask"],
                   seqlens_q=None if sq is None else np.array(sq),
                   seqlens_k=None if sk is None else np.array(sk))
