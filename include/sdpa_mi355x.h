@@ -211,9 +211,10 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_split
  * `fwd` is the argument block of the forward call whose output is being
  * differentiated: q, k, v, mask, sinks, seqlens_q / seqlens_k, scale and
  * causal as there; lse (its log-sum-exp, REQUIRED) is read, not written.
- * o (the forward's output) is part of the signature, as in the cuDNN graph,
- * and is validated, but D_i is formed as sum_j P_ij (dO V^T)_ij, which equals
- * dO_i . O_i without inheriting the rounding of a 16-bit O; o is not read.
+ * o (the forward's output, [B, Hq, Lq, Dv]) is read for D_i = dO_i . O_i on
+ * query blocks whose every row sees more than 256 keys (no mask), where the
+ * 16-bit rounding of O averages out; for the other rows D_i is formed as
+ * sum_j P_ij (dO V^T)_ij (equal to dO_i . O_i), free of that rounding.
  * dK and dV of a KV head sum over the
  * Hq / Hkv query heads that read it.  The mask is a constant (no gradient).
  * Padding rows (past seqlens_q[b]) get dQ = 0, padding keys dK = dV = 0.

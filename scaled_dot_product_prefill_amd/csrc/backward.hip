@@ -16,19 +16,22 @@
 // token).  A sink only enters the denominator, so it changes dQ, dK, dV only
 // through the LSE; its own gradient is -sum_i exp(sink - LSE_i) D_i.
 //
-// D_i is formed as sum_j P_ij dP_ij, which equals dO_i . O_i, instead of from
-// the stored O: a 16-bit O carries its rounding (and the forward's P
-// rounding) into every dS of the row, which showed as errors of a few 1e-3 in
-// bf16 dQ for rows with few keys.
+// For rows that see few keys (at most 256, or any row under a mask) D_i is
+// formed as sum_j P_ij dP_ij, which equals dO_i . O_i, instead of from the
+// stored O: a 16-bit O carries its rounding (and the forward's P rounding)
+// into every dS of the row, which showed as errors of a few 1e-3 in bf16 dQ
+// for such rows.  Rows that see more keys read O (one pass over the keys
+// fewer in the dQ kernel).
 //
 // Kernels, in launch order:
 //   bwd_prep_kernel   LSE_i in log2 units (+inf for rows without a key or
 //                     past the batch's length) into the workspace;
 //   bwd_dq_kernel     workgroup = 128 query rows of one (batch, query head);
-//                     each wave owns 32 rows, key tiles stream through LDS
-//                     twice: S^T = K Q^T and dP^T = V dO^T (lanes own
-//                     queries) give D_i on the first pass (written to the
-//                     workspace), then dQ^T += K^T dS^T on the second;
+//                     each wave owns 32 rows, key tiles stream through LDS:
+//                     for rows that see few keys twice, S^T = K Q^T and
+//                     dP^T = V dO^T (lanes own queries) giving D_i on the
+//                     first pass, otherwise D_i = dO_i . O_i; D_i goes to the
+//                     workspace, then dQ^T += K^T dS^T on the (last) pass;
 //   bwd_dkv_kernel    workgroup = 256 keys of one (batch, KV head), 8 waves
 //                     (two per SIMD: K rows in registers, V rows in LDS, so
 //                     a wave fits half the register file); each wave
@@ -266,10 +269,36 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
     }
   };
 
-  // pass 1: D_i = sum_j P_ij dP_ij
+  // D_i.  Where every row of the workgroup sees more than 256 keys (and no
+  // mask can hide them), D_i = dO_i . O_i from the forward's output: the
+  // 16-bit rounding of O then shifts dS_ij = P_ij (dP_ij - D_i) by the same
+  // tiny amount across many keys, and dQ_i = scale sum_j dS_ij K_j averages
+  // it away.  Rows that see fewer keys form D_i = sum_j P_ij dP_ij in a first
+  // pass over the keys (pass 1), free of that rounding.
+  const int first_keys = i0 < lq ? (CAUSAL ? min(lk, i0 + 1 + coff) : lk) : 0;
+  const bool d_from_o = !MASK && first_keys > 256;
   float dsum = 0.f;
-  if (ntiles > 0) issue(0);
-  for (int t = 0; t < ntiles; ++t) {
+  if (d_from_o) {
+    if (ok) {
+      const S* orow = (const S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)my_i * p.os[2];
+      const int nd = p.Dv / 8;
+#pragma unroll
+      for (int s = 0; s < NQ; ++s) {
+        const int ch = 2 * s + g;  // the chunk of dO this lane holds
+        if (ch < nd) {
+          const u32x4 ov = ldg16_cached(orow + ch * 8);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dsum = fmaf(T::to_f32((uint16_t)(ov[e] & 0xffffu)), T::to_f32((uint16_t)(doreg[s][e] & 0xffffu)), dsum);
+            dsum = fmaf(T::to_f32((uint16_t)(ov[e] >> 16)), T::to_f32((uint16_t)(doreg[s][e] >> 16)), dsum);
+          }
+        }
+      }
+    }
+  }
+  // pass 1: D_i = sum_j P_ij dP_ij
+  if (!d_from_o && ntiles > 0) issue(0);
+  for (int t = 0; t < (d_from_o ? 0 : ntiles); ++t) {
     wait_vmcnt<0>();
     lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
     if (t + 1 < ntiles) issue(t + 1);
