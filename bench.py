@@ -204,8 +204,8 @@ class Timed:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
