@@ -763,82 +763,104 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // ---- pipeline.  Tile t lives in stage t & 1 of both rings.  Iteration t
   // waits for K(t+1) and V(t) (issued one iteration earlier), then refills the
   // stages that K(t) and V(t-1) occupied, whose last reads precede the barrier.
-  f32x16 sa[C::NKB], sb[C::NKB];
-  if (ntiles > 0) {
-    issue_k(0, Kring);
-    if (ntiles > 1) issue_k(1, Kring + C::TILE);
-    issue_v(0, Vring);
-    wait_vmcnt<0>();
-    lds_barrier();
-    qk(Kring, sa);
-    update_max(0 < n_int ? tile_max(0, sa, std::false_type{}) : tile_max(0, sa, std::true_type{}));
+  // A wave whose 32 rows all lie past the batch's real rows (the ragged last
+  // workgroup of a head) computes nothing: it only keeps its share of the K /
+  // V loads and the workgroup's barriers, in the same order as the others,
+  // and leaves its rows empty.  Its SIMD time goes to the waves beside it.
+  const bool idle = iw >= lq;
+  if (idle) {
+    if (ntiles > 0) {
+      issue_k(0, Kring);
+      if (ntiles > 1) issue_k(1, Kring + C::TILE);
+      issue_v(0, Vring);
+      wait_vmcnt<0>();
+      lds_barrier();
+    }
+    for (int t = 0; t < ntiles; ++t) {
+      const int par = t & 1;
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
+      if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
+    }
+  } else {
+    f32x16 sa[C::NKB], sb[C::NKB];
+    if (ntiles > 0) {
+      issue_k(0, Kring);
+      if (ntiles > 1) issue_k(1, Kring + C::TILE);
+      issue_v(0, Vring);
+      wait_vmcnt<0>();
+      lds_barrier();
+      qk(Kring, sa);
+      update_max(0 < n_int ? tile_max(0, sa, std::false_type{}) : tile_max(0, sa, std::true_type{}));
+    }
+    // steady state (tiles t, t+1 interior, tile t+2 exists, single bf16 P): no
+    // branch between the barrier and the max update, stage offsets fixed by
+    // the parity of t, so matrix-core and VALU work of the two tiles interleave
+    auto steady = [&](int t, auto par_tag, f32x16* cur, f32x16* nxt) {
+      constexpr int PAR = decltype(par_tag)::value;
+      wait_vmcnt<0>();
+      lds_barrier();
+      issue_v(t + 1, Vring + (PAR ^ 1) * C::TILE);
+      issue_k(t + 2, Kring + PAR * C::TILE);
+      const float mx = steady_slots(Kring + (PAR ^ 1) * C::TILE, Vring + PAR * C::TILE, cur, nxt);
+      if constexpr (!kRel) {
+        update_max(mx);
+      } else if (__any(mx > kRescaleSlack)) {
+        // update_max in relative units; S'(t+1) follows the moved max
+        const float d = fmaxf(mx, 0.f);
+        const float corr = fast_exp2(-d);
+  #pragma unroll
+        for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+        l_run *= corr;
+        m_run += d;
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) nxt[kb] -= d;
+        mneg = -m_run;
+      }
+    };
+    auto general = [&](int t, auto edge_tag) {
+      const int par = t & 1;
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
+      if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
+      u32x4 hi[C::NKB][2], lo[C::NKB][2];
+      probs(sa, hi, lo, edge_tag, split_p);
+      pv(Vring + par * C::TILE, hi, lo, split_p);
+      if (t + 1 < ntiles) {
+        qk(Kring + (par ^ 1) * C::TILE, sa);
+        update_max(t + 1 < n_int ? tile_max(t + 1, sa, std::false_type{})
+                                 : tile_max(t + 1, sa, std::true_type{}));
+      }
+    };
+    int t = 0;
+    if constexpr (D <= 128) {
+      const int n_steady = split_p || (kRel && !pre) ? 0 : max(0, min(n_int - 1, ntiles - 2));
+      if (kRel && n_steady > 0) {
+        // tile 0 was interior, so m_run is finite
+        mneg = -m_run;
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += mneg;
+      }
+      for (; t + 1 < n_steady; t += 2) {
+        steady(t, std::integral_constant<int, 0>{}, sa, sb);
+        steady(t + 1, std::integral_constant<int, 1>{}, sb, sa);
+      }
+      if (t < n_steady) {
+        steady(t, std::integral_constant<int, 0>{}, sa, sb);
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
+        ++t;
+      }
+      if (kRel && n_steady > 0) {
+  #pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += m_run;
+      }
+    }
+    for (; t < n_int; ++t) general(t, std::false_type{});
+    for (; t < ntiles; ++t) general(t, std::true_type{});
   }
-  // steady state (tiles t, t+1 interior, tile t+2 exists, single bf16 P): no
-  // branch between the barrier and the max update, stage offsets fixed by
-  // the parity of t, so matrix-core and VALU work of the two tiles interleave
-  auto steady = [&](int t, auto par_tag, f32x16* cur, f32x16* nxt) {
-    constexpr int PAR = decltype(par_tag)::value;
-    wait_vmcnt<0>();
-    lds_barrier();
-    issue_v(t + 1, Vring + (PAR ^ 1) * C::TILE);
-    issue_k(t + 2, Kring + PAR * C::TILE);
-    const float mx = steady_slots(Kring + (PAR ^ 1) * C::TILE, Vring + PAR * C::TILE, cur, nxt);
-    if constexpr (!kRel) {
-      update_max(mx);
-    } else if (__any(mx > kRescaleSlack)) {
-      // update_max in relative units; S'(t+1) follows the moved max
-      const float d = fmaxf(mx, 0.f);
-      const float corr = fast_exp2(-d);
-#pragma unroll
-      for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
-      l_run *= corr;
-      m_run += d;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) nxt[kb] -= d;
-      mneg = -m_run;
-    }
-  };
-  auto general = [&](int t, auto edge_tag) {
-    const int par = t & 1;
-    wait_vmcnt<0>();
-    lds_barrier();
-    if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
-    if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
-    u32x4 hi[C::NKB][2], lo[C::NKB][2];
-    probs(sa, hi, lo, edge_tag, split_p);
-    pv(Vring + par * C::TILE, hi, lo, split_p);
-    if (t + 1 < ntiles) {
-      qk(Kring + (par ^ 1) * C::TILE, sa);
-      update_max(t + 1 < n_int ? tile_max(t + 1, sa, std::false_type{})
-                               : tile_max(t + 1, sa, std::true_type{}));
-    }
-  };
-  int t = 0;
-  if constexpr (D <= 128) {
-    const int n_steady = split_p || (kRel && !pre) ? 0 : max(0, min(n_int - 1, ntiles - 2));
-    if (kRel && n_steady > 0) {
-      // tile 0 was interior, so m_run is finite
-      mneg = -m_run;
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += mneg;
-    }
-    for (; t + 1 < n_steady; t += 2) {
-      steady(t, std::integral_constant<int, 0>{}, sa, sb);
-      steady(t + 1, std::integral_constant<int, 1>{}, sb, sa);
-    }
-    if (t < n_steady) {
-      steady(t, std::integral_constant<int, 0>{}, sa, sb);
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
-      ++t;
-    }
-    if (kRel && n_steady > 0) {
-#pragma unroll
-      for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += m_run;
-    }
-  }
-  for (; t < n_int; ++t) general(t, std::false_type{});
-  for (; t < ntiles; ++t) general(t, std::true_type{});
 
   // ---- epilogue (padding rows see no key) ----
   float l_tot = sum_xor32(l_run);
