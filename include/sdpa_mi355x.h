@@ -218,8 +218,9 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_split
  * dK and dV of a KV head sum over the
  * Hq / Hkv query heads that read it.  The mask is a constant (no gradient).
  * Padding rows (past seqlens_q[b]) get dQ = 0, padding keys dK = dV = 0.
- * Supported: dtype F16 or BF16; D (q, k, dq, dk) and Dv (v, o, dout, dv) any
- * multiples of 8 up to 128, as in the forward.  dq, dk, dv are written in
+ * Supported: dtype F32, F16 or BF16; D (q, k, dq, dk) and Dv (v, o, dout, dv)
+ * any multiples of 8 up to 128, as in the forward.  F32 runs fp32 matrix
+ * cores and takes D_i = dO_i . O_i from its fp32 O for every row.  dq, dk, dv are written in
  * the input dtype with the layout rules of q, k, v (last dim contiguous,
  * 16-byte aligned pointers and strides); dsinks (optional, used only with
  * sinks) is fp32 [Hq].  The workspace (device memory, 16-byte aligned,

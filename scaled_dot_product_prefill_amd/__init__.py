@@ -294,7 +294,7 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
                      want_dsinks: bool = False, workspace: Optional[torch.Tensor] = None):
     """Gradients of prefill(q, k, v, ...) = o (with log-sum-exp ``lse``) for the
     upstream gradient ``dout``: returns (dq, dk, dv) or, with ``want_dsinks``,
-    (dq, dk, dv, dsinks).  fp16 / bf16 inputs, head dims (D of q, k; Dv of v)
+    (dq, dk, dv, dsinks).  fp32 / fp16 / bf16 inputs, head dims (D of q, k; Dv of v)
     multiples of 8 up to 128."""
     lib = library()
     q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)

@@ -274,7 +274,7 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
   int st = check_common(a);
   if (st != SDPA_OK) return st;
   if (!g) return fail(SDPA_ERR_NULL, "gradient arguments are NULL");
-  if (a->dtype == SDPA_F32) return fail(SDPA_ERR_UNSUPPORTED, "backward supports F16 and BF16 inputs");
+  const int es = a->dtype == SDPA_F32 ? 4 : 2;  // element bytes of every tensor
   const int kd = kernel_dim(a);
   if (kd != 64 && kd != 128)
     return fail(SDPA_ERR_UNSUPPORTED, "backward supports head dims up to 128, got D=%lld Dv=%lld", (long long)a->D,
@@ -288,14 +288,14 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
     if ((uintptr_t)ptrs[t] % 16 != 0) return fail(SDPA_ERR_ALIGN, "%s is not 16-byte aligned", names[t]);
     for (int d = 0; d < 3; ++d) {
       if (strides[t][d] < 0) return fail(SDPA_ERR_ARG, "%s stride %d is negative", names[t], d);
-      if ((strides[t][d] * 2) % 16 != 0)
+      if ((strides[t][d] * es) % 16 != 0)
         return fail(SDPA_ERR_ALIGN, "%s stride %d (%lld elements) is not a multiple of 16 bytes", names[t], d,
                     (long long)strides[t][d]);
     }
   }
-  if (g->dout_stride[2] * 2 > kMaxRowBytes)
+  if (g->dout_stride[2] * es > kMaxRowBytes)
     return fail(SDPA_ERR_UNSUPPORTED, "dout row stride above %lld bytes", (long long)kMaxRowBytes);
-  if (a->q_stride[2] * 2 > kMaxRowBytes)
+  if (a->q_stride[2] * es > kMaxRowBytes)
     return fail(SDPA_ERR_UNSUPPORTED, "q row stride above %lld bytes", (long long)kMaxRowBytes);
   if (g->dq_stride[2] < a->D || g->dk_stride[2] < a->D || g->dv_stride[2] < dv_of(a))
     return fail(SDPA_ERR_ARG, "gradient rows overlap (row stride below the head dim)");
@@ -306,20 +306,20 @@ int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, s
   if (ws_bytes < need) return fail(SDPA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
 
   // outputs: disjoint from each other, from every input and from the workspace
-  const Extent outs[4] = {tensor_extent(g->dq, g->dq_stride, a->B, a->Hq, a->Lq, a->D, 2),
-                          tensor_extent(g->dk, g->dk_stride, a->B, a->Hkv, a->Lk, a->D, 2),
-                          tensor_extent(g->dv, g->dv_stride, a->B, a->Hkv, a->Lk, dv_of(a), 2), Extent{}};
+  const Extent outs[4] = {tensor_extent(g->dq, g->dq_stride, a->B, a->Hq, a->Lq, a->D, es),
+                          tensor_extent(g->dk, g->dk_stride, a->B, a->Hkv, a->Lk, a->D, es),
+                          tensor_extent(g->dv, g->dv_stride, a->B, a->Hkv, a->Lk, dv_of(a), es), Extent{}};
   Extent eds;
   if (g->dsinks) { eds.lo = (uintptr_t)g->dsinks; eds.hi = eds.lo + a->Hq * 4; eds.valid = true; }
   Extent ews;
   ews.lo = (uintptr_t)ws; ews.hi = ews.lo + need; ews.valid = true;
   Extent ins[12];
   int n = 0;
-  ins[n++] = tensor_extent(a->q, a->q_stride, a->B, a->Hq, a->Lq, a->D, 2);
-  ins[n++] = tensor_extent(a->k, a->k_stride, a->B, a->Hkv, a->Lk, a->D, 2);
-  ins[n++] = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, dv_of(a), 2);
-  ins[n++] = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, dv_of(a), 2);
-  ins[n++] = tensor_extent(g->dout, g->dout_stride, a->B, a->Hq, a->Lq, dv_of(a), 2);
+  ins[n++] = tensor_extent(a->q, a->q_stride, a->B, a->Hq, a->Lq, a->D, es);
+  ins[n++] = tensor_extent(a->k, a->k_stride, a->B, a->Hkv, a->Lk, a->D, es);
+  ins[n++] = tensor_extent(a->v, a->v_stride, a->B, a->Hkv, a->Lk, dv_of(a), es);
+  ins[n++] = tensor_extent(a->o, a->o_stride, a->B, a->Hq, a->Lq, dv_of(a), es);
+  ins[n++] = tensor_extent(g->dout, g->dout_stride, a->B, a->Hq, a->Lq, dv_of(a), es);
   { Extent e; e.lo = (uintptr_t)a->lse; e.hi = e.lo + a->B * a->Hq * a->Lq * 4; e.valid = true; ins[n++] = e; }
   if (a->mask) {
     const int64_t last = (a->B - 1) * a->mask_stride[0] + (a->Hq - 1) * a->mask_stride[1] +

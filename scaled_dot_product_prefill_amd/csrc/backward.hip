@@ -1,4 +1,4 @@
-// Gradients of the prefill attention (fp16 / bf16 inputs; head dims D of q, k
+// Gradients of the prefill attention (fp32 / fp16 / bf16 inputs; head dims D of q, k
 // and Dv of v, o, any multiples of 8 up to 128, run at kernel dim 64 or 128
 // with the chunks past the real dims loaded as zero and never stored).
 //
@@ -568,17 +568,311 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_dsink_kernel(BwdParams bp) {
   if (threadIdx.x == 0) bp.dsinks[hq] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+// ---- fp32 inputs ---------------------------------------------------------------
+// fp32 matrix cores (32x32x2; one 16-byte operand vector holds four k-steps,
+// see mma32(TF32)).  Tiles of 32 rows are staged through registers into LDS,
+// single-buffered; the transposed copies the second products read are
+// written by the loading threads (no transposing LDS read exists for 32-bit
+// data).  D_i = dO_i . O_i from the fp32 O.  Layouts as in the 16-bit
+// kernels: in dQ lanes own queries (S^T = K Q^T), in dK / dV lanes own keys
+// (S = Q K^T); an accumulator's registers 4u .. 4u+3 (rows 8u + 4g + t) are
+// the B operand of k-group u, matched by transposed rows read at 8u + 4g.
+template <int D>
+struct F32T {
+  static constexpr int NCH = D / 4;        // 16-byte chunks per row
+  static constexpr int RP = D * 4 + 16;    // row-major pitch (bytes)
+  static constexpr int TP = 32 * 4 + 16;   // transposed pitch: 32 rows + pad
+  static constexpr int RBYTES = 32 * RP;
+  static constexpr int TBYTES = D * TP;
+  static constexpr int IT = 32 * NCH / kBwdThreads;  // 16-byte chunks per thread
+  static constexpr int NQ = NCH / 2;       // operand vectors per lane (chunk 2s + g)
+  static constexpr int NMB = D / 32;       // 32-row blocks of a transposed product
+  static_assert(IT >= 1 && 32 * NCH % kBwdThreads == 0, "tile split");
+};
+
+// Rows [r0, r0 + 32) of a [rows, D] fp32 matrix (rows >= nrows and columns >=
+// real_d as zero) into row-major and / or transposed LDS copies.
+template <int D>
+__device__ inline void f32_tile_load(const float* base, int64_t rs, int r0, int nrows, int real_d, uint8_t* dst_r,
+                                     uint8_t* dst_t, int tid) {
+  using L = F32T<D>;
+  u32x4 v[L::IT];
+#pragma unroll
+  for (int it = 0; it < L::IT; ++it) {
+    const int u = tid + kBwdThreads * it, row = u / L::NCH, c = u % L::NCH, r = r0 + row;
+    v[it] = r < nrows && 4 * c < real_d ? ldg16_cached(base + (int64_t)r * rs + 4 * c) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int it = 0; it < L::IT; ++it) {
+    const int u = tid + kBwdThreads * it, row = u / L::NCH, c = u % L::NCH;
+    if (dst_r) lds_write16(dst_r + row * L::RP + c * 16, v[it]);
+    if (dst_t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) *(uint32_t*)(dst_t + (4 * c + e) * L::TP + row * 4) = v[it][e];
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_f32_kernel(BwdParams bp) {
+  const AttnParams& p = bp.f;
+  using L = F32T<D>;
+  constexpr int NQ = L::NQ, NMB = L::NMB;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::RBYTES + L::TBYTES];  // K, V rows; K^T
+  uint8_t* const Ks = smem;
+  uint8_t* const Vs = smem + L::RBYTES;
+  uint8_t* const Kt = smem + 2 * L::RBYTES;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  const int nqt = (p.Lq + 127) / 128;
+  int qt, bh;
+  prefill_tile((int)blockIdx.x, (int)gridDim.x, nqt, p.B * p.Hq, CAUSAL, qt, bh);
+  const int b = bh / p.Hq, hq = bh % p.Hq, hk = hq / p.group;
+  const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
+  const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
+  const int coff = lk - lq;
+  const int i0 = qt * 128;
+  const int my_i = i0 + 32 * wave + l32;
+  const bool ok = my_i < lq;
+  const float c = p.scale_log2;
+
+  // this lane's query row: Q and dO as B operands; D_i = dO_i . O_i
+  u32x4 qreg[NQ], doreg[NQ];
+  float dsum = 0.f;
+  {
+    const int ii = ok ? my_i : 0;
+    const float* qr = (const float*)p.q + b * p.qs[0] + hq * p.qs[1] + (int64_t)ii * p.qs[2];
+    const float* dr = (const float*)bp.dout + b * bp.dos[0] + hq * bp.dos[1] + (int64_t)ii * bp.dos[2];
+    const float* orow = (const float*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)ii * p.os[2];
+    const int nq = p.Dqk / 4, nd = p.Dv / 4;  // real 16-byte chunks; the rest is zero
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const int ch = 2 * s + g;
+      const u32x4 a = ldg16_cached(qr + min(ch, nq - 1) * 4), d = ldg16_cached(dr + min(ch, nd - 1) * 4);
+      const u32x4 o = ldg16_cached(orow + min(ch, nd - 1) * 4);
+      qreg[s] = ok && ch < nq ? a : u32x4{0, 0, 0, 0};
+      doreg[s] = ok && ch < nd ? d : u32x4{0, 0, 0, 0};
+      if (ok && ch < nd) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dsum = fmaf(as_float(o[e]), as_float(d[e]), dsum);
+      }
+    }
+  }
+  const float dval = ok ? sum_xor32(dsum) : 0.f;
+  const int64_t wrow = ((int64_t)b * p.Hq + hq) * p.Lq + (ok ? my_i : 0);
+  const float lse2 = ok ? bp.ws_l[wrow] : __builtin_inff();
+  if (my_i < p.Lq && g == 0) bp.ws_d[((int64_t)b * p.Hq + hq) * p.Lq + my_i] = dval;
+
+  int kend = i0 < lq ? lk : 0;
+  if (CAUSAL) kend = min(kend, min(i0 + 128, lq) + coff);
+  const int ntiles = kend > 0 ? (kend + 31) / 32 : 0;
+  const float* kbase = (const float*)p.k + b * p.ks[0] + hk * p.ks[1];
+  const float* vbase = (const float*)p.v + b * p.vs[0] + hk * p.vs[1];
+
+  f32x16 acc[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x16{};
+  for (int t = 0; t < ntiles; ++t) {
+    const int j0 = 32 * t;
+    __syncthreads();  // the previous tile is no longer read
+    f32_tile_load<D>(kbase, p.ks[2], j0, lk, p.Dqk, Ks, Kt, tid);
+    f32_tile_load<D>(vbase, p.vs[2], j0, lk, p.Dv, Vs, nullptr, tid);
+    __syncthreads();
+    // S^T and dP^T (m = key j0 + lane row, n = query)
+    f32x16 st = f32x16{}, dpt = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      st = mma32(TF32{}, lds_read16(Ks + l32 * L::RP + (2 * s + g) * 16), qreg[s], st);
+      dpt = mma32(TF32{}, lds_read16(Vs + l32 * L::RP + (2 * s + g) * 16), doreg[s], dpt);
+    }
+    f32x16 ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = j0 + 8 * (r >> 2) + 4 * g + (r & 3);
+      float x = st[r] * c;
+      if (MASK) {
+        const int ii = ok ? my_i : 0, jj = j < lk ? j : lk - 1;
+        x += kLog2e * mask_val(p.mask, p.mask_bool,
+                               b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
+      }
+      const bool vis = ok && j < lk && (!CAUSAL || j <= my_i + coff);
+      const float pr = vis ? fast_exp2(x - lse2) : 0.f;
+      ds[r] = pr * (dpt[r] - dval);
+    }
+    // dQ^T += K^T dS^T: k-group u holds keys 8u + 4g + (0..3)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 bv = {as_uint(ds[4 * u]), as_uint(ds[4 * u + 1]), as_uint(ds[4 * u + 2]), as_uint(ds[4 * u + 3])};
+        acc[mb] = mma32(TF32{}, lds_read16(Kt + (32 * mb + l32) * L::TP + (8 * u + 4 * g) * 4), bv, acc[mb]);
+      }
+  }
+
+  if (my_i < p.Lq) {
+    float* orow = (float*)bp.dq + b * bp.dqs[0] + hq * bp.dqs[1] + (int64_t)my_i * bp.dqs[2];
+    const float sc = bp.scale;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * mb + 8 * q4 + 4 * g;
+        if (d0 < p.Dqk)
+          *(f32x4*)(orow + d0) = f32x4{acc[mb][4 * q4] * sc, acc[mb][4 * q4 + 1] * sc, acc[mb][4 * q4 + 2] * sc,
+                                       acc[mb][4 * q4 + 3] * sc};
+      }
+  }
+}
+
+template <int D, bool CAUSAL, bool MASK>
+__global__ __launch_bounds__(kBwdThreads, 1) void bwd_dkv_f32_kernel(BwdParams bp) {
+  const AttnParams& p = bp.f;
+  using L = F32T<D>;
+  constexpr int NQ = L::NQ, NMB = L::NMB;
+  // Q, dO rows; Q^T, dO^T; the tile's LSE (log2 units) and D
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * L::RBYTES + 2 * L::TBYTES + 256];
+  uint8_t* const Qs = smem;
+  uint8_t* const Ds = smem + L::RBYTES;
+  uint8_t* const Qt = smem + 2 * L::RBYTES;
+  uint8_t* const Dt = Qt + L::TBYTES;
+  float* const Ls = (float*)(Dt + L::TBYTES);
+  float* const Dd = Ls + 32;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+  // key blocks in increasing order: under causal masking the first key
+  // blocks are seen by the most query rows, so the heaviest go first
+  const int nbh = p.B * p.Hkv;
+  const int kt = (int)blockIdx.x / nbh, bhk = (int)blockIdx.x % nbh;
+  const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+  const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
+  const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
+  const int coff = lk - lq;
+  const int k0 = kt * 128;
+  const int kw0 = k0 + 32 * wave;
+  const int my_j = kw0 + l32;
+  const bool kok = my_j < lk;
+  const float c = p.scale_log2;
+
+  // this lane's key and value rows as B operands (zero past the real dims)
+  u32x4 kreg[NQ], vreg[NQ];
+  {
+    const int jj = kok ? my_j : 0;
+    const float* kr = (const float*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)jj * p.ks[2];
+    const float* vr = (const float*)p.v + b * p.vs[0] + hk * p.vs[1] + (int64_t)jj * p.vs[2];
+    const int nk = p.Dqk / 4, nv = p.Dv / 4;
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      const int ch = 2 * s + g;
+      const u32x4 a = ldg16_cached(kr + min(ch, nk - 1) * 4), d = ldg16_cached(vr + min(ch, nv - 1) * 4);
+      kreg[s] = kok && ch < nk ? a : u32x4{0, 0, 0, 0};
+      vreg[s] = kok && ch < nv ? d : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // query tiles [qt0, nqt) of 32 rows, for every query head of the group
+  const int ibeg = CAUSAL ? max(0, k0 - coff) : 0;
+  const int qt0 = ibeg / 32;
+  const int nqt = k0 < lk ? (lq + 31) / 32 : 0;
+  const int per_head = max(0, nqt - qt0);
+  const int ntiles = per_head * p.group;
+
+  f32x16 dk[NMB], dv[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) dk[mb] = dv[mb] = f32x16{};
+  for (int t = 0; t < ntiles; ++t) {
+    const int hq = hk * p.group + t % p.group;
+    const int q0 = 32 * (qt0 + t / p.group);
+    __syncthreads();  // the previous tile is no longer read
+    const float* qb = (const float*)p.q + b * p.qs[0] + hq * p.qs[1];
+    const float* db = (const float*)bp.dout + b * bp.dos[0] + hq * bp.dos[1];
+    f32_tile_load<D>(qb, p.qs[2], q0, lq, p.Dqk, Qs, Qt, tid);
+    f32_tile_load<D>(db, bp.dos[2], q0, lq, p.Dv, Ds, Dt, tid);
+    if (tid < 32) {
+      const int i = q0 + tid;
+      const int64_t row = ((int64_t)b * p.Hq + hq) * p.Lq + (i < p.Lq ? i : 0);
+      Ls[tid] = i < lq ? bp.ws_l[row] : __builtin_inff();
+      Dd[tid] = i < lq ? bp.ws_d[row] : 0.f;
+    }
+    __syncthreads();
+    // nothing of this wave's keys is visible to the tile's rows
+    if (kw0 >= lk || (CAUSAL && kw0 > q0 + 31 + coff)) continue;
+    // S and dP (m = query q0 + lane row, n = key)
+    f32x16 s_ = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int s = 0; s < NQ; ++s) {
+      s_ = mma32(TF32{}, lds_read16(Qs + l32 * L::RP + (2 * s + g) * 16), kreg[s], s_);
+      dp = mma32(TF32{}, lds_read16(Ds + l32 * L::RP + (2 * s + g) * 16), vreg[s], dp);
+    }
+    f32x16 pr, ds;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ir = 8 * (r >> 2) + 4 * g + (r & 3), i = q0 + ir;
+      float x = s_[r] * c;
+      if (MASK) {
+        const int ii = i < lq ? i : lq - 1, jj = kok ? my_j : lk - 1;
+        x += kLog2e * mask_val(p.mask, p.mask_bool,
+                               b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
+      }
+      const bool vis = kok && i < lq && (!CAUSAL || my_j <= i + coff);
+      pr[r] = vis ? fast_exp2(x - Ls[ir]) : 0.f;
+      ds[r] = pr[r] * (dp[r] - Dd[ir]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS: k-group u holds rows 8u + 4g + (0..3)
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4 pb = {as_uint(pr[4 * u]), as_uint(pr[4 * u + 1]), as_uint(pr[4 * u + 2]), as_uint(pr[4 * u + 3])};
+        const u32x4 db = {as_uint(ds[4 * u]), as_uint(ds[4 * u + 1]), as_uint(ds[4 * u + 2]), as_uint(ds[4 * u + 3])};
+        const int off = (32 * mb + l32) * L::TP + (8 * u + 4 * g) * 4;
+        dv[mb] = mma32(TF32{}, lds_read16(Dt + off), pb, dv[mb]);
+        dk[mb] = mma32(TF32{}, lds_read16(Qt + off), db, dk[mb]);
+      }
+  }
+
+  if (my_j < p.Lk) {
+    float* kr = (float*)bp.dk + b * bp.dks[0] + hk * bp.dks[1] + (int64_t)my_j * bp.dks[2];
+    float* vr = (float*)bp.dv + b * bp.dvs[0] + hk * bp.dvs[1] + (int64_t)my_j * bp.dvs[2];
+    const float sc = bp.scale;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * mb + 8 * q4 + 4 * g;
+        if (d0 < p.Dqk)
+          *(f32x4*)(kr + d0) = f32x4{dk[mb][4 * q4] * sc, dk[mb][4 * q4 + 1] * sc, dk[mb][4 * q4 + 2] * sc,
+                                     dk[mb][4 * q4 + 3] * sc};
+        if (d0 < p.Dv)
+          *(f32x4*)(vr + d0) = f32x4{dv[mb][4 * q4], dv[mb][4 * q4 + 1], dv[mb][4 * q4 + 2], dv[mb][4 * q4 + 3]};
+      }
+  }
+}
+
 template <class T, int D, bool CAUSAL, bool MASK>
 hipError_t launch_main(const BwdParams& bp, hipStream_t s) {
   const AttnParams& p = bp.f;
   const dim3 block(kBwdThreads);
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, MASK>), dim3((unsigned)((p.Lq + 127) / 128 * p.B * p.Hq)),
-                     block, 0, s, bp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, MASK>),
-                     dim3((unsigned)((p.Lk + kDkvKeys - 1) / kDkvKeys * p.B * p.Hkv)), dim3(kDkvThreads), 0, s, bp);
-  return hipGetLastError();
+  if constexpr (std::is_same<T, TF32>::value) {
+    hipLaunchKernelGGL((bwd_dq_f32_kernel<D, CAUSAL, MASK>), dim3((unsigned)((p.Lq + 127) / 128 * p.B * p.Hq)),
+                       block, 0, s, bp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkv_f32_kernel<D, CAUSAL, MASK>), dim3((unsigned)((p.Lk + 127) / 128 * p.B * p.Hkv)),
+                       block, 0, s, bp);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, CAUSAL, MASK>), dim3((unsigned)((p.Lq + 127) / 128 * p.B * p.Hq)),
+                       block, 0, s, bp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, MASK>),
+                       dim3((unsigned)((p.Lk + kDkvKeys - 1) / kDkvKeys * p.B * p.Hkv)), dim3(kDkvThreads), 0, s, bp);
+    return hipGetLastError();
+  }
 }
 
 template <class T, int D>
@@ -627,7 +921,11 @@ hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float sc
   bp.ws_d = ws;
   bp.ws_l = ws + nrows;
   if (p.sinks == nullptr) bp.dsinks = nullptr;
-  return dtype == SDPA_BF16 ? launch_t<TBF16>(bp, causal, s) : launch_t<TF16>(bp, causal, s);
+  switch (dtype) {
+    case SDPA_F32: return launch_t<TF32>(bp, causal, s);
+    case SDPA_F16: return launch_t<TF16>(bp, causal, s);
+    default: return launch_t<TBF16>(bp, causal, s);
+  }
 }
 
 }  // namespace sdpa

@@ -266,7 +266,8 @@ def _bwd(lib, ws=1 << 45, ws_bytes=1 << 30, gkw=None, **kw):
 
 def test_backward_validation(lib):
     assert _bwd(lib) == S.OK
-    assert _bwd(lib, dtype=sdpa.F32) == S.ERR_UNSUPPORTED
+    assert _bwd(lib, dtype=sdpa.F32) == S.OK                      # fp32 matrix cores
+    assert _bwd(lib, dtype=sdpa.F32, gkw={"dq_stride": (8 * 64 * 128, 64 * 128, 130)}) == S.ERR_ALIGN
     assert _bwd(lib, D=96) == S.OK                               # runs at kernel dim 128
     assert _bwd(lib, Dv=64) == S.OK                              # D = 128, Dv = 64
     assert _bwd(lib, D=100) == S.ERR_UNSUPPORTED                 # not a multiple of 8

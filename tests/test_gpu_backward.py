@@ -2,14 +2,15 @@
 ABI) against the fp64 gradient oracle: a grid of small cases spanning several
 tiles with ragged tails (GQA, bottom-right causal with Lq != Lk, rows without
 keys, additive mask with -inf entries, sinks and their gradient, per-batch
-lengths with NaN in the padding) for fp16 / bf16 and D = 64 / 128, head dims
+lengths with NaN in the padding) for fp32 / fp16 / bf16 and D = 64 / 128, head dims
 that are multiples of 8 up to 128 with Dv != D, plus the
 autograd wrapper.
 
 Tolerance: gradients are linear in dO, so the forward's elementwise bound
 (abs 2e-3, rel 1e-2 for 16-bit inputs) is applied with the absolute part
 scaled by the tensor's largest reference magnitude (at least 1):
-|got - ref| <= 2e-3 * max(1, max|ref|) + 1e-2 * |ref|.  The kernels round P
+|got - ref| <= 2e-3 * max(1, max|ref|) + 1e-2 * |ref| (fp32: 1e-5 * max(1, max|ref|),
+the forward's fp32 bound scaled the same way).  The 16-bit kernels round P
 and dS to the input type (unit roundoff 2^-11 fp16, 2^-8 bf16) before the
 second products and accumulate in fp32, which stays inside this bound."""
 import math
@@ -26,18 +27,19 @@ from workloads import DTYPES, random_case
 pytestmark = pytest.mark.gpu
 
 
-def _report(got, ref, what):
+def _report(got, ref, what, dtype="bf16"):
     ref = np.asarray(ref, dtype=np.float64)
     s = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
-    rep = allclose_report(got.float().cpu().numpy(), ref, 2e-3 * s, 1e-2)
-    ok = rep["ok"] and rep["norm_rel"] <= 1e-2
+    atol, rtol, nrel = (1e-5, 0.0, 1e-5) if dtype == "fp32" else (2e-3, 1e-2, 1e-2)
+    rep = allclose_report(got.float().cpu().numpy(), ref, atol * s, rtol)
+    ok = rep["ok"] and rep["norm_rel"] <= nrel
     say(f"  {what}: max_abs={rep['max_abs']:.3e} (scale {s:.3g}) norm_rel={rep['norm_rel']:.3e} ok={ok}")
     return None if ok else f"{what}: {rep}"
 
 
-def _check_all(pairs):
+def _check_all(pairs, dtype="bf16"):
     """Report every gradient, then fail on the first mismatch."""
-    bad = [m for m in (_report(g, r, w) for g, r, w in pairs) if m]
+    bad = [m for m in (_report(g, r, w, dtype) for g, r, w in pairs) if m]
     assert not bad, bad
 
 
@@ -70,7 +72,7 @@ GRID = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("case", range(len(GRID)))
 def test_backward_grid(dtype, D, case):
@@ -87,7 +89,7 @@ def test_backward_grid(dtype, D, case):
         pairs.append((ds, rs, "dsinks"))
     else:
         assert ds is None
-    _check_all(pairs)
+    _check_all(pairs, dtype)
 
 
 # (D, Dv): head dims that are multiples of 8 up to 128, run at kernel dim 64
@@ -95,7 +97,7 @@ def test_backward_grid(dtype, D, case):
 BWD_DIMS = [(8, 8), (40, 40), (96, 96), (112, 112), (128, 64), (64, 120)]
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 @pytest.mark.parametrize("dims", BWD_DIMS, ids=lambda d: f"{d[0]}x{d[1]}")
 @pytest.mark.parametrize("causal", [False, True])
 def test_backward_head_dims(dtype, dims, causal):
@@ -111,10 +113,10 @@ def test_backward_head_dims(dtype, dims, causal):
     pairs = [(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")]
     if causal:
         pairs.append((ds, rs, "dsinks"))
-    _check_all(pairs)
+    _check_all(pairs, dtype)
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_backward_seqlens(dtype):
     B, Hq, Hkv, Lq, Lk, D = 3, 4, 2, 300, 333, 128
     sq, sk = [300, 129, 0], [333, 200, 3]
@@ -131,7 +133,7 @@ def test_backward_seqlens(dtype):
     (dq, dk, dv, ds), sc = _run(y, dpad, dtype, True, sq, sk, want_dsinks=True)
     rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
                                              sinks=x["sinks"], seqlens_q=np.array(sq), seqlens_k=np.array(sk))
-    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")])
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
 
 
 def test_autograd_wrapper_matches_entry_point():
@@ -151,7 +153,7 @@ def test_autograd_wrapper_matches_entry_point():
 
 
 def test_backward_rejects_unsupported():
-    x = to_dev(random_case(5300, 1, 2, 2, 8, 8, 64, "fp32"))
+    x = to_dev(random_case(5300, 1, 2, 2, 8, 8, 136, "fp16"))   # head dim above 128
     o, lse = sdpa.prefill(x["q"], x["k"], x["v"], return_lse=True)
     with pytest.raises(sdpa.SdpaError) as e:
         sdpa.prefill_backward(x["q"], x["k"], x["v"], o, lse, o)
@@ -179,7 +181,7 @@ def test_causal_full_size_sampled_heads():
                     (dv[:, sl], rv, f"dv head {h}")])
 
 
-@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
 def test_backward_bool_mask(dtype):
     B, Hq, Hkv, Lq, Lk, D = 1, 4, 2, 200, 190, 128
     x = random_case(5400, B, Hq, Hkv, Lq, Lk, D, dtype, sinks=True, sink_scale=2.0)
@@ -190,4 +192,4 @@ def test_backward_bool_mask(dtype):
     (dq, dk, dv, ds), sc = _run(x, dout, dtype, True, want_dsinks=True)
     rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
                                              mask=x["mask"], sinks=x["sinks"])
-    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")])
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
