@@ -569,9 +569,11 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
 #pragma unroll
   for (int i = 0; i < NOB; ++i) acc[i] = f32x4{};
   float m_run = kNegInf, l_run = 0.f;
-  // bf16 P goes in as hi + lo: always in decode (the matrix cores have ample
-  // headroom in this bandwidth-bound kernel); in prefill where rows may see
-  // few keys (at most 256, or any row under a mask), as in the prefill kernel
+  // bf16 P goes in as hi + lo: always with one shared block (CPW = 1: the
+  // matrix cores have ample headroom in this bandwidth-bound form); with
+  // CPW > 1, where the products double per wave, only on workgroups whose rows
+  // may see few keys (at most 256 in this split, or any row under a mask), as
+  // in the prefill kernel
   const bool split_p = std::is_same<T, TBF16>::value && (CPW == 1 || MASK || kend - kbeg <= 256);
 
   // mask values for tile t, loaded one tile ahead
