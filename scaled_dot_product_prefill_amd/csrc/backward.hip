@@ -118,7 +118,8 @@ __device__ inline void tile_issue(const uint16_t* base, int64_t rs, int r0, int 
   const uint16_t* tb = base + (int64_t)r0 * rs;
   const int rows = min(nrows - r0, L::ROWS);
   const uint32_t rowb = (uint32_t)(rs * 2);
-  const uint32_t nb = (uint32_t)(rows - 1) * rowb + (uint32_t)real_d * 2;
+  // no rows: a zero range, so that even the kNoLoad lanes read nothing
+  const uint32_t nb = rows > 0 ? (uint32_t)(rows - 1) * rowb + (uint32_t)real_d * 2 : 0u;
 #pragma unroll
   for (int i = 0; i < L::LPW; ++i)
     dma16(tb, nb, lds + (wave + NW * i) * 1024, off, i * L::STEP_ROWS * rowb);
@@ -452,7 +453,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
     } else {
       // query tiles qt0 .. qs - 1 hold a row that sees at most 256 keys
       const int qs = CAUSAL ? (lk <= 256 ? nqt : min(nqt, max(qt0, (256 - coff) / 64 + 1))) : (lk <= 256 ? nqt : qt0);
-      n_split = (qs - qt0) * p.group;
+      // a key block past this batch's keys has nqt = 0 < qt0: no tiles at all
+      n_split = max(0, qs - qt0) * p.group;
     }
   }
   auto run = [&](int t_begin, int t_end, auto split_tag) {

@@ -136,6 +136,22 @@ def test_backward_seqlens(dtype):
     _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_backward_seqlens_keys_end_early(dtype):
+    """Per-batch key lengths that end several 256-key blocks before Lk, under
+    causal masking: those key blocks have no query tile at all while their
+    first visible query tile lies past the batch's queries, and must load
+    nothing.  D = 104 leaves chunks past the real head dim in every row."""
+    B, Hq, Hkv, Lq, Lk, D = 3, 8, 2, 200, 1100, 104
+    sq, sk = [200, 66, 133], [1100, 962, 404]
+    x = random_case(5150, B, Hq, Hkv, Lq, Lk, D, dtype, sinks=True, sink_scale=2.0)
+    dout = _dout(5150, x["q"].shape, dtype)
+    (dq, dk, dv, ds), sc = _run(x, dout, dtype, True, sq, sk, want_dsinks=True)
+    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+                                             sinks=x["sinks"], seqlens_q=np.array(sq), seqlens_k=np.array(sk))
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
+
+
 def test_autograd_wrapper_matches_entry_point():
     x = to_dev(random_case(5200, 2, 4, 2, 150, 150, 64, "bf16", sinks=True))
     q, k, v = (x[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
