@@ -19,7 +19,7 @@ from workloads import DTYPES, random_case
 
 pytestmark = pytest.mark.gpu
 
-N_PREFILL, N_DECODE, N_BACKWARD = 24, 16, 12
+N_PREFILL, N_DECODE, N_BACKWARD = 48, 32, 32
 
 
 def _draw(seed, decode=False, backward=False):
