@@ -24,6 +24,9 @@ long_decode_bf16|<gqa8 decode name>|mq4_gqa8_decode_b1_lk32768_fp16 (multi-query
 kvcache_ragged_decode_bf16 (KV cache with per-batch fill levels; GB/s over the filled part)|
 causal_bf16_bwd (gradients of the causal prefill; 10*D flops per visible pair)|
 causal_gqa8_d512_bf16 (prefill at head dim 512, GQA-8).
+``drift`` is the median of the last 8 step times over that of the first 7
+(a run outside 1 +- ``gate`` drifted and should be repeated); ``env`` records
+the GPU, the torch / HIP versions and the sha256 of the loaded library.
 --cold makes every decode call read K and V from HBM: the calls rotate over
 copies totalling more than 1 GiB (the GQA-8 shapes of 64 MiB and less fit in
 the 256 MiB last-level cache and otherwise run from it).
@@ -75,6 +78,24 @@ def decode_bytes(w) -> int:
     qo = 2 * w.B * w.Hq * w.Lq * w.D * es
     mask = 4 * w.B * w.Lk if w.mask else 0
     return kv + qo + mask
+
+
+def drift(samples):
+    """Median of the last 8 per-step times over the median of the first 7 (in
+    the order they ran): a clock or thermal drift across the timed region shows
+    as a ratio away from 1.  None for fewer than 15 steps."""
+    if len(samples) < 15:
+        return None
+    med = lambda xs: sorted(xs)[len(xs) // 2]
+    return round(med(samples[-8:]) / med(samples[:7]), 4)
+
+
+def file_sha256(path: str):
+    try:
+        with open(path, "rb") as f:
+            return hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
 
 
 def source_hash() -> str:
@@ -173,24 +194,30 @@ def cpu_baseline_decode(w, budget_s: float = 8.0):
     es = 4 if w.dtype == "fp32" else 2
     units = [(b, hk) for b in range(w.B) for hk in range(w.Hkv)]
     fill = w.seqlens_k()
-    for b, hk in units:
-        q = torch.stack([workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, hk * G + i, w.Lq, w.D, dt)
-                         for i in range(G)])[None]
-        k = workloads.slice_normal(w.cfg_id, workloads.TENSOR_K, b, hk, w.Lk, w.D, dt)[None, None]
-        v = workloads.slice_normal(w.cfg_id, workloads.TENSOR_V, b, hk, w.Lk, w.D, dt)[None, None]
-        mask = workloads.tail_mask(1, w.Lk) if w.mask else None
-        sk = None if fill is None else fill[b:b + 1]
-        t0 = time.perf_counter()
-        sdpa_reference(q, k, v, scale=w.scale, causal=w.causal, mask=mask, seqlens_k=sk)
-        t_used += time.perf_counter() - t0
-        done += 1
-        keys = w.Lk if fill is None else int(fill[b])
-        nbytes += 2 * keys * w.D * es + 2 * G * w.Lq * w.D * es + (4 * w.Lk if w.mask else 0)
-        if t_used >= budget_s:
-            break
+    passes = 0
+    # whole passes over the groups until at least 1 s of oracle time (small
+    # shapes), or the budget within a pass (large ones)
+    while t_used < 1.0 and done < len(units) * 1000:
+        passes += 1
+        for b, hk in units:
+            q = torch.stack([workloads.slice_normal(w.cfg_id, workloads.TENSOR_Q, b, hk * G + i, w.Lq, w.D, dt)
+                             for i in range(G)])[None]
+            k = workloads.slice_normal(w.cfg_id, workloads.TENSOR_K, b, hk, w.Lk, w.D, dt)[None, None]
+            v = workloads.slice_normal(w.cfg_id, workloads.TENSOR_V, b, hk, w.Lk, w.D, dt)[None, None]
+            mask = workloads.tail_mask(1, w.Lk) if w.mask else None
+            sk = None if fill is None else fill[b:b + 1]
+            t0 = time.perf_counter()
+            sdpa_reference(q, k, v, scale=w.scale, causal=w.causal, mask=mask, seqlens_k=sk)
+            t_used += time.perf_counter() - t0
+            done += 1
+            keys = w.Lk if fill is None else int(fill[b])
+            nbytes += 2 * keys * w.D * es + 2 * G * w.Lq * w.D * es + (4 * w.Lk if w.mask else 0)
+            if t_used >= budget_s:
+                break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    per = f"{passes} passes over all {len(units)}" if passes > 1 else f"{done} of {len(units)}"
     return {"value": nbytes / t_used / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {len(units)} (batch, KV head) groups of {w.name}, fp64 numpy, {t_used:.1f} s"}
+            "sample": f"{per} (batch, KV head) groups of {w.name}, fp64 numpy, {t_used:.1f} s"}
 
 
 class Timed:
@@ -325,6 +352,10 @@ def main():
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic (seeded N(0,1), see workloads/)"}
+    res["env"] = {"gpu": torch.cuda.get_device_name(dev), "torch": torch.__version__, "hip": torch.version.hip,
+                  "library_sha256": file_sha256(sdpa.library_path), "source_hash": source_hash()}
+    res["drift"] = {"prefill": drift(tp.ms()) if tp else None, "decode": drift(td.ms()) if td else None,
+                    "gate": 0.05}
     cfg = {}
     if P is not None:
         pm = sorted(tp.ms())

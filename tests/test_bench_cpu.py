@@ -60,3 +60,10 @@ def test_traffic_from_other_sources_is_not_reported(monkeypatch):
     monkeypatch.setattr(bench, "source_hash", lambda: "0" * 16)
     assert bench.load_traffic("prefill_dit_fp16") is None
     assert bench.load_traffic("no_such_kernel") is None
+
+
+def test_drift_ratio():
+    # first 7 steps at 1.0 ms, last 8 at 1.1 ms: a 10 % slow-down across the run
+    assert bench.drift([1.0] * 7 + [1.1] * 8) == pytest.approx(1.1)
+    assert bench.drift([2.0] * 30) == 1.0
+    assert bench.drift([1.0] * 14) is None
