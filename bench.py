@@ -330,21 +330,25 @@ def main():
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    # A short call (a decode step, a small prefill) can take less GPU time
-    # than its submission through Python, which would leave the GPU idle
-    # between a start event and the kernels; and after the synchronisation
-    # above the first timed calls would start on an idle GPU.  A bounded spin
-    # kernel queued first lets the host run ahead, so the timed calls execute
-    # back to back; its own duration is taken out of the wall-clock step time.
-    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    r0.record()
-    torch.cuda._sleep(2_000_000 * max(1, args.steps // 10))
-    r1.record()
+    runway_ms = 0.0
+    if P is None:
+        # A decode call can take less GPU time than its submission through
+        # Python, which would leave the GPU idle between the start event and
+        # the kernels.  A bounded spin kernel queued first lets the host run
+        # ahead, so the timed calls execute back to back; its own duration is
+        # taken out of the wall-clock step time below.  (Prefill steps keep
+        # the GPU busy by themselves; measured with the spin in front, their
+        # first steps ran slower while the clock recovered.)
+        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        r0.record()
+        torch.cuda._sleep(2_000_000 * max(1, args.steps // 10))
+        r1.record()
     for i in range(args.steps):
         step(tp, td, i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    runway_ms = r0.elapsed_time(r1)
+    if P is None:
+        runway_ms = r0.elapsed_time(r1)
     ms_step = (wall * 1e3 - runway_ms) / args.steps
 
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
