@@ -1,5 +1,6 @@
 """GPU parity of the prefill kernel (sdpa_prefill through the C ABI) against the
-fp64 oracle: the tiny, DiT and causal workloads at full size (sampled rows),
+fp64 oracle: the tiny, DiT and causal workloads at full size (every row of
+every head),
 a grid of small cases spanning several tiles with ragged tails, and the
 edge cases of the method (empty rows, fully masked rows, sinks, GQA,
 non-contiguous layouts, one key)."""
@@ -83,25 +84,28 @@ def _full_size(w, heads, rows):
     compare_sampled(out, l, x, sc, w.dtype, w.name, heads, rows, causal=w.causal)
 
 
-@pytest.mark.timeout(600)
-def test_dit_fp16_full_size_sampled():
-    w = workloads.DIT_FP16
-    rows = [0, 1, 127, 128, 2000, 4095, 4096, 4224, 4249]
-    _full_size(w, [(0, 0), (0, 37), (1, 19), (1, 37)], rows)
+def _full_size_every_row(w):
+    """The workload at its full size, in the launch configuration the
+    benchmark times, compared with the oracle on every row of every head."""
+    say("full size, every row", w)
+    x = workloads.make_inputs(w)
+    out, l, sc = _run(x, w.dtype, causal=w.causal)
+    compare_full(out, l, x, sc, w.dtype, w.name, causal=w.causal)
 
 
 @pytest.mark.timeout(600)
-def test_dit_fp32_full_size_sampled():
-    w = workloads.DIT_FP32
-    rows = [0, 5, 1000, 4127, 4128, 4249]
-    _full_size(w, [(0, 1), (1, 36)], rows)
+def test_dit_fp16_full_size():
+    _full_size_every_row(workloads.DIT_FP16)
 
 
 @pytest.mark.timeout(600)
-def test_causal_bf16_full_size_sampled():
-    w = workloads.CAUSAL
-    rows = [0, 1, 2, 63, 64, 127, 128, 1000, 2047, 2048, 3071, 4094, 4095]
-    _full_size(w, [(0, 0), (0, 13), (0, 31)], rows)
+def test_dit_fp32_full_size():
+    _full_size_every_row(workloads.DIT_FP32)
+
+
+@pytest.mark.timeout(600)
+def test_causal_bf16_full_size():
+    _full_size_every_row(workloads.CAUSAL)
 
 
 # ---------------------------------------------------------------------------
