@@ -30,6 +30,23 @@ the GPU, the torch / HIP versions and the sha256 of the loaded library.
 --cold makes every decode call read K and V from HBM: the calls rotate over
 copies totalling more than 1 GiB (the GQA-8 shapes of 64 MiB and less fit in
 the 256 MiB last-level cache and otherwise run from it).
+
+Timing protocol (after the timing protocol of the reproducer on the "Add D512
+support to Metal vector attention" page: a drift check per cell, re-measured
+when it fails):
+  * an untimed pre-roll runs the step in chunks until two consecutive chunk
+    medians agree within 1.5 % and at least ``--preroll-s`` seconds have
+    passed (the GPU clock ramps for a few hundred milliseconds after load
+    starts);
+  * the timed region is repeated (up to 3 attempts) while its drift ratio is
+    outside 1 +- gate; every attempt's mean is reported in ``attempts``;
+  * the default run adds a ``configs`` block: the tiny fp32 case (µs per
+    call, with a dependent chain x = prefill(x, k, v) of 8 calls), the DiT
+    shape in fp32, the causal bf16 prefill with LSE and the GQA-8 D512 decode
+    B2 Lk32768 fp16 read cold from HBM, each with its roofline fraction;
+  * ``cpu_baseline`` records the host CPU model; ``cpu_oracle_1thread`` times
+    the oracle with one BLAS thread on the tiny case and on the GQA-8 D512
+    decode B1 Lk1024 fp16.
 """
 from __future__ import annotations
 
@@ -231,6 +248,184 @@ class Timed:
         return [a.elapsed_time(b) for a, b in self.ev]
 
 
+def median(xs):
+    ys = sorted(xs)
+    return ys[len(ys) // 2]
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def settle(torch, run_chunk, min_s: float, max_s: float, tol: float = 0.015):
+    """Untimed pre-roll: run_chunk() runs a few steps and returns their
+    event-timed durations (ms).  Stops once two consecutive chunk medians
+    agree within ``tol`` and at least min_s seconds have passed, or at max_s."""
+    if max_s <= 0:
+        return {"seconds": 0.0, "chunks": 0, "settled": None}
+    t0 = time.perf_counter()
+    prev, n, settled = None, 0, False
+    while True:
+        med = median(run_chunk())
+        n += 1
+        el = time.perf_counter() - t0
+        if prev is not None and abs(med / prev - 1.0) <= tol and el >= min_s:
+            settled = True
+            break
+        if el >= max_s:
+            break
+        prev = med
+    return {"seconds": round(time.perf_counter() - t0, 2), "chunks": n, "settled": settled}
+
+
+def time_calls(torch, call, n: int, spin_cycles: int = 0):
+    """Event-timed durations (ms) of n back-to-back calls of call(i).  With
+    spin_cycles a bounded spin kernel is queued first so that the host runs
+    ahead and short calls do not wait for their submission."""
+    t = Timed(torch, n)
+    if spin_cycles:
+        torch.cuda._sleep(spin_cycles)
+    for i in range(n):
+        t.ev[i][0].record()
+        call(i)
+        t.ev[i][1].record()
+    torch.cuda.synchronize()
+    return t.ms()
+
+
+def time_chain(torch, call, x0, chain: int = 8, outer: int = 5, spin_cycles: int = 0):
+    """Dependent chain x = call(x) of ``chain`` calls, ``outer`` times: per-call
+    ms of each chain (the warm latency of one call whose input is the previous
+    call's output)."""
+    out = []
+    for _ in range(outer):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if spin_cycles:
+            torch.cuda._sleep(spin_cycles)
+        x = x0
+        a.record()
+        for _ in range(chain):
+            x = call(x)
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b) / chain)
+    return out
+
+
+def cpu_oracle_1thread():
+    """The oracle with one BLAS thread on two small cases, repeated to >= 1 s:
+    the tiny fp32 prefill (TFLOP/s) and the GQA-8 D512 decode B1 Lk1024 fp16
+    (GB/s, all (batch, KV head) groups)."""
+    import torch
+
+    import workloads
+    from oracle import sdpa_reference
+    from threadpoolctl import threadpool_limits
+
+    out = {}
+    with threadpool_limits(limits=1):
+        w = workloads.TINY
+        x = workloads.make_inputs(w)
+        n, t_used = 0, 0.0
+        while t_used < 1.0:
+            t0 = time.perf_counter()
+            sdpa_reference(x["q"], x["k"], x["v"], scale=w.scale)
+            t_used += time.perf_counter() - t0
+            n += 1
+        out[w.name] = {"value": prefill_flops(w) * n / t_used / 1e12, "unit": "TFLOP/s", "cores": 1,
+                       "us_per_call": round(t_used / n * 1e6, 1), "kind": "oracle",
+                       "sample": f"{n} whole calls, fp64 numpy, {t_used:.2f} s"}
+        w = workloads.gqa_decode(1, 1024, "fp16", False)
+        x = workloads.make_inputs(w)
+        n, t_used = 0, 0.0
+        while t_used < 1.0:
+            t0 = time.perf_counter()
+            sdpa_reference(x["q"], x["k"], x["v"], scale=w.scale)
+            t_used += time.perf_counter() - t0
+            n += 1
+        out[w.name] = {"value": decode_bytes(w) * n / t_used / 1e9, "unit": "GB/s", "cores": 1,
+                       "us_per_call": round(t_used / n * 1e6, 1), "kind": "oracle",
+                       "sample": f"{n} whole calls (all 4 KV-head groups), fp64 numpy, {t_used:.2f} s"}
+    return out
+
+
+def config_cells(torch, sdpa, workloads, dev, preroll_s: float):
+    """The other configurations, each timed on its own after a pre-roll:
+    tiny fp32 (µs per call and a dependent chain), DiT fp32, causal bf16 with
+    LSE, GQA-8 D512 decode B2 Lk32768 fp16 read cold from HBM."""
+    cells = {}
+
+    def prefill_cell(w, ncalls, spin=0, chain=False):
+        x = workloads.make_inputs(w, device=dev)
+        out = torch.empty_like(x["q"])
+        call = lambda i: sdpa.prefill(x["q"], x["k"], x["v"], scale=w.scale, causal=w.causal,
+                                      return_lse=w.lse, out=out)
+        call(0)
+        torch.cuda.synchronize()
+        pre = settle(torch, lambda: time_calls(torch, call, 8, spin), preroll_s / 2, 4 * preroll_s)
+        ms = time_calls(torch, call, ncalls, spin)
+        avg = sum(ms) / len(ms)
+        fl = prefill_flops(w)
+        tf = fl / (avg * 1e-3) / 1e12
+        c = {"workload": w.name, "dtype": w.dtype, "calls": ncalls, "avg_us": round(avg * 1e3, 2),
+             "median_us": round(median(ms) * 1e3, 2), "min_us": round(min(ms) * 1e3, 2),
+             "drift": drift(ms), "preroll": pre, "samples_us": [round(t * 1e3, 2) for t in ms],
+             "value": round(tf, 3), "unit": "TFLOP/s",
+             "roofline": {"bound": "mfma", "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                          "frac": round(tf / PEAK_TFLOPS[w.dtype], 4), "flops_per_launch": fl}}
+        if chain:
+            ch = time_chain(torch, lambda y: sdpa.prefill(y, x["k"], x["v"], scale=w.scale), x["q"],
+                            spin_cycles=spin)
+            c["chain8_us_per_call"] = {"median": round(median(ch) * 1e3, 2),
+                                       "samples": [round(t * 1e3, 2) for t in ch]}
+        del x, out
+        torch.cuda.empty_cache()
+        return c
+
+    cells["tiny_fp32"] = prefill_cell(workloads.TINY, 40, spin=4_000_000, chain=True)
+    cells["tiny_fp32"]["roofline"]["note"] = "2 workgroups: latency-bound, reported in µs"
+    cells["dit_fp32"] = prefill_cell(workloads.DIT_FP32, 15)
+    cells["causal_bf16"] = prefill_cell(workloads.CAUSAL, 30)
+
+    # GQA-8 D512 decode, B2 Lk32768 fp16, every call reading K / V from HBM
+    w = workloads.gqa_decode(2, 32768, "fp16", False)
+    x = workloads.make_inputs(w, device=dev)
+    kvb = x["k"].numel() * x["k"].element_size() * 2
+    ncopy = -(-(1 << 30) // kvb) + 1
+    sets = [(x["k"], x["v"])] + [(x["k"].clone(), x["v"].clone()) for _ in range(ncopy - 1)]
+    ws = torch.empty(max(16, sdpa.decode_workspace_bytes(x["q"], x["k"], x["v"])), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(x["q"])
+    call = lambda i: sdpa.decode(x["q"], sets[i % ncopy][0], sets[i % ncopy][1], scale=w.scale,
+                                 workspace=ws, out=out)
+    call(0)
+    torch.cuda.synchronize()
+    pre = settle(torch, lambda: time_calls(torch, call, 3 * ncopy, 2_000_000), preroll_s / 2, 4 * preroll_s)
+    ms = time_calls(torch, call, 10 * ncopy, 8_000_000)
+    avg = sum(ms) / len(ms)
+    nb = decode_bytes(w)
+    gbs = nb / (avg * 1e-3) / 1e9
+    cells[w.name + "_cold"] = {
+        "workload": w.name, "dtype": w.dtype, "calls": len(ms), "kv_copies": ncopy,
+        "splits": sdpa.decode_num_splits(x["q"], x["k"], x["v"]),
+        "avg_us": round(avg * 1e3, 2), "median_us": round(median(ms) * 1e3, 2),
+        "drift": drift(ms), "preroll": pre, "samples_us": [round(t * 1e3, 2) for t in ms],
+        "value": round(gbs, 1), "unit": "GB/s",
+        "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "bytes_per_launch": nb, "kernel": "decode_kernel + merge_kernel"}}
+    del x, sets, ws, out
+    torch.cuda.empty_cache()
+    return cells
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +433,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="default")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="default workload: skip the per-configuration cells")
+    ap.add_argument("--preroll-s", type=float, default=1.0,
+                    help="minimum seconds of untimed pre-roll before the timed region (0 = none, e.g. under "
+                         "a counter profiler)")
     ap.add_argument("--cold", action="store_true",
                     help="decode: rotate over copies of K and V totalling more than 1 GiB, so that every call "
                          "reads them from HBM and not from the 256 MiB last-level cache")
@@ -321,46 +521,71 @@ def main():
                         seqlens_k=Dd.get("seqlens_k"))
             if td: td.ev[i][1].record()
 
+    def whole_steps(n):
+        """n steps with one event pair per step around both forms (ms each)."""
+        t = Timed(torch, n)
+        for i in range(n):
+            t.ev[i][0].record()
+            step()
+            t.ev[i][1].record()
+        torch.cuda.synchronize()
+        return t.ms()
+
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    tp = Timed(torch, args.steps) if P is not None else None
-    td = Timed(torch, args.steps) if Dd is not None else None
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    runway_ms = 0.0
-    if P is None:
-        # A decode call can take less GPU time than its submission through
-        # Python, which would leave the GPU idle between the start event and
-        # the kernels.  A bounded spin kernel queued first lets the host run
-        # ahead, so the timed calls execute back to back; its own duration is
-        # taken out of the wall-clock step time below.  (Prefill steps keep
-        # the GPU busy by themselves; measured with the spin in front, their
-        # first steps ran slower while the clock recovered.)
-        r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        r0.record()
-        torch.cuda._sleep(2_000_000 * max(1, args.steps // 10))
-        r1.record()
-    for i in range(args.steps):
-        step(tp, td, i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if P is None:
-        runway_ms = r0.elapsed_time(r1)
-    ms_step = (wall * 1e3 - runway_ms) / args.steps
+    print(f"[bench] pre-roll >= {args.preroll_s} s", file=sys.stderr, flush=True)
+    preroll = settle(torch, lambda: whole_steps(8), args.preroll_s, 6 * args.preroll_s)
+
+    # A decode call can take less GPU time than its submission through Python,
+    # which would leave the GPU idle between the start event and the kernels.
+    # A bounded spin kernel queued first lets the host run ahead, so the timed
+    # calls execute back to back; its own duration is taken out of the
+    # wall-clock step time below.  (Prefill steps keep the GPU busy by
+    # themselves; measured with the spin in front, their first steps ran
+    # slower while the clock recovered.)
+    spin = P is None
+    attempts = []
+    for attempt in range(3):
+        tp = Timed(torch, args.steps) if P is not None else None
+        td = Timed(torch, args.steps) if Dd is not None else None
+        print(f"[bench] timing {args.steps} steps (attempt {attempt + 1})", file=sys.stderr, flush=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        if spin:
+            r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            r0.record()
+            torch.cuda._sleep(2_000_000 * max(1, args.steps // 10))
+            r1.record()
+        for i in range(args.steps):
+            step(tp, td, i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        runway_ms = r0.elapsed_time(r1) if spin else 0.0
+        dr = {"prefill": drift(tp.ms()) if tp else None, "decode": drift(td.ms()) if td else None}
+        att = {"ms_per_step": round((wall * 1e3 - runway_ms) / args.steps, 4), "drift": dr}
+        if tp:
+            att["prefill_avg_ms"] = round(sum(tp.ms()) / args.steps, 5)
+        if td:
+            att["decode_avg_ms"] = round(sum(td.ms()) / args.steps, 5)
+        attempts.append(att)
+        if all(d is None or abs(d - 1.0) <= 0.05 for d in dr.values()):
+            break
+    ms_step = attempts[-1]["ms_per_step"]
 
     res = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "data": "synthetic (seeded N(0,1), see workloads/)"}
     res["env"] = {"gpu": torch.cuda.get_device_name(dev), "torch": torch.__version__, "hip": torch.version.hip,
                   "library_sha256": file_sha256(sdpa.library_path), "source_hash": source_hash()}
-    res["drift"] = {"prefill": drift(tp.ms()) if tp else None, "decode": drift(td.ms()) if td else None,
-                    "gate": 0.05}
+    res["drift"] = dict(attempts[-1]["drift"], gate=0.05)
+    res["timing"] = {"preroll": preroll, "attempts": attempts,
+                     "note": "value = mean over the last attempt's timed steps; an attempt whose drift ratio "
+                             "leaves 1 +- gate is repeated (at most 3)"}
     cfg = {}
     if P is not None:
-        pm = sorted(tp.ms())
+        pm = tp.ms()
         avg = sum(pm) / len(pm)
         fl = backward_flops(pre_w) if pre_w.grad else prefill_flops(pre_w)
         tf = fl / (avg * 1e-3) / 1e12
@@ -370,23 +595,27 @@ def main():
                            "frac": round(tf / peak, 4), "traffic": load_traffic("prefill_" + pre_w.name),
                            "kernel": ("bwd_prep + bwd_dq + bwd_dkv kernels" if pre_w.grad else "prefill_kernel"),
                            "avg_ms": round(avg, 5),
-                           "median_ms": round(pm[len(pm) // 2], 5),
-                           "flops_per_launch": fl}
+                           "median_ms": round(median(pm), 5),
+                           "median_frac": round(fl / (median(pm) * 1e-3) / 1e12 / peak, 4),
+                           "flops_per_launch": fl,
+                           "samples_ms": [round(t, 5) for t in pm]}
         cfg["workload"] = pre_w.name
         cfg.update(prefill={"B": pre_w.B, "Hq": pre_w.Hq, "Hkv": pre_w.Hkv, "Lq": pre_w.Lq,
                             "Lk": pre_w.Lk, "D": pre_w.D, "dtype": pre_w.dtype,
                             "causal": pre_w.causal, "lse": pre_w.lse, "gradients": pre_w.grad})
     if Dd is not None:
-        dm = sorted(td.ms())
+        dm = td.ms()
         avg = sum(dm) / len(dm)
         nbytes = decode_bytes(dec_w)
         gbs = nbytes / (avg * 1e-3) / 1e9
         dec = {"value": round(gbs, 1), "unit": "GB/s", "dtype": dec_w.dtype, "avg_ms": round(avg, 5),
-               "median_ms": round(dm[len(dm) // 2], 5), "splits": nsplit,
+               "median_ms": round(median(dm), 5), "splits": nsplit,
                "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "median_frac": round(nbytes / (median(dm) * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
                             "traffic": load_traffic("decode_" + dec_w.name),
-                            "kernel": "decode_kernel + merge_kernel", "bytes_per_launch": nbytes}}
+                            "kernel": "decode_kernel + merge_kernel", "bytes_per_launch": nbytes,
+                            "samples_ms": [round(t, 5) for t in dm]}}
         cfg["workload"] = (cfg.get("workload", "") + " + " if P is not None else "") + dec_w.name
         cfg["decode"] = {"B": dec_w.B, "Hq": dec_w.Hq, "Hkv": dec_w.Hkv, "Lq": dec_w.Lq, "Lk": dec_w.Lk,
                          "D": dec_w.D, "dtype": dec_w.dtype, "causal": dec_w.causal, "mask": dec_w.mask,
@@ -397,14 +626,23 @@ def main():
             res.update(value=dec["value"], unit="GB/s", dtype=dec_w.dtype, roofline=dec["roofline"])
         res["decode"] = dec
     res["config"] = cfg
+    if wl == "default" and not args.no_configs:
+        print("[bench] per-configuration cells", file=sys.stderr, flush=True)
+        del P, Dd, ws, kv_sets
+        torch.cuda.empty_cache()
+        res["configs"] = config_cells(torch, sdpa, workloads, dev, max(args.preroll_s, 0.25))
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (fp64 oracle)", file=sys.stderr, flush=True)
-        if P is not None:
+        if run_prefill:
             res["cpu_baseline"] = cpu_baseline_backward(pre_w) if pre_w.grad else cpu_baseline_prefill(pre_w)
-            if Dd is not None:
+            if dec_w is not None:
                 res["decode"]["cpu_baseline"] = cpu_baseline_decode(dec_w)
         else:
             res["cpu_baseline"] = cpu_baseline_decode(dec_w)
+        res["cpu_baseline"]["cpu_model"] = cpu_model()
+        res["cpu_baseline"]["host_cpus"] = os.cpu_count()
+        if wl == "default":
+            res["cpu_oracle_1thread"] = cpu_oracle_1thread()
     res["source_hash"] = source_hash()
     print(json.dumps(res), flush=True)
 

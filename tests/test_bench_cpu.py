@@ -67,3 +67,27 @@ def test_drift_ratio():
     assert bench.drift([1.0] * 7 + [1.1] * 8) == pytest.approx(1.1)
     assert bench.drift([2.0] * 30) == 1.0
     assert bench.drift([1.0] * 14) is None
+
+
+def test_settle_stops_when_chunks_agree():
+    seq = iter([[2.0], [1.5], [1.2], [1.1], [1.1], [1.1]])
+    r = bench.settle(None, lambda: next(seq), min_s=0.0, max_s=10.0)
+    assert r["settled"] and r["chunks"] == 5
+
+
+def test_settle_gives_up_at_its_limit():
+    vals = iter((1.0, 1.1)[x % 2] for x in range(10 ** 9))   # 10 % apart, never settles
+    r = bench.settle(None, lambda: [next(vals)], min_s=0.0, max_s=0.05)
+    assert r["settled"] is False and r["chunks"] >= 2
+
+
+def test_settle_disabled():
+    assert bench.settle(None, lambda: 1 / 0, min_s=0.0, max_s=0.0)["chunks"] == 0
+
+
+def test_cpu_oracle_one_thread():
+    r = bench.cpu_oracle_1thread()
+    assert set(r) == {"tiny_fp32", "gqa8_decode_b1_lk1024_fp16"}
+    for v in r.values():
+        assert v["cores"] == 1 and v["value"] > 0 and v["kind"] == "oracle"
+    assert bench.cpu_model()
