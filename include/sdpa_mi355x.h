@@ -29,13 +29,15 @@
  *   - query head hq reads KV head hq / (Hq / Hkv)   (Hq % Hkv must be 0);
  *   - S[i,j] = scale * (q_i . k_j) computed from the dtype inputs with fp32
  *     products and fp32 accumulation, then + mask[b,hq,i,j] (fp32), or -inf
- *     where a boolean mask is 0.  One exception, fp16 prefill with
- *     c = |scale| * log2(e) <= 1 (every D >= 3 at the default scale): the
- *     kernel multiplies each q element by c once and rounds it to fp16 before
- *     the product, so that the matrix cores deliver the exponent directly.
- *     That is one more rounding of at most 2^-11 relative per q element:
- *     |error of S[i,j]| <= 2^-11 * |scale| * sum_d |q_id k_jd|, which
- *     perturbs each probability by a factor within exp(+-that bound);
+ *     where a boolean mask is 0.  One exception: an fp16 sdpa_prefill call
+ *     without mask and without lse output, with c = |scale| * log2(e) <= 1
+ *     (every D >= 3 at the default scale), multiplies each q element by c once
+ *     and rounds it to fp16 before the product, so that the matrix cores
+ *     deliver the exponent directly.  That is one more rounding of at most
+ *     2^-11 relative per q element: |error of S[i,j]| <= 2^-11 * |scale| *
+ *     sum_d |q_id k_jd|, which perturbs each probability by a factor within
+ *     exp(+-that bound).  Calls that return lse keep the exact fp32 scale, so
+ *     O may differ in its last bits between the two kinds of call;
  *   - causal (bottom-right): key j is visible to query i iff
  *     j <= i + (Lk - Lq); for Lq == 1 every key is visible;
  *   - sinks[hq] (fp32, not multiplied by scale) adds exp(sinks[hq]) to the

@@ -401,7 +401,10 @@ __device__ inline float dot2_ones(TBF16, uint32_t pk, float acc) {
 // tile ahead, with one fence-free barrier per tile.  V^T is read with
 // ds_read_b64_tr_b16.  Interior tiles (every key visible to the whole
 // workgroup, no mask) skip per-element masking.
-template <class T, int D, bool CAUSAL, bool MASK, int NW>
+// REL (fp16 only): Q is pre-multiplied by the exponent scale and the scores
+// are kept relative to the reference max (below); the host selects it for
+// calls without a log-sum-exp output.
+template <class T, int D, bool CAUSAL, bool MASK, int NW, bool REL>
 __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   using C = Cfg16<D, NW>;
   constexpr int BM = 32 * NW;  // query rows per workgroup
@@ -432,14 +435,17 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   const int coff = lk - lq;
 
   // exponent scale c = |scale| log2(e); a negative scale is moved into Q.
-  // fp16 with c <= 1: Q is multiplied by c once (it cannot overflow; each
-  // element takes one more rounding, 2^-11 relative), so the matrix cores
+  // REL (fp16, c <= 1, no log-sum-exp output): Q is multiplied by c once (it
+  // cannot overflow; each element takes one more rounding, 2^-11 relative, so
+  // a score moves by at most 2^-11 c sum_d |q_d k_d|), the matrix cores
   // deliver c S itself and the steady loop, which also starts its score
   // accumulators at -m, feeds the exponential without any per-score
-  // arithmetic.  (bf16 would round c Q to 8 bits, which shows in rows that
-  // average few keys, so bf16 keeps one multiply-add per score.)  cs is the
-  // factor the scores still owe.
-  constexpr bool kRel = std::is_same<T, TF16>::value;
+  // arithmetic.  Calls that return the log-sum-exp keep the exact fp32 scale:
+  // that error would reach the LSE undamped at large logits.  (bf16 would
+  // round c Q to 8 bits, which shows in rows that average few keys, so bf16
+  // never takes this form.)  cs is the factor the scores still owe.
+  static_assert(!REL || std::is_same<T, TF16>::value, "pre-scaled Q is fp16 only");
+  constexpr bool kRel = REL;
   const float c = fabsf(p.scale_log2);
   const bool pre = kRel && c <= 1.f;
   const float cs = pre ? 1.f : c;
@@ -899,13 +905,13 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
 // than two.  D = 128: two waves per SIMD.  D = 256: one.  The masked variants
 // keep a second score tile plus the mask gathers live across the pipeline and
 // get the whole register file.
-template <class T, int D, bool CAUSAL, int NW>
+template <class T, int D, bool CAUSAL, int NW, bool REL>
 __global__ __launch_bounds__(64 * NW, D >= 256 ? 1 : (D == 64 ? 3 : 2)) void prefill16_kernel(AttnParams p) {
-  prefill16_body<T, D, CAUSAL, false, NW>(p);
+  prefill16_body<T, D, CAUSAL, false, NW, REL>(p);
 }
 template <class T, int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void prefill16_mask_kernel(AttnParams p) {
-  prefill16_body<T, D, CAUSAL, true, kWaves>(p);
+  prefill16_body<T, D, CAUSAL, true, kWaves, false>(p);
 }
 
 template <class T, int D>
@@ -928,12 +934,19 @@ hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
     // LDS, and measure slower.)
     const dim3 grid((unsigned)((p.Lq + kBM - 1) / kBM * p.B * p.Hq));
     const dim3 block(kThreads);
+    // pre-scaled Q: fp16, exponent scale at most 1, no log-sum-exp output
+    const bool rel = std::is_same<T, TF16>::value && fabsf(p.scale_log2) <= 1.f && p.lse == nullptr;
     if (mask) {
       if (causal) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, true>), grid, block, 0, s, p);
       else hipLaunchKernelGGL((prefill16_mask_kernel<T, D, false>), grid, block, 0, s, p);
+    } else if (rel) {
+      if constexpr (std::is_same<T, TF16>::value) {
+        if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves, true>), grid, block, 0, s, p);
+      }
     } else {
-      if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves>), grid, block, 0, s, p);
+      if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves, false>), grid, block, 0, s, p);
+      else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves, false>), grid, block, 0, s, p);
     }
   }
   return hipGetLastError();

@@ -19,13 +19,16 @@ pytestmark = pytest.mark.gpu
 
 
 def _run(x, dtype_name, causal=False, scale=None, lse=True):
+    """One prefill call; with lse=False the call itself asks for no
+    log-sum-exp (fp16 then takes the pre-scaled-Q kernels)."""
     d = to_dev(x)
     D = x["q"].shape[-1]
     scale = 1.0 / math.sqrt(D) if scale is None else scale
-    out, l = sdpa.prefill(d["q"], d["k"], d["v"], scale=scale, causal=causal, mask=d["mask"],
-                          sinks=d["sinks"], return_lse=True)
+    r = sdpa.prefill(d["q"], d["k"], d["v"], scale=scale, causal=causal, mask=d["mask"],
+                     sinks=d["sinks"], return_lse=lse)
+    out, l = r if lse else (r, None)
     torch.cuda.synchronize()
-    return out, (l if lse else None), scale
+    return out, l, scale
 
 
 def test_tiny_fp32_full():
@@ -57,6 +60,9 @@ def test_prefill_grid(dtype, D, case):
                     sink_scale=2.0, mask_neg_inf_frac=0.1)
     out, l, sc = _run(x, dtype, causal=causal)
     compare_full(out, l, x, sc, dtype, f"grid{case}-{dtype}-D{D}", causal=causal)
+    if dtype == "fp16":   # no log-sum-exp requested: the pre-scaled-Q kernels
+        out, _, sc = _run(x, dtype, causal=causal, lse=False)
+        compare_full(out, None, x, sc, dtype, f"grid{case}-{dtype}-D{D} O only", causal=causal)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -69,6 +75,9 @@ def test_prefill_grid_d256(dtype, case):
                     sink_scale=2.0, mask_neg_inf_frac=0.1)
     out, l, sc = _run(x, dtype, causal=causal)
     compare_full(out, l, x, sc, dtype, f"grid{case}-{dtype}-D256", causal=causal)
+    if dtype == "fp16":
+        out, _, sc = _run(x, dtype, causal=causal, lse=False)
+        compare_full(out, None, x, sc, dtype, f"grid{case}-{dtype}-D256 O only", causal=causal)
 
 
 def test_d256_long_causal_sampled():
@@ -86,10 +95,11 @@ def _full_size(w, heads, rows):
 
 def _full_size_every_row(w):
     """The workload at its full size, in the launch configuration the
-    benchmark times, compared with the oracle on every row of every head."""
+    benchmark times (log-sum-exp output only where the workload asks for
+    it), compared with the oracle on every row of every head."""
     say("full size, every row", w)
     x = workloads.make_inputs(w)
-    out, l, sc = _run(x, w.dtype, causal=w.causal)
+    out, l, sc = _run(x, w.dtype, causal=w.causal, lse=w.lse)
     compare_full(out, l, x, sc, w.dtype, w.name, causal=w.causal)
 
 
@@ -152,6 +162,10 @@ def test_dominant_logit_and_identical_keys(dtype):
     x["k"] = k.to(x["q"].dtype)
     out, l, sc = _run(x, dtype)
     compare_full(out, l, x, sc, dtype, "dominant/identical")
+    # without the log-sum-exp (fp16: Q pre-multiplied by the exponent scale);
+    # the dominant score is 4 |q_3|^2 / 8, about 32
+    out, _, sc = _run(x, dtype, lse=False)
+    compare_full(out, None, x, sc, dtype, "dominant/identical, O only")
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -167,6 +181,8 @@ def test_running_max_moves(dtype, D):
     x["q"], x["k"] = q.to(x["v"].dtype), k.to(x["v"].dtype)
     out, l, sc = _run(x, dtype)
     compare_full(out, l, x, sc, dtype, f"moving max {dtype} D{D}")
+    out, _, sc = _run(x, dtype, lse=False)
+    compare_full(out, None, x, sc, dtype, f"moving max {dtype} D{D} O only")
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -188,6 +204,8 @@ def test_tail_workgroup_waves(dtype, tail):
     x = random_case(2100 + tail, 2, 2, 1, Lq, 300, 64, dtype, sinks=True)
     out, l, sc = _run(x, dtype, causal=tail % 2 == 1)
     compare_full(out, l, x, sc, dtype, f"tail {tail}", causal=tail % 2 == 1)
+    out, _, sc = _run(x, dtype, causal=tail % 2 == 1, lse=False)
+    compare_full(out, None, x, sc, dtype, f"tail {tail} O only", causal=tail % 2 == 1)
 
 
 def test_non_contiguous_layouts():

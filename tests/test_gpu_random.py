@@ -67,8 +67,11 @@ def test_random_prefill(seed):
     x = _inputs(seed, c)
     d = to_dev(x)
     sc = 1.0 / math.sqrt(c["D"])
-    out, lse = sdpa.prefill(d["q"], d["k"], d["v"], scale=sc, causal=c["causal"], mask=d["mask"],
-                            sinks=d["sinks"], return_lse=True, seqlens_q=c["sq"], seqlens_k=c["sk"])
+    # odd seeds ask for no log-sum-exp (fp16 then runs the pre-scaled-Q kernels)
+    want_lse = seed % 2 == 0
+    r = sdpa.prefill(d["q"], d["k"], d["v"], scale=sc, causal=c["causal"], mask=d["mask"],
+                     sinks=d["sinks"], return_lse=want_lse, seqlens_q=c["sq"], seqlens_k=c["sk"])
+    out, lse = r if want_lse else (r, None)
     torch.cuda.synchronize()
     compare_full(out, lse, x, sc, c["dtype"], f"random prefill {seed}", causal=c["causal"], **_lens(c))
 

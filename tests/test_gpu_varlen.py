@@ -51,6 +51,12 @@ def test_prefill_seqlens(dtype, D, case):
     torch.cuda.synchronize()
     compare_full(out, lse, x, sc, dtype, f"seqlens{case}-{dtype}-D{D}", causal=causal,
                  seqlens_q=np.array(sq), seqlens_k=np.array(sk))
+    if dtype == "fp16":   # no log-sum-exp requested: the pre-scaled-Q kernels
+        out = sdpa.prefill(d["q"], d["k"], d["v"], scale=sc, causal=causal, mask=d["mask"],
+                           sinks=d["sinks"], seqlens_q=sq, seqlens_k=sk)
+        torch.cuda.synchronize()
+        compare_full(out, None, x, sc, dtype, f"seqlens{case}-{dtype}-D{D} O only", causal=causal,
+                     seqlens_q=np.array(sq), seqlens_k=np.array(sk))
 
 
 def test_prefill_full_lengths_equal_no_lengths():
