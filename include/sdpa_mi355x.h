@@ -194,6 +194,24 @@ SDPA_API int sdpa_decode(const sdpa_args *args, int num_splits,
 SDPA_API int sdpa_decode_check(const sdpa_args *args, int num_splits,
                       const void *workspace, size_t workspace_bytes);
 
+/* Decode that allocates nothing, for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, kernels, split choice and results as sdpa_decode, but the
+ * two-pass form keeps its split partials in a static device array of the
+ * library instead of a caller workspace: SDPA_DECODE_SCRATCH_BYTES (16 MiB)
+ * on each GPU the library runs on, held until the process ends.  A request
+ * whose partials need more (sdpa_decode_workspace_bytes() above that, e.g.
+ * B * Hq * Lq * splits * (kernel head dim + 2) * 4 > 16 MiB) returns
+ * SDPA_ERR_WORKSPACE before anything is enqueued: pass fewer splits, or use
+ * sdpa_decode with a workspace.  The array belongs to the CURRENT device and
+ * `stream` must belong to it too (SDPA_ERR_ARG otherwise).  Every call on one
+ * GPU shares the array and leaves its partials there, so calls that overlap
+ * on one GPU (other streams, other host threads) race: the caller orders
+ * them.  The first call on each device looks up the array's device address
+ * (hipGetSymbolAddress); no call allocates, frees or synchronises. */
+#define SDPA_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+SDPA_API int sdpa_decode_noalloc(const sdpa_args *args, int num_splits, void *stream);
+
 /* Number of key-range splits sdpa_decode will use for this request and
  * num_splits value (0 = automatic); 1 means the single-pass kernel.
  * Returns 0 when the request is invalid. */

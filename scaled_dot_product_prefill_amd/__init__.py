@@ -104,6 +104,8 @@ def library():
     lib.sdpa_decode.restype = ctypes.c_int
     lib.sdpa_decode_check.argtypes = [P, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
     lib.sdpa_decode_check.restype = ctypes.c_int
+    lib.sdpa_decode_noalloc.argtypes = [P, ctypes.c_int, ctypes.c_void_p]
+    lib.sdpa_decode_noalloc.restype = ctypes.c_int
     lib.sdpa_decode_num_splits.argtypes = [P, ctypes.c_int]
     lib.sdpa_decode_num_splits.restype = ctypes.c_int
     lib.sdpa_decode_workspace_bytes.argtypes = [P, ctypes.c_int]
@@ -282,6 +284,37 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
     ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib.sdpa_decode(ctypes.byref(a), int(num_splits), ws_ptr, ws_bytes, ctypes.c_void_p(stream))
+    if st != 0:
+        _raise(st)
+    return (o, lse) if return_lse else o
+
+
+# bytes of the library's static per-GPU scratch that decode_noalloc uses
+DECODE_SCRATCH_BYTES = 16 << 20
+
+
+def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
+                   causal: bool = False, mask: Optional[torch.Tensor] = None,
+                   sinks: Optional[torch.Tensor] = None, return_lse: bool = False, num_splits: int = 0,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   seqlens_q=None, seqlens_k=None):
+    """decode() through sdpa_decode_noalloc: the split partials live in the
+    library's static per-GPU scratch, so the library call allocates nothing
+    (pass ``out`` -- and ``lse`` with return_lse -- to allocate nothing here
+    either).  Calls that overlap on one GPU share that scratch and race."""
+    lib = library()
+    q, k, v, scale, mask, sinks = _decode_args(q, k, v, scale, mask, sinks)
+    B, Hq, Lq, D = q.shape
+    o = torch.empty((B, Hq, Lq, v.shape[3]), dtype=q.dtype, device=q.device) if out is None else out
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
+    if not return_lse:
+        lse = None
+    sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
+    sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
+    a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    st = lib.sdpa_decode_noalloc(ctypes.byref(a), int(num_splits), ctypes.c_void_p(stream))
     if st != 0:
         _raise(st)
     return (o, lse) if return_lse else o

@@ -12,10 +12,15 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "sdpa_internal.hpp"
 #include "sdpa_mi355x.h"
+
+// Split partials of sdpa_decode_noalloc: one copy per GPU, alive until the
+// process ends, shared by every call on that GPU.
+static __device__ __align__(256) unsigned char scratch[SDPA_DECODE_SCRATCH_BYTES];
 
 namespace sdpa {
 namespace {
@@ -242,7 +247,10 @@ size_t workspace_for(const sdpa_args* a, const SplitPlan& sp) {
   return (size_t)a->B * a->Hq * a->Lq * sp.nsplit * (kernel_dim(a) + 2) * sizeof(float);
 }
 
-int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_bytes, SplitPlan* out) {
+// static_scratch: the partials go to the library's static device array
+// (sdpa_decode_noalloc) instead of the caller's workspace.
+int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_bytes, SplitPlan* out,
+                 bool static_scratch = false) {
   int st = check_common(a);
   if (st != SDPA_OK) return st;
   if (a->Lq > kMaxDecodeLq)
@@ -256,7 +264,13 @@ int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_b
   if ((int64_t)sp.nsplit * decode_chunks(a) * a->Hkv * a->B > kMaxInt)
     return fail(SDPA_ERR_UNSUPPORTED, "grid too large");
   const size_t need = workspace_for(a, sp);
-  if (need > 0) {
+  if (static_scratch) {
+    if (need > SDPA_DECODE_SCRATCH_BYTES)
+      return fail(SDPA_ERR_WORKSPACE,
+                  "the %d-split partials need %zu bytes, above the %zu-byte static scratch of "
+                  "sdpa_decode_noalloc (pass fewer splits, or sdpa_decode with a workspace)",
+                  sp.nsplit, need, (size_t)SDPA_DECODE_SCRATCH_BYTES);
+  } else if (need > 0) {
     if (!ws) return fail(SDPA_ERR_WORKSPACE, "two-pass decode needs a workspace of %zu bytes", need);
     if ((uintptr_t)ws % 16 != 0) return fail(SDPA_ERR_ALIGN, "workspace is not 16-byte aligned");
     if (ws_bytes < need)
@@ -351,6 +365,39 @@ int launch_status(hipError_t e) {
   return ok();
 }
 
+// Device address of the static decode scratch on the current device, looked
+// up once per device (each GPU holds its own copy of the array).  In host code
+// the array's name only stands for the symbol; kernels get this address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+int scratch_address(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SDPA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SDPA_ERR_UNSUPPORTED, "device %d is beyond the %d devices the static scratch covers", dev,
+                kMaxDevices);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return fail(SDPA_ERR_HIP, "hipStreamGetDevice: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(SDPA_ERR_ARG, "stream belongs to device %d, the current device is %d", (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SDPA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return SDPA_OK;
+}
+
 }  // namespace
 
 AttnParams make_params(const sdpa_args& a) {
@@ -432,6 +479,25 @@ int sdpa_decode(const sdpa_args* args, int num_splits, void* workspace, size_t w
   p.nchunk = (int)sdpa::decode_chunks(args);
   if (sp.nsplit > 1) {
     float* ws = (float*)workspace;
+    p.part_o = ws;
+    p.part_ml = ws + (size_t)args->B * args->Hq * args->Lq * sp.nsplit * sdpa::kernel_dim(args);
+  }
+  return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
+}
+
+int sdpa_decode_noalloc(const sdpa_args* args, int num_splits, void* stream) {
+  sdpa::SplitPlan sp;
+  int st = sdpa::check_decode(args, num_splits, nullptr, 0, &sp, /*static_scratch=*/true);
+  if (st != SDPA_OK) return st;
+  sdpa::AttnParams p = sdpa::make_params(*args);
+  p.nsplit = sp.nsplit;
+  p.split_len = sp.split_len;
+  p.nchunk = (int)sdpa::decode_chunks(args);
+  if (sp.nsplit > 1) {
+    void* base = nullptr;
+    st = sdpa::scratch_address(stream, &base);
+    if (st != SDPA_OK) return st;
+    float* ws = (float*)base;
     p.part_o = ws;
     p.part_ml = ws + (size_t)args->B * args->Hq * args->Lq * sp.nsplit * sdpa::kernel_dim(args);
   }

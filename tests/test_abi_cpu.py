@@ -290,3 +290,20 @@ def test_backward_validation(lib):
     assert _bwd(lib, ws=(1 << 41) + 64) == S.ERR_ARG                           # workspace inside dout
     a = _args()
     assert lib.sdpa_prefill_backward_workspace_bytes(ctypes.byref(a)) == 2 * 8 * 64 * 2 * 4
+
+
+def test_noalloc_decode_rejects_partials_beyond_the_static_scratch(lib):
+    # long-context decode shape at 128 splits: 8*32*1*128*(128+2)*4 bytes of
+    # partials > 16 MiB; rejected by validation before any HIP call
+    B, Hq, Hkv, Lk, D = 8, 32, 8, 131072, 128
+    a = _args(B=B, Hq=Hq, Hkv=Hkv, Lq=1, Lk=Lk, D=D)
+    for n, L, H in (("q", 1, Hq), ("k", Lk, Hkv), ("v", Lk, Hkv), ("o", 1, Hq)):
+        st = getattr(a, n + "_stride")
+        st[0], st[1], st[2] = H * L * D, L * D, D
+    need = lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 128)
+    assert need == B * Hq * 128 * (D + 2) * 4 > 16 << 20
+    assert lib.sdpa_decode_noalloc(ctypes.byref(a), 128, None) == S.ERR_WORKSPACE
+    assert b"static scratch" in lib.sdpa_last_error()
+    # invalid arguments are still reported as such
+    a.Hq = 30
+    assert lib.sdpa_decode_noalloc(ctypes.byref(a), 0, None) == S.ERR_SHAPE
