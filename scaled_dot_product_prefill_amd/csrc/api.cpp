@@ -209,9 +209,13 @@ struct SplitPlan {
 // Split of the key range for decode.  Automatic: start from one workgroup per
 // compute unit (MI355X: 256), then double the split count while a split would
 // still hold more than 32 key tiles (up to 16 workgroups per CU); never more
-// splits than tiles, each split a whole number of tiles.  Measured on the
-// GQA-8 D512 and long-context D128 decode shapes, this is within a few percent
-// of the best fixed split count for each.
+// splits than tiles, each split a whole number of tiles.  16-bit kernels at
+// head dim 256 / 512 with one 16-column block stop at one workgroup per CU
+// instead: such a grid runs with a four-stage load ring (three tiles in
+// flight), which streams faster than two workgroups of two stages each
+// (GQA-8 D512 B2 Lk32768 fp16, cold: 32 splits 100 us, 64 splits 102 us).
+// Measured on the GQA-8 D512 and long-context D128 decode shapes, this is
+// within a few percent of the best fixed split count for each.
 constexpr int64_t kDecodeCUs = 256;
 constexpr int64_t kDecodeMaxTilesPerSplit = 32;
 
@@ -230,8 +234,10 @@ SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
     const int64_t tk = decode_tile_keys(a->dtype, kernel_dim(a), decode_cpw(a->dtype, a->Lq * (a->Hq / a->Hkv)));
     const int64_t tiles = (Lk + tk - 1) / tk;
     const int64_t units = a->B * a->Hkv * decode_chunks(a);
-    int64_t ns = (kDecodeCUs + units - 1) / units;
-    while ((tiles + ns - 1) / ns > kDecodeMaxTilesPerSplit && ns * units < 16 * kDecodeCUs) ns *= 2;
+    const bool deep = a->dtype != SDPA_F32 && kernel_dim(a) >= 256 &&
+                      decode_cpw(a->dtype, a->Lq * (a->Hq / a->Hkv)) == 1;
+    int64_t ns = deep ? kDecodeCUs / units : (kDecodeCUs + units - 1) / units;
+    while (!deep && (tiles + ns - 1) / ns > kDecodeMaxTilesPerSplit && ns * units < 16 * kDecodeCUs) ns *= 2;
     if (ns > tiles) ns = tiles;
     if (ns < 1) ns = 1;
     const int64_t tiles_per = (tiles + ns - 1) / ns;

@@ -456,13 +456,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_f32_kernel(AttnParams p) {
 #ifndef SDPA_DECODE16_STAGES_LARGE
 #define SDPA_DECODE16_STAGES_LARGE 2  // ring stages at D >= 256 (32 KiB stages)
 #endif
-template <int D, int TKO = 0, int NWV = kWaves>
+template <int D, int TKO = 0, int NWV = kWaves, int NSTO = 0>
 struct Dec16 {
   static constexpr int RB = D * 2;                 // row bytes
   static constexpr int NCH = D / 8;                // 16-byte chunks per row
   static constexpr int TK = TKO ? TKO : (D >= 512 ? 16 : (D >= 256 ? 32 : SDPA_DECODE16_TK128 * 128 / D));
   static constexpr int TILE = TK * RB;             // bytes of the K (or V) tile
-  static constexpr int NST = D >= 256 ? SDPA_DECODE16_STAGES_LARGE : SDPA_DECODE16_STAGES;
+  static constexpr int NST = NSTO ? NSTO : (D >= 256 ? SDPA_DECODE16_STAGES_LARGE : SDPA_DECODE16_STAGES);
   static constexpr int STAGE = 2 * TILE;
   static constexpr int LINES = TILE / 1024;        // 1 KiB load lines per K (or V) tile
   static constexpr int LPW = 2 * LINES / NWV;      // load instructions per wave per tile
@@ -472,6 +472,21 @@ struct Dec16 {
   static_assert(LINES % NWV == 0 && LINES >= NWV, "tile lines");
   static_assert(NST >= 2 && (NST - 2) * LPW < 64, "ring depth");
 };
+
+// Wait until at most rem later tiles' direct loads (LPW per tile) are in
+// flight: the oldest tile has landed.  R (the ring's spare depth) bounds rem.
+template <int LPW, int R>
+__device__ inline void wait_ring(int rem) {
+  if constexpr (R > 0) {
+    if (rem >= R) {
+      wait_vmcnt<R * LPW>();
+      return;
+    }
+    wait_ring<LPW, R - 1>(rem);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
 
 // chunk swizzle of a row (both K and V): low chunk bits ^= f(row)
 template <int NCH>
@@ -485,11 +500,13 @@ __device__ constexpr int chunk_swz(int row) { return NCH >= 16 ? (row & 15) : ((
 // every wave its own 16 columns and all O^T rows.  With CPW > 1 the tiles are
 // a multiple of 32 keys (at D = 512: 32 keys, 128 KiB of LDS) and P.V runs as
 // 16x16x32 products, 32 keys per step, at the full matrix rate.
-template <class T, int D, bool MASK, bool SPLIT, int CPW = 1>
+// NSTO (ring stages, 0 = default) deepens the ring where a grid of at most
+// one workgroup per compute unit leaves LDS to spare.
+template <class T, int D, bool MASK, bool SPLIT, int CPW = 1, int NSTO = 0>
 __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode16_kernel(AttnParams p) {
   constexpr int NW = CPW > kWaves ? CPW : kWaves;  // waves per workgroup
   constexpr int WPB = NW / CPW;                     // waves per 16-column block
-  using C = Dec16<D, (CPW > 1 && D >= 512 ? 32 : 0), NW>;
+  using C = Dec16<D, (CPW > 1 && D >= 512 ? 32 : 0), NW, NSTO>;
   using S = uint16_t;
   static_assert(CPW == 1 || C::NBLK % 2 == 0, "32-key products");
   constexpr int NOB = D / 16 / WPB;  // O^T row blocks per wave
@@ -600,9 +617,7 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
   for (int t = 0; t < ntiles; ++t) {
     // this wave's loads of tile t have landed once at most `rem` later tiles remain
     const int rem = min(C::NST - 2, ntiles - 1 - t);
-    if constexpr (C::NST >= 4) { if (rem >= 2) wait_vmcnt<2 * C::LPW>(); }
-    if constexpr (C::NST >= 3) { if (rem == 1) wait_vmcnt<C::LPW>(); }
-    if (rem <= 0) wait_vmcnt<0>();
+    wait_ring<C::LPW, C::NST - 2>(rem);
     lds_barrier();  // ... and every wave's; tile t - 1 is no longer read
     const int j0 = kbeg + t * C::TK;
     // this tile's mask values were loaded in the previous iteration; the next
@@ -854,11 +869,31 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(AttnParams p) {
   }
 }
 
+#ifndef SDPA_DECODE_DEEP_RING_MAX_WG
+#define SDPA_DECODE_DEEP_RING_MAX_WG 256
+#endif
+#ifndef SDPA_DECODE_DEEP_STAGES
+#define SDPA_DECODE_DEEP_STAGES 4
+#endif
+constexpr int kDeepStages = SDPA_DECODE_DEEP_STAGES;
 template <class T, int D, bool SPLIT>
 void launch16(const AttnParams& p, int cpw, bool mask, dim3 grid, hipStream_t s) {
   const dim3 block(kThreads);  // four waves for CPW <= 4
+  // At D >= 256 a stage holds 32 KiB of K and V.  A grid that fits one
+  // workgroup per compute unit keeps only the one workgroup's loads in
+  // flight per CU, so it gets a four-stage ring (128 KiB: three tiles in
+  // flight); larger grids keep two stages and two workgroups per CU.
+  constexpr bool kDeep = D >= 256;
+  const bool deep = kDeep && grid.x <= (unsigned)SDPA_DECODE_DEEP_RING_MAX_WG;
   switch (cpw) {
     case 1:
+      if constexpr (kDeep) {
+        if (deep) {
+          if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, SPLIT, 1, kDeepStages>), grid, block, 0, s, p);
+          else hipLaunchKernelGGL((decode16_kernel<T, D, false, SPLIT, 1, kDeepStages>), grid, block, 0, s, p);
+          break;
+        }
+      }
       if (mask) hipLaunchKernelGGL((decode16_kernel<T, D, true, SPLIT, 1>), grid, block, 0, s, p);
       else hipLaunchKernelGGL((decode16_kernel<T, D, false, SPLIT, 1>), grid, block, 0, s, p);
       break;

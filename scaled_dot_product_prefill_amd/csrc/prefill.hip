@@ -380,12 +380,15 @@ __device__ constexpr int swz_k(int row) { return NCH >= 16 ? (row & 15) : ((row 
 template <int NCH>
 __device__ constexpr int swz_v(int row) { return NCH >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
-// Row sum of two packed 16-bit probabilities, accumulated in fp32.
-__device__ inline float dot2_ones(TF16, uint32_t pk, float acc) {
-  typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2, pk), __builtin_bit_cast(h2, 0x3C003C00u), acc, false);
-}
-__device__ inline float dot2_ones(TBF16, uint32_t pk, float acc) {
+// Row-sum contribution of one packed pair of probabilities (p0, p1), in fp32.
+// fp16 adds the fp32 values themselves: two plain adds cost less VALU time
+// than one v_dot2 beside the matrix cores, and against the fp16-rounded
+// values P.V multiplies they differ by at most 2^-11 relative per term
+// (about 2^-11 / sqrt(keys) on the sum).  bf16 keeps the sum of the rounded
+// values (v_dot2 against ones): its 2^-9 rounding would otherwise show in
+// rows that average a few hundred keys.
+__device__ inline float row_sum2(TF16, uint32_t, float p0, float p1, float acc) { return acc + (p0 + p1); }
+__device__ inline float row_sum2(TBF16, uint32_t pk, float, float, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, 0x3F803F80u),
                                          acc, false);
 }
@@ -601,8 +604,8 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   };
   // P = exp2(S cs - m) (interior) or exp2(S - m) (edge, already scaled), packed
   // as the B operands of P.V: k-step u of block kb <-> accumulator rows 8u..8u+7.
-  // Without the split the row sum adds the packed (rounded) probabilities,
-  // the values P.V multiplies.
+  // Without the split the row sum is row_sum2's (bf16: the rounded values
+  // P.V multiplies).
   auto probs = [&](f32x16* sc, u32x4 (&hi)[C::NKB][2], u32x4 (&lo)[C::NKB][2], auto edge_tag,
                    bool split) {
     constexpr bool EDGE = decltype(edge_tag)::value;
@@ -626,7 +629,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
             l_run += p0 + p1;
           } else {
             hi[kb][u][e] = cvt_pk(T{}, p0, p1);
-            l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
+            l_run = row_sum2(T{}, hi[kb][u][e], p0, p1, l_run);
           }
         }
     }
@@ -724,7 +727,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     auto ec_c = [&](int it) {
       const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
       hi[kb][u][e] = cvt_pk(T{}, ps[it][0], ps[it][1]);
-      l_run = dot2_ones(T{}, hi[kb][u][e], l_run);
+      l_run = row_sum2(T{}, hi[kb][u][e], ps[it][0], ps[it][1], l_run);
     };
     // v_max3 written out: fmaxf on matrix-core results would first quieten
     // each operand (two extra VALU ops), and volatile keeps it in its slot.

@@ -181,8 +181,16 @@ def test_split_plan(lib):
     a = _sizes(8, 32, 8, 131072, 128, sdpa.BF16)
     assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
     assert lib.sdpa_decode_workspace_bytes(ctypes.byref(a), 0) == 8 * 32 * 64 * 130 * 4
-    # GQA-8 D512, B2, Lk=32768 (2048 tiles of 16 keys): 32 -> 64 splits
+    # GQA-8 D512, B2, Lk=32768 (2048 tiles of 16 keys): 16-bit head dim 512
+    # stays at one workgroup per CU (the four-stage ring): 8 units x 32 splits
     a = _sizes(2, 32, 4, 32768, 512, sdpa.F16)
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 32
+    # ... and three units aim at floor(256 / 3) = 85 splits: 2048 tiles give
+    # ceil(2048 / 85) = 25 tiles (400 keys) per split, 82 splits, 246 workgroups
+    a = _sizes(1, 24, 3, 32768, 512, sdpa.BF16)
+    assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 82
+    # fp32 at head dim 512 keeps doubling: 32 -> 64 splits
+    a = _sizes(2, 32, 4, 32768, 512, sdpa.F32)
     assert lib.sdpa_decode_num_splits(ctypes.byref(a), 0) == 64
     # GQA-8 D=512, B=1, Lk=1024: one 16-key tile per split
     a = _sizes(1, 32, 4, 1024, 512, sdpa.F16)
