@@ -380,6 +380,28 @@ __device__ constexpr int swz_k(int row) { return NCH >= 16 ? (row & 15) : ((row 
 template <int NCH>
 __device__ constexpr int swz_v(int row) { return NCH >= 16 ? 4 * (row & 3) : 4 * ((row >> 1) & 1); }
 
+// Two packed fp16 values.  By value: a bit-cast applied directly to an
+// element of an ext_vector_type expression does not select the element on
+// this compiler.
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+__device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
+
+// max(a, b) over this lane and lane ^ 32, written out so that no operand is
+// first quietened (fmaxf would add one move per operand): the two halves of
+// the wave trade places with v_permlane32_swap.
+__device__ inline float max2_xor32(float a, float b) {
+  float m, t;
+  asm volatile(
+      "v_max_f32 %0, %2, %3\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "=&v"(m), "=&v"(t)
+      : "v"(a), "v"(b));
+  return m;
+}
+
 // Row-sum contribution of one packed pair of probabilities (p0, p1), in fp32.
 // fp16 adds the fp32 values themselves: two plain adds cost less VALU time
 // than one v_dot2 beside the matrix cores, and against the fp16-rounded
@@ -519,17 +541,22 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     const int rows = min(lk - j0, C::BN);
     return (uint32_t)(rows - 1) * rowb + real_rb;
   };
-  auto issue = [&](const S* base, int64_t rs, uint32_t rowb, uint32_t real_rb, const uint32_t* off, int noff,
-                   uint32_t step, uint8_t* st, int t) {
+  // a full tile's byte count, once (uniform)
+  const uint32_t kfull = __builtin_amdgcn_readfirstlane((C::BN - 1) * krow + 2 * p.Dqk);
+  const uint32_t vfull = __builtin_amdgcn_readfirstlane((C::BN - 1) * vrow + 2 * p.Dv);
+  auto issue = [&](const S* base, int64_t rs, uint32_t rowb, uint32_t real_rb, uint32_t full, const uint32_t* off,
+                   int noff, uint32_t step, uint8_t* st, int t) {
     const int j0 = t * C::BN;
     const S* tb = base + (int64_t)j0 * rs;
-    const uint32_t nb = tile_bytes(j0, rowb, real_rb);
+    const uint32_t nb = j0 + C::BN <= lk ? full : tile_bytes(j0, rowb, real_rb);
     const uint32_t la = lds_addr(st) + wave * 1024;
 #pragma unroll
     for (int i = 0; i < C::LPW; ++i) dma16(tb, nb, la + NW * i * 1024, off[i % noff], i * step);
   };
-  auto issue_k = [&](int t, uint8_t* st) { issue(kbase, p.ks[2], krow, 2 * p.Dqk, koff, C::KVAR, kstep, st, t); };
-  auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, 2 * p.Dv, &voff, 1, vstep, st, t); };
+  auto issue_k = [&](int t, uint8_t* st) {
+    issue(kbase, p.ks[2], krow, 2 * p.Dqk, kfull, koff, C::KVAR, kstep, st, t);
+  };
+  auto issue_v = [&](int t, uint8_t* st) { issue(vbase, p.vs[2], vrow, 2 * p.Dv, vfull, &voff, 1, vstep, st, t); };
 
   // ---- per-lane LDS read offsets
   const uint32_t k_lane = l32 * C::RB;                 // + (32 kb) rows
@@ -724,10 +751,21 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       ps[it][0] = fast_exp2(kRel ? cur[kb][8 * u + 2 * e] : xs[it][0]);
       ps[it][1] = fast_exp2(kRel ? cur[kb][8 * u + 2 * e + 1] : xs[it][1]);
     };
+    // The pre-scaled fp16 form sums the packed fp16 probabilities the P.V
+    // products multiply in two fp16 pairs (one add per two probabilities),
+    // folded into the fp32 row sum once per tile: 16 values of at most 2^8
+    // per pair, each add rounded to 11 bits (at most 2^-11 x 16 relative on a
+    // tile's sum, about 2^-11 / sqrt(keys) on the row's after the rounding of
+    // independent tiles averages).
+    h2 lh[2];
     auto ec_c = [&](int it) {
       const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
       hi[kb][u][e] = cvt_pk(T{}, ps[it][0], ps[it][1]);
-      l_run = row_sum2(T{}, hi[kb][u][e], ps[it][0], ps[it][1], l_run);
+      if constexpr (kRel) {
+        if (it < 2) lh[it] = as_h2(hi[kb][u][e]);
+        else lh[it & 1] += as_h2(hi[kb][u][e]);
+      }
+      else l_run = row_sum2(T{}, hi[kb][u][e], ps[it][0], ps[it][1], l_run);
     };
     // v_max3 written out: fmaxf on matrix-core results would first quieten
     // each operand (two extra VALU ops), and volatile keeps it in its slot.
@@ -765,8 +803,12 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       for (int it = x_begin(i); it < x_begin(i + 1); ++it) x_item(it);
       __builtin_amdgcn_sched_barrier(0);
     }
-    const float mx = fmaxf(mx2[0], mx2[1]);
-    return kRel ? max_xor32(mx) : max_xor32(mx) * c;
+    if constexpr (kRel) {
+      const h2 t = lh[0] + lh[1];
+      l_run += (float)t[0] + (float)t[1];
+    }
+    const float mx = max2_xor32(mx2[0], mx2[1]);
+    return kRel ? mx : mx * c;
   };
 
   // ---- pipeline.  Tile t lives in stage t & 1 of both rings.  Iteration t
