@@ -402,15 +402,13 @@ __device__ inline float max2_xor32(float a, float b) {
   return m;
 }
 
-// Row-sum contribution of one packed pair of probabilities (p0, p1), in fp32.
-// fp16 adds the fp32 values themselves: two plain adds cost less VALU time
-// than one v_dot2 beside the matrix cores, and against the fp16-rounded
-// values P.V multiplies they differ by at most 2^-11 relative per term
-// (about 2^-11 / sqrt(keys) on the sum).  bf16 keeps the sum of the rounded
-// values (v_dot2 against ones): its 2^-9 rounding would otherwise show in
-// rows that average a few hundred keys.
-__device__ inline float row_sum2(TF16, uint32_t, float p0, float p1, float acc) { return acc + (p0 + p1); }
-__device__ inline float row_sum2(TBF16, uint32_t pk, float, float, float acc) {
+// Row-sum contribution of one packed pair of probabilities, in fp32: a v_dot2
+// of the packed (rounded) values P.V multiplies against ones.  The steady
+// loop of steady_slots picks its own form per type and masking.
+__device__ inline float row_sum2(TF16, uint32_t pk, float acc) {
+  return __builtin_amdgcn_fdot2(as_h2(pk), as_h2(0x3C003C00u), acc, false);
+}
+__device__ inline float row_sum2(TBF16, uint32_t pk, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk), __builtin_bit_cast(bf16x2, 0x3F803F80u),
                                          acc, false);
 }
@@ -656,7 +654,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
             l_run += p0 + p1;
           } else {
             hi[kb][u][e] = cvt_pk(T{}, p0, p1);
-            l_run = row_sum2(T{}, hi[kb][u][e], p0, p1, l_run);
+            l_run = row_sum2(T{}, hi[kb][u][e], l_run);
           }
         }
     }
@@ -751,21 +749,29 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       ps[it][0] = fast_exp2(kRel ? cur[kb][8 * u + 2 * e] : xs[it][0]);
       ps[it][1] = fast_exp2(kRel ? cur[kb][8 * u + 2 * e + 1] : xs[it][1]);
     };
-    // The pre-scaled fp16 form sums the packed fp16 probabilities the P.V
-    // products multiply in two fp16 pairs (one add per two probabilities),
+    // Row sum.  Without causal masking fp16 takes the cheapest VALU form:
+    // the exact-scale path adds the two fp32 probabilities themselves
+    // (against the fp16-rounded values P.V multiplies they differ by at most
+    // 2^-11 relative per term); the pre-scaled path sums the packed fp16
+    // probabilities in two fp16 pairs (one add per two probabilities),
     // folded into the fp32 row sum once per tile: 16 values of at most 2^8
     // per pair, each add rounded to 11 bits (at most 2^-11 x 16 relative on a
     // tile's sum, about 2^-11 / sqrt(keys) on the row's after the rounding of
-    // independent tiles averages).
+    // independent tiles averages).  With causal masking one v_dot2 of the
+    // packed pair against ones into the fp32 sum measured 3-4 % faster on
+    // both paths (the masked kernel schedules the slots differently), and
+    // bf16 always sums the rounded values that way: its 2^-9 rounding would
+    // otherwise show in rows of a few hundred keys.
     h2 lh[2];
     auto ec_c = [&](int it) {
       const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
       hi[kb][u][e] = cvt_pk(T{}, ps[it][0], ps[it][1]);
-      if constexpr (kRel) {
+      if constexpr (kRel && !CAUSAL) {
         if (it < 2) lh[it] = as_h2(hi[kb][u][e]);
         else lh[it & 1] += as_h2(hi[kb][u][e]);
       }
-      else l_run = row_sum2(T{}, hi[kb][u][e], ps[it][0], ps[it][1], l_run);
+      else if constexpr (std::is_same<T, TF16>::value && !CAUSAL) l_run += ps[it][0] + ps[it][1];
+      else l_run = row_sum2(T{}, hi[kb][u][e], l_run);
     };
     // v_max3 written out: fmaxf on matrix-core results would first quieten
     // each operand (two extra VALU ops), and volatile keeps it in its slot.
@@ -803,7 +809,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       for (int it = x_begin(i); it < x_begin(i + 1); ++it) x_item(it);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (kRel) {
+    if constexpr (kRel && !CAUSAL) {
       const h2 t = lh[0] + lh[1];
       l_run += (float)t[0] + (float)t[1];
     }
