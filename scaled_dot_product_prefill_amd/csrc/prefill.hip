@@ -372,6 +372,14 @@ struct Cfg16 {
 // below 2^8, and O = sum(p v) / sum(p) is unchanged by which max is used.
 constexpr float kRescaleSlack = 8.f;
 
+// Fast pass of the pre-scaled fp16 form (steady tiles only): no row max is
+// taken before the exponentials; each tile's row sum is checked afterwards.
+// Every probability is at most that sum, so a finite sum means each was a
+// finite fp16 value.  A row sum of kFastSumMax or more moves the reference
+// max by its log2; one that is not finite sends the workgroup through the
+// tiles again with the max taken before every exponential.
+constexpr float kFastSumMax = 16384.f;
+
 // 16-byte chunk swizzles of the unpadded LDS rows (low chunk bits ^= f(row)):
 // K: the Q.K^T operand read touches 16 consecutive rows in one chunk;
 // V: a transposed read touches 8 rows x 4 consecutive chunks.
@@ -694,7 +702,24 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // spaced by a few VALU ops lets both units run at once; a run of
   // back-to-back matrix ops stalls the VALU of the other wave on the SIMD.
   f32x16 mneg;
-  auto steady_slots = [&](const uint8_t* Kst, const uint8_t* Vst, f32x16* cur, f32x16* nxt) -> float {
+  bool bad = false;  // fast pass: a tile's row sum was not finite (wave-uniform)
+  // update_max in relative units; S'(t+1) follows the moved max
+  auto rel_move = [&](float mx, f32x16* nxt) {
+    if (__any(mx > kRescaleSlack)) {
+      const float d = fmaxf(mx, 0.f);
+      const float corr = fast_exp2(-d);
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
+      l_run *= corr;
+      m_run += d;
+#pragma unroll
+      for (int kb = 0; kb < C::NKB; ++kb) nxt[kb] -= d;
+      mneg = -m_run;
+    }
+  };
+  auto steady_slots = [&](auto fast_tag, const uint8_t* Kst, const uint8_t* Vst, f32x16* cur,
+                          f32x16* nxt) -> float {
+    constexpr bool kFast = decltype(fast_tag)::value;
     constexpr int NQK = C::NKB * C::NQ;
     constexpr int GOPS = C::NMB;
     constexpr int NOPS = NQK + C::NKB * 2 * GOPS;
@@ -763,6 +788,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     // bf16 always sums the rounded values that way: its 2^-9 rounding would
     // otherwise show in rows of a few hundred keys.
     h2 lh[2];
+    float lsum = 0.f;  // fast pass under causal masking: this tile's row sum
     auto ec_c = [&](int it) {
       const int kb = it / 8, u = (it % 8) / 4, e = it % 4;
       hi[kb][u][e] = cvt_pk(T{}, ps[it][0], ps[it][1]);
@@ -771,6 +797,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
         else lh[it & 1] += as_h2(hi[kb][u][e]);
       }
       else if constexpr (std::is_same<T, TF16>::value && !CAUSAL) l_run += ps[it][0] + ps[it][1];
+      else if constexpr (kFast) lsum = row_sum2(T{}, hi[kb][u][e], lsum);
       else l_run = row_sum2(T{}, hi[kb][u][e], l_run);
     };
     // v_max3 written out: fmaxf on matrix-core results would first quieten
@@ -778,6 +805,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     // Two running maxima halve the dependent chain.
     float mx2[2] = {kNegInf, kNegInf};
     auto x_item = [&](int it) {
+      if constexpr (kFast) return;
       const int kb = it / 8, r = 2 * (it % 8);
       float& m = mx2[it & 1];
       asm volatile("v_max3_f32 %0, %1, %2, %3" : "=v"(m) : "v"(m), "v"(nxt[kb][r]), "v"(nxt[kb][r + 1]));
@@ -787,6 +815,17 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     auto ec_begin = [](int i) { return i >= EC_END ? NEC : (i * NEC + EC_END - 1) / EC_END; };
     auto x_begin = [](int i) {
       return i <= X_BEG ? 0 : (i >= NOPS ? NX : ((i - X_BEG) * NX + (NOPS - X_BEG) - 1) / (NOPS - X_BEG));
+    };
+    // this tile's row sum over the lane's keys, once every EC item is done
+    float lt = 0.f;
+    unsigned long long trig = 0;  // fast pass: lanes whose sum reached kFastSumMax
+    auto tile_sum = [&]() {
+      if constexpr (kRel && !CAUSAL) {
+        const h2 t = lh[0] + lh[1];
+        lt = (float)t[0] + (float)t[1];
+      } else {
+        lt = lsum;
+      }
     };
 #pragma unroll
     for (int i = 0; i < W && i < NOPS; ++i) load_op(i);
@@ -807,12 +846,28 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       for (int it = ec_begin(i); it < ec_begin(i + 1); ++it) ec_c(it);
 #pragma unroll
       for (int it = x_begin(i); it < x_begin(i + 1); ++it) x_item(it);
+      // fast pass: the sum and its check in the slots the row max would
+      // take; after the last slot only a scalar branch remains
+      if constexpr (kFast) {
+        if (i == X_BEG) tile_sum();
+        if (i == X_BEG + 1) l_run += lt;
+        if (i == X_BEG + 2) trig = __ballot(!(lt < kFastSumMax));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if constexpr (kRel && !CAUSAL) {
-      const h2 t = lh[0] + lh[1];
-      l_run += (float)t[0] + (float)t[1];
+    if constexpr (!kFast) tile_sum();
+    if constexpr (kFast) {
+      static_assert(X_BEG + 2 < NOPS, "slots for the fast pass's check");
+      if (__builtin_expect(trig != 0, 0)) {
+        // (rare) the reference max moves by log2 of the row's tile sum, the
+        // same for both halves of a row, so that the tile's sum becomes 1
+        const float lr = lt + __shfl_xor(lt, 32, 64);
+        if (__any(!(lr < -kNegInf))) bad = true;
+        rel_move(fast_log2(lr), nxt);
+      }
+      return kNegInf;  // nothing left for the caller to move
     }
+    if constexpr (kRel && !CAUSAL) l_run += lt;
     const float mx = max2_xor32(mx2[0], mx2[1]);
     return kRel ? mx : mx * c;
   };
@@ -825,14 +880,21 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // V loads and the workgroup's barriers, in the same order as the others,
   // and leaves its rows empty.  Its SIMD time goes to the waves beside it.
   const bool idle = iw >= lq;
-  if (idle) {
-    if (ntiles > 0) {
-      issue_k(0, Kring);
-      if (ntiles > 1) issue_k(1, Kring + C::TILE);
-      issue_v(0, Vring);
-      wait_vmcnt<0>();
-      lds_barrier();
-    }
+  // The pre-scaled form at D <= 128 takes the fast pass first; a workgroup
+  // where it met a tile out of range (kFastSumMax) takes the checked pass.
+  constexpr bool kTwoPass = kRel && D <= 128;
+  __shared__ int wg_bad;
+  if (kTwoPass && tid == 0) wg_bad = 0;  // ordered before any vote by the tile barriers
+  // K(0), K(1) and V(0) in flight and landed
+  auto prologue = [&]() {
+    issue_k(0, Kring);
+    if (ntiles > 1) issue_k(1, Kring + C::TILE);
+    issue_v(0, Vring);
+    wait_vmcnt<0>();
+    lds_barrier();
+  };
+  auto idle_pass = [&]() {
+    if (ntiles > 0) prologue();
     for (int t = 0; t < ntiles; ++t) {
       const int par = t & 1;
       wait_vmcnt<0>();
@@ -840,56 +902,46 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
       if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
     }
-  } else {
-    f32x16 sa[C::NKB], sb[C::NKB];
+  };
+  f32x16 sa[C::NKB], sb[C::NKB];
+  auto first_tile = [&]() {
     if (ntiles > 0) {
-      issue_k(0, Kring);
-      if (ntiles > 1) issue_k(1, Kring + C::TILE);
-      issue_v(0, Vring);
-      wait_vmcnt<0>();
-      lds_barrier();
+      prologue();
       qk(Kring, sa);
       update_max(0 < n_int ? tile_max(0, sa, std::false_type{}) : tile_max(0, sa, std::true_type{}));
     }
+  };
+  auto general = [&](int t, auto edge_tag) {
+    const int par = t & 1;
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
+    if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
+    u32x4 hi[C::NKB][2], lo[C::NKB][2];
+    probs(sa, hi, lo, edge_tag, split_p);
+    pv(Vring + par * C::TILE, hi, lo, split_p);
+    if (t + 1 < ntiles) {
+      qk(Kring + (par ^ 1) * C::TILE, sa);
+      update_max(t + 1 < n_int ? tile_max(t + 1, sa, std::false_type{})
+                               : tile_max(t + 1, sa, std::true_type{}));
+    }
+  };
+  if (idle) {
+    idle_pass();
+  } else {
+    first_tile();
     // steady state (tiles t, t+1 interior, tile t+2 exists, single bf16 P): no
     // branch between the barrier and the max update, stage offsets fixed by
     // the parity of t, so matrix-core and VALU work of the two tiles interleave
-    auto steady = [&](int t, auto par_tag, f32x16* cur, f32x16* nxt) {
+    auto steady = [&](auto fast_tag, int t, auto par_tag, f32x16* cur, f32x16* nxt) {
       constexpr int PAR = decltype(par_tag)::value;
       wait_vmcnt<0>();
       lds_barrier();
       issue_v(t + 1, Vring + (PAR ^ 1) * C::TILE);
       issue_k(t + 2, Kring + PAR * C::TILE);
-      const float mx = steady_slots(Kring + (PAR ^ 1) * C::TILE, Vring + PAR * C::TILE, cur, nxt);
-      if constexpr (!kRel) {
-        update_max(mx);
-      } else if (__any(mx > kRescaleSlack)) {
-        // update_max in relative units; S'(t+1) follows the moved max
-        const float d = fmaxf(mx, 0.f);
-        const float corr = fast_exp2(-d);
-  #pragma unroll
-        for (int mb = 0; mb < C::NMB; ++mb) acc[mb] *= corr;
-        l_run *= corr;
-        m_run += d;
-  #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) nxt[kb] -= d;
-        mneg = -m_run;
-      }
-    };
-    auto general = [&](int t, auto edge_tag) {
-      const int par = t & 1;
-      wait_vmcnt<0>();
-      lds_barrier();
-      if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
-      if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
-      u32x4 hi[C::NKB][2], lo[C::NKB][2];
-      probs(sa, hi, lo, edge_tag, split_p);
-      pv(Vring + par * C::TILE, hi, lo, split_p);
-      if (t + 1 < ntiles) {
-        qk(Kring + (par ^ 1) * C::TILE, sa);
-        update_max(t + 1 < n_int ? tile_max(t + 1, sa, std::false_type{})
-                                 : tile_max(t + 1, sa, std::true_type{}));
-      }
+      const float mx = steady_slots(fast_tag, Kring + (PAR ^ 1) * C::TILE, Vring + PAR * C::TILE, cur, nxt);
+      if constexpr (!kRel) update_max(mx);
+      else if constexpr (!decltype(fast_tag)::value) rel_move(mx, nxt);  // the fast pass moved it itself
     };
     int t = 0;
     if constexpr (D <= 128) {
@@ -900,16 +952,20 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += mneg;
       }
-      for (; t + 1 < n_steady; t += 2) {
-        steady(t, std::integral_constant<int, 0>{}, sa, sb);
-        steady(t + 1, std::integral_constant<int, 1>{}, sb, sa);
-      }
-      if (t < n_steady) {
-        steady(t, std::integral_constant<int, 0>{}, sa, sb);
-  #pragma unroll
-        for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
-        ++t;
-      }
+      auto run_steady = [&](auto fast_tag) {
+        for (; t + 1 < n_steady; t += 2) {
+          steady(fast_tag, t, std::integral_constant<int, 0>{}, sa, sb);
+          steady(fast_tag, t + 1, std::integral_constant<int, 1>{}, sb, sa);
+        }
+        if (t < n_steady) {
+          steady(fast_tag, t, std::integral_constant<int, 0>{}, sa, sb);
+    #pragma unroll
+          for (int kb = 0; kb < C::NKB; ++kb) sa[kb] = sb[kb];
+          ++t;
+        }
+      };
+      if constexpr (kTwoPass) run_steady(std::true_type{});
+      else run_steady(std::false_type{});
       if (kRel && n_steady > 0) {
   #pragma unroll
         for (int kb = 0; kb < C::NKB; ++kb) sa[kb] += m_run;
@@ -917,6 +973,25 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     }
     for (; t < n_int; ++t) general(t, std::false_type{});
     for (; t < ntiles; ++t) general(t, std::true_type{});
+  }
+  if constexpr (kTwoPass) {
+    if (bad && lane == 0) wg_bad = 1;
+    __syncthreads();  // also: every wave is past its last read of the rings
+    if (wg_bad) {
+      // the checked pass: every tile again, on the general path (row max first)
+  #pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) acc[mb] = f32x16{};
+      m_run = kNegInf;
+      l_run = 0.f;
+      if (idle) {
+        idle_pass();
+      } else {
+        first_tile();
+        int t = 0;
+        for (; t < n_int; ++t) general(t, std::false_type{});
+        for (; t < ntiles; ++t) general(t, std::true_type{});
+      }
+    }
   }
 
   // ---- epilogue (padding rows see no key) ----

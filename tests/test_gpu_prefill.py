@@ -186,6 +186,32 @@ def test_running_max_moves(dtype, D):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("jump", [10.0, 30.0, 200.0])
+def test_fp16_score_jump_inside_the_steady_tiles(causal, D, jump):
+    # Without a log-sum-exp, fp16 takes the steady tiles without a row max
+    # and checks each tile's row sum afterwards.  Key 150 (a steady tile of
+    # every workgroup, causal or not) is made to lift the score of query 300
+    # by `jump` nats over its first tile's maximum; along that direction it
+    # also moves the other rows' scores by up to several times as much, either
+    # way.  Rows whose tile sum passes 2^14 but stays finite move the
+    # reference max in the fast pass; rows whose probabilities overflow fp16
+    # (or, at 200, fp32's exponential) send their workgroup through the
+    # tiles again with the max taken first.
+    x = random_case(2020 + D, 1, 2, 2, 640, 640, D, "fp16")
+    q, k = x["q"].float(), x["k"].float()
+    i, j = 300, 150
+    qn = q[0, 0, i] / q[0, 0, i].norm()
+    # score(i, j) = scale q_i . k_j = jump + (a typical first-tile maximum)
+    target = jump + 3.0
+    k[0, 0, j] = qn * target * math.sqrt(D) / q[0, 0, i].norm()
+    x["k"] = k.half()
+    x["q"] = q.half()
+    out, _, sc = _run(x, "fp16", causal=causal, lse=False)
+    compare_full(out, None, x, sc, "fp16", f"score jump {jump} D{D} causal={causal}", causal=causal)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 def test_fp16_scale_above_one_log2_unit(causal):
     # |scale| log2(e) > 1: Q is not pre-multiplied and every tile takes the
     # general path
