@@ -73,21 +73,32 @@ constexpr int kDkvKeys = 32 * kDkvWaves;
 // (4 waves) swap the two 2-bit halves of row % 16, which keeps both patterns
 // free of conflicts (measured: transposed reads take 0.39x the time of the
 // plain row % 16 swizzle, row reads the same).  The dK / dV kernel's tiles (8
-// waves) keep row % 16, whose transposed reads conflict 4 ways: the swapped
-// form's extra address registers raised that kernel's register spills and it
-// ran 10 % slower overall.
+// waves) at D = 64 keep row % 16, whose transposed reads conflict 4 ways (the
+// swapped form's extra address registers raised that kernel's spills).  At
+// D = 128 they are padded instead (PAD): rows of 320 bytes, so each row
+// starts 4 chunks further round the banks, with chunks swizzled by
+// (row / 4) % 4 in their low two bits.  A transposed read then covers all 16
+// bank groups (rows by the padding, chunks by themselves), and so does a row
+// read (low bits by the swizzle, high bits by the padding), while a chunk's
+// offset stays additive in the column block: no extra address registers.
 template <int D, int NW = kBwdWaves>
 struct Tile64 {
+  static constexpr bool PAD = NW == kDkvWaves && D == 128;
   static constexpr int ROWS = 64;
-  static constexpr int RB = D * 2;                      // row bytes
   static constexpr int NCH = D / 8;                     // 16-byte chunks per row
+  static constexpr int RB = D * 2 + (PAD ? 64 : 0);     // row bytes
   static constexpr int BYTES = ROWS * RB;
   static constexpr int LINES = BYTES / 1024;
-  static constexpr int LPW = LINES / NW;                // lines per wave
-  static constexpr int STEP_ROWS = NW * 64 / NCH;       // rows between a wave's lines
-  static_assert(LINES % NW == 0 && STEP_ROWS % 16 == 0, "tile lines");
+  // unpadded: wave w fills lines w, w + NW, ... (LPW of them, STEP_ROWS rows
+  // apart); padded: a 1 KiB line holds 3.2 rows, so the lines' patterns
+  // repeat every 5 lines (16 rows), and waves 0..4 fill lines w, w + 5, w + 10
+  // and w + 15
+  static constexpr int LPW = PAD ? 4 : LINES / NW;      // lines per loading wave
+  static constexpr int STEP_ROWS = PAD ? 16 : NW * 64 / NCH;
+  static_assert(PAD ? LINES == 20 : (LINES % NW == 0 && STEP_ROWS % 16 == 0), "tile lines");
   __device__ static constexpr int swz(int row) {
-    if constexpr (NW == kDkvWaves) return NCH >= 16 ? (row & 15) : ((row >> 1) & 7);
+    if constexpr (PAD) return (row >> 2) & 3;
+    else if constexpr (NW == kDkvWaves) return NCH >= 16 ? (row & 15) : ((row >> 1) & 7);
     else return NCH >= 16 ? (((row & 3) << 2) | ((row >> 2) & 3)) : ((((row >> 1) & 1) << 2) | ((row >> 2) & 3));
   }
 };
@@ -115,10 +126,18 @@ struct BwdParams {
 template <int D, int NW = kBwdWaves>
 __device__ inline uint32_t tile_lane_off(int wave, int lane, int64_t row_stride_elems, int real_d) {
   using L = Tile64<D, NW>;
-  const int pos = wave * 64 + lane;
-  const int row = pos / L::NCH, pch = pos % L::NCH;
-  const int lch = pch ^ L::swz(row);
-  return lch * 8 < real_d ? (uint32_t)(row * row_stride_elems * 2 + lch * 16) : kNoLoad;
+  if constexpr (L::PAD) {
+    // 20 slots per row, the last 4 padding (they load nothing)
+    const int pos = wave * 64 + lane;
+    const int row = pos / 20, pch = pos % 20;
+    const int lch = pch ^ L::swz(row);
+    return wave < 5 && pch < 16 && lch * 8 < real_d ? (uint32_t)(row * row_stride_elems * 2 + lch * 16) : kNoLoad;
+  } else {
+    const int pos = wave * 64 + lane;
+    const int row = pos / L::NCH, pch = pos % L::NCH;
+    const int lch = pch ^ L::swz(row);
+    return lch * 8 < real_d ? (uint32_t)(row * row_stride_elems * 2 + lch * 16) : kNoLoad;
+  }
 }
 
 // Issue this wave's direct loads of rows [r0, r0 + 64) of a matrix (rows >=
@@ -133,9 +152,16 @@ __device__ inline void tile_issue(const uint16_t* base, int64_t rs, int r0, int 
   const uint32_t rowb = (uint32_t)(rs * 2);
   // no rows: a zero range, so that even the kNoLoad lanes read nothing
   const uint32_t nb = rows > 0 ? (uint32_t)(rows - 1) * rowb + (uint32_t)real_d * 2 : 0u;
+  if constexpr (L::PAD) {
+    if (wave < 5) {
 #pragma unroll
-  for (int i = 0; i < L::LPW; ++i)
-    dma16(tb, nb, lds + (wave + NW * i) * 1024, off, i * L::STEP_ROWS * rowb);
+      for (int i = 0; i < L::LPW; ++i) dma16(tb, nb, lds + (wave + 5 * i) * 1024, off, i * L::STEP_ROWS * rowb);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < L::LPW; ++i)
+      dma16(tb, nb, lds + (wave + NW * i) * 1024, off, i * L::STEP_ROWS * rowb);
+  }
 }
 
 // Matrix-core A operand from a Tile64, row-major: A[m = row rb + lane%32][k =
@@ -161,6 +187,14 @@ __device__ inline u32x4 tile_cols(const uint8_t* t, int rb, int mb, int lane) {
   const uint8_t* p1 = t + (vr + 8) * L::RB + ((ch ^ L::swz(vr + 8)) * 16) + (r16 & 1) * 8;
   const u32x2 a0 = lds_read_tr16(p0), a1 = lds_read_tr16(p1);
   return u32x4{a0[0], a0[1], a1[0], a1[1]};
+}
+
+// v itself, as a value the compiler cannot trace back: what it derives from
+// the result is computed where it is used instead of being kept (or spilled)
+// across a loop
+__device__ inline int fresh(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 // registers 8u .. 8u+7 as bf16 hi + lo pairs (about 16 significant bits)
@@ -381,7 +415,11 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   using L = Tile64<D, kDkvWaves>;
   constexpr int NQ = D / 16, NMB = D / 32;
   constexpr int STAGE = 2 * L::BYTES + 2048;  // Q, dO, LSE line, D line
-  constexpr int VBYTES = kDkvKeys * L::RB;     // the workgroup's value rows
+  // the workgroup's value rows: unpadded, chunks swizzled as in an unpadded
+  // tile (each lane reads back only its own row; 16 rows per pass)
+  constexpr int VRB = D * 2;
+  auto vswz = [](int row) { return D >= 128 ? (row & 15) : ((row >> 1) & 7); };
+  constexpr int VBYTES = kDkvKeys * VRB;
   using S = uint16_t;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + VBYTES];
 
@@ -407,7 +445,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   // same operand order, in this wave's own LDS rows (each lane reads back only
   // what it wrote); both zero past the batch's keys
   u32x4 kreg[NQ];
-  uint8_t* const Vw = smem + 2 * STAGE + 32 * wave * L::RB;
+  uint8_t* const Vw = smem + 2 * STAGE + 32 * wave * VRB;
   {
     const int jj = kok ? my_j : 0;
     const S* kr = (const S*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)jj * p.ks[2];
@@ -418,7 +456,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
       const int ch = 2 * s + g;
       const u32x4 a = ldg16_cached(kr + min(ch, nk - 1) * 8), d = ldg16_cached(vr + min(ch, nv - 1) * 8);
       kreg[s] = kok && ch < nk ? a : u32x4{0, 0, 0, 0};
-      lds_write16(Vw + l32 * L::RB + ((ch ^ L::swz(l32)) * 16), kok && ch < nv ? d : u32x4{0, 0, 0, 0});
+      lds_write16(Vw + l32 * VRB + ((ch ^ vswz(l32)) * 16), kok && ch < nv ? d : u32x4{0, 0, 0, 0});
     }
   }
 
@@ -441,7 +479,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
     const S* db = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1];
     tile_issue<D, kDkvWaves>(qb, p.qs[2], q0, lq, qoff, st, wave, p.Dqk);
     tile_issue<D, kDkvWaves>(db, bp.dos[2], q0, lq, dooff, st + L::BYTES, wave, p.Dv);
-    if (wave == 0) {
+    if (wave == (L::PAD ? 5 : 0)) {  // (padded tiles: a wave that loads no tile lines)
       const int64_t r0 = ((int64_t)b * p.Hq + hq) * p.Lq + q0;
       const uint32_t nb = (uint32_t)min(64, p.Lq - q0) * 4;
       dma16(bp.ws_l + r0, nb, st + 2 * L::BYTES, lane * 16, 0);
@@ -488,14 +526,21 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x16 s_ = f32x16{}, dp = f32x16{};
+        // At D = 128 the per-lane LDS offsets of each phase are derived from
+        // a fresh copy of the lane index.  Held across the loop they do not
+        // fit the registers: they were reloaded from scratch on every tile,
+        // and each reload's wait also waited for the next tile's loads in
+        // flight (measured: causal bf16 8 % faster, GQA-4 15 %).  At D = 64
+        // they fit, and recomputing them cost 4 %.
+        const int lane_a = D >= 128 ? fresh(lane) : lane, l32_a = lane_a & 31, g_a = lane_a >> 5;
         // operand reads run at most two k-steps ahead of the products (a
         // fence every second step), which keeps the wave inside half the
         // register file
 #pragma unroll
         for (int s = 0; s < NQ; ++s) {
-          s_ = mma32(T{}, tile_rows<D, kDkvWaves>(Qs, 32 * qb, s, l32, g), kreg[s], s_);
-          dp = mma32(T{}, tile_rows<D, kDkvWaves>(Ds, 32 * qb, s, l32, g),
-                     lds_read16(Vw + l32 * L::RB + (((2 * s + g) ^ L::swz(l32)) * 16)), dp);
+          s_ = mma32(T{}, tile_rows<D, kDkvWaves>(Qs, 32 * qb, s, l32_a, g_a), kreg[s], s_);
+          dp = mma32(T{}, tile_rows<D, kDkvWaves>(Ds, 32 * qb, s, l32_a, g_a),
+                     lds_read16(Vw + l32_a * VRB + (((2 * s + g_a) ^ vswz(l32_a)) * 16)), dp);
           if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
         f32x16 pr, ds;
@@ -524,6 +569,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
             ds[r] = pv * (dp[r] - d4[e]);
           }
         }
+        const int lane_b = D >= 128 ? fresh(lane) : lane;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const u32x4 db = pack_b<T>(ds, u);
@@ -532,10 +578,10 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
           else pb = pack_b<T>(pr, u);
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
-            const u32x4 da = tile_cols<D, kDkvWaves>(Ds, 32 * qb + 16 * u, mb, lane);
+            const u32x4 da = tile_cols<D, kDkvWaves>(Ds, 32 * qb + 16 * u, mb, lane_b);
             dv[mb] = mma32(T{}, da, pb, dv[mb]);
             if constexpr (SPLIT) dv[mb] = mma32(T{}, da, pl, dv[mb]);
-            dk[mb] = mma32(T{}, tile_cols<D, kDkvWaves>(Qs, 32 * qb + 16 * u, mb, lane), db, dk[mb]);
+            dk[mb] = mma32(T{}, tile_cols<D, kDkvWaves>(Qs, 32 * qb + 16 * u, mb, lane_b), db, dk[mb]);
             if (mb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
           }
         }
