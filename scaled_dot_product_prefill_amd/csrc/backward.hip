@@ -189,14 +189,6 @@ __device__ inline u32x4 tile_cols(const uint8_t* t, int rb, int mb, int lane) {
   return u32x4{a0[0], a0[1], a1[0], a1[1]};
 }
 
-// v itself, as a value the compiler cannot trace back: what it derives from
-// the result is computed where it is used instead of being kept (or spilled)
-// across a loop
-__device__ inline int fresh(int v) {
-  asm volatile("" : "+v"(v));
-  return v;
-}
-
 // registers 8u .. 8u+7 as bf16 hi + lo pairs (about 16 significant bits)
 __device__ inline void pack_b_split(const f32x16& x, int u, u32x4& hi, u32x4& lo) {
 #pragma unroll

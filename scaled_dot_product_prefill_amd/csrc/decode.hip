@@ -576,11 +576,8 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
     }
   };
 
-  // ---- per-lane LDS read offsets
-  const int swk = chunk_swz<C::NCH>(n);                     // K rows 16 blk + n
-  const int vrow = 4 * g4 + (n >> 2);                       // V rows 16 blk + vrow
-  const int swv = chunk_swz<C::NCH>(vrow);
-  const uint32_t vlane = vrow * C::RB + (n & 1) * 8;
+  // (per-lane LDS read offsets: in the tile loop; K rows 16 blk + n, V rows
+  // 16 blk + 4 g4 + n / 4)
 
   f32x4 acc[NOB];
 #pragma unroll
@@ -633,15 +630,25 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
 
     const uint8_t* Ks = ring + (t % C::NST) * C::STAGE;
     const uint8_t* Vs = Ks + C::TILE;
+    // The wide form (CPW > 1) derives its per-lane LDS offsets from a fresh
+    // copy of the lane index every tile: held across the loop they do not
+    // fit its registers, and reloading them from scratch waited on the ring's
+    // loads in flight (the reload's wait counts those too).
+    const int lane_t = CPW > 1 ? fresh(lane) : lane;
+    const int n_t = lane_t & 15, g4_t = lane_t >> 4;
+    const int swk_t = chunk_swz<C::NCH>(n_t);
+    const int vrow_t = 4 * g4_t + (n_t >> 2);
+    const int swv_t = chunk_swz<C::NCH>(vrow_t);
+    const uint32_t vlane_t = vrow_t * C::RB + (n_t & 1) * 8;
     // ---- S^T = K . Q^T
     f32x4 sc[C::NBLK];
 #pragma unroll
     for (int blk = 0; blk < C::NBLK; ++blk) {
       f32x4 s = f32x4{};
-      const uint8_t* krow = Ks + (16 * blk + n) * C::RB;
+      const uint8_t* krow = Ks + (16 * blk + n_t) * C::RB;
 #pragma unroll
       for (int ss = 0; ss < C::NQ; ++ss) {
-        s = mma16(T{}, lds_read16(krow + ((4 * ss + g4) ^ swk) * 16), qreg[ss], s);
+        s = mma16(T{}, lds_read16(krow + ((4 * ss + g4_t) ^ swk_t) * 16), qreg[ss], s);
         // two waves per SIMD hold half the register file: keep the operand
         // reads from being hoisted all at once
         if (CPW > 1 && ss % 4 == 3) __builtin_amdgcn_sched_barrier(0);
@@ -698,12 +705,12 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
             }
           }
         }
-        const uint8_t* vb = Vs + 32 * bp * C::RB + vlane;
+        const uint8_t* vb = Vs + 32 * bp * C::RB + vlane_t;
 #pragma unroll
         for (int i = 0; i < NOB; ++i) {
-          const int lch = 2 * (ob0 + i) + ((n >> 1) & 1);
-          const u32x2 v0 = lds_read_tr16(vb + ((lch ^ swv) * 16));
-          const u32x2 v1 = lds_read_tr16(vb + 16 * C::RB + ((lch ^ swv) * 16));
+          const int lch = 2 * (ob0 + i) + ((n_t >> 1) & 1);
+          const u32x2 v0 = lds_read_tr16(vb + ((lch ^ swv_t) * 16));
+          const u32x2 v1 = lds_read_tr16(vb + 16 * C::RB + ((lch ^ swv_t) * 16));
           const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
           acc[i] = mma16(T{}, va, hi, acc[i]);
           if (split_p) acc[i] = mma16(T{}, va, lo, acc[i]);
@@ -731,11 +738,11 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
           lo = u32x2{l0, l1};
         }
       }
-      const uint8_t* vb = Vs + 16 * blk * C::RB + vlane;
+      const uint8_t* vb = Vs + 16 * blk * C::RB + vlane_t;
 #pragma unroll
       for (int i = 0; i < NOB; ++i) {
-        const int lch = 2 * (ob0 + i) + ((n >> 1) & 1);  // chunk of columns d0 + 4(n%4)
-        const u32x2 va = lds_read_tr16(vb + ((lch ^ swv) * 16));
+        const int lch = 2 * (ob0 + i) + ((n_t >> 1) & 1);  // chunk of columns d0 + 4(n%4)
+        const u32x2 va = lds_read_tr16(vb + ((lch ^ swv_t) * 16));
         acc[i] = mma16k16(T{}, va, hi, acc[i]);
         if (split_p) acc[i] = mma16k16(T{}, va, lo, acc[i]);
       }

@@ -298,6 +298,14 @@ __device__ inline float sum_xor32(float v) {
   return as_float(r[0]) + as_float(r[1]);
 }
 
+// v itself, as a value the compiler cannot trace back: what a loop derives
+// from the result is computed where it is used instead of being kept (or,
+// short of registers, spilled to scratch and reloaded) across iterations
+__device__ inline int fresh(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // exchange with lane l ^ 32 (the other half of the wave)
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32, 64); }
 __device__ inline float xor16(float v) { return __shfl_xor(v, 16, 64); }
