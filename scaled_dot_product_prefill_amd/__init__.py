@@ -28,8 +28,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["prefill", "decode", "decode_num_splits", "decode_workspace_bytes", "prefill_backward",
-           "attention", "SdpaArgs", "SdpaBwdArgs", "library", "library_path", "Status", "SdpaError"]
+__all__ = ["prefill", "decode", "decode_noalloc", "DECODE_SCRATCH_BYTES", "decode_num_splits",
+           "decode_workspace_bytes", "prefill_backward", "attention", "SdpaArgs", "SdpaBwdArgs", "library",
+           "library_path", "Status", "SdpaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_PKG, "lib", "libsdpa_mi355x.so")
