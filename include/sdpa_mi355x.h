@@ -251,8 +251,14 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_split
  * 16-byte aligned pointers and strides); dsinks (optional, used only with
  * sinks) is fp32 [Hq].  The workspace (device memory, 16-byte aligned,
  * caller-owned, need not be initialised) holds
- * sdpa_prefill_backward_workspace_bytes() = 8 * B * Hq * Lq bytes.  Four
- * kernels are enqueued on `stream`; nothing is allocated or synchronised.
+ * sdpa_prefill_backward_workspace_bytes(): 8 * B * Hq * Lq bytes (D_i and
+ * the LSE per row), rounded up to 16, plus, for 16-bit GQA calls whose
+ * 256-key dK / dV blocks are split over hs query-head groups (hs the largest
+ * divisor of Hq / Hkv with B * Hkv * ceil(Lk / 256) * hs <= 512),
+ * hs * B * Hkv * Lk * 2 * (64 or 128, the kernel head dim) * 4 bytes of
+ * fp32 dK / dV shares.  Four or five kernels are enqueued on `stream`
+ * (a reduction of the shares when split); nothing is allocated or
+ * synchronised.
  * The outputs must not overlap each other, the inputs or the workspace. */
 typedef struct sdpa_bwd_args {
   const void *dout; int64_t dout_stride[3];  /* [B, Hq,  Lq, Dv] upstream gradient */

@@ -288,7 +288,26 @@ int check_decode(const sdpa_args* a, int num_splits, const void* ws, size_t ws_b
 
 // Backward: the forward's checks (o and lse are inputs), 16-bit only,
 // D in {64, 128}, and the gradient outputs.
-size_t backward_workspace(const sdpa_args* a) { return (size_t)a->B * a->Hq * a->Lq * 2 * sizeof(float); }
+// Query-head groups a 16-bit dK / dV key block is split over (GQA): the
+// largest divisor of Hq / Hkv that keeps the grid within two workgroups per
+// compute unit.  Each group's workgroup accumulates its heads' share in
+// fp32; a reduction pass adds the groups up.
+int bwd_head_split(const sdpa_args* a) {
+  if (a->dtype == SDPA_F32 || a->Hkv <= 0) return 1;
+  const int64_t g = a->Hq / a->Hkv;
+  const int64_t units = a->B * a->Hkv * ((a->Lk + kBwdKeyBlock - 1) / kBwdKeyBlock);
+  int hs = 1;
+  for (int64_t d = 2; d <= g; ++d)
+    if (g % d == 0 && units * d <= 2 * kDecodeCUs) hs = (int)d;
+  return hs;
+}
+size_t backward_workspace(const sdpa_args* a) {
+  // D_i and LSE rows, rounded up to 16 bytes, then the head groups' shares
+  size_t n = ((size_t)a->B * a->Hq * a->Lq * 2 * sizeof(float) + 15) / 16 * 16;
+  const int hs = bwd_head_split(a);
+  if (hs > 1) n += (size_t)hs * a->B * a->Hkv * a->Lk * 2 * kernel_dim(a) * sizeof(float);
+  return n;
+}
 
 int check_backward(const sdpa_args* a, const sdpa_bwd_args* g, const void* ws, size_t ws_bytes) {
   int st = check_common(a);
@@ -527,7 +546,7 @@ int sdpa_prefill_backward(const sdpa_args* fwd, const sdpa_bwd_args* grad, void*
   if (st != SDPA_OK) return st;
   sdpa::AttnParams p = sdpa::make_params(*fwd);
   return sdpa::launch_status(sdpa::launch_backward(p, *grad, fwd->scale, (float*)workspace, fwd->dtype,
-                                                   fwd->causal != 0, (hipStream_t)stream));
+                                                   fwd->causal != 0, sdpa::bwd_head_split(fwd), (hipStream_t)stream));
 }
 
 const char* sdpa_status_string(int status) {

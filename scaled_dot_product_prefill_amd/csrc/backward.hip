@@ -62,6 +62,7 @@ constexpr int kBwdThreads = 64 * kBwdWaves;
 constexpr int kDkvWaves = 8;
 constexpr int kDkvThreads = 64 * kDkvWaves;
 constexpr int kDkvKeys = 32 * kDkvWaves;
+static_assert(kDkvKeys == kBwdKeyBlock, "the host plans the head split with this key block");
 
 // A 64-row tile of a [rows, D] 16-bit matrix in LDS: unpadded rows whose
 // 16-byte chunks are XOR-swizzled by the row (period 16 rows), filled by
@@ -117,6 +118,8 @@ struct BwdParams {
   float scale;
   float* ws_d;           // [B*Hq*Lq] D_i
   float* ws_l;           // [B*Hq*Lq] LSE_i * log2(e), +inf for rows without a key
+  int hsplit;            // query-head groups per dK / dV key block (16-bit)
+  float* ws_part;        // hsplit > 1: [hsplit][B][Hkv][Lk][2 D] fp32 dK (scaled), dV
 };
 
 // Per-lane source offset of the direct loads of a Tile64: the 16 bytes that
@@ -421,9 +424,14 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
 
   // key blocks in increasing order: under causal masking the first key
   // blocks are seen by the most query rows, so the heaviest go first
+  // workgroup = (key block kt, batch, KV head, query-head group hsi): the
+  // group's gsub query heads hq0 .. hq0 + gsub - 1
   const int nbh = p.B * p.Hkv;
-  const int kt = (int)blockIdx.x / nbh, bhk = (int)blockIdx.x % nbh;
+  const int hsi = (int)blockIdx.x % bp.hsplit, unit = (int)blockIdx.x / bp.hsplit;
+  const int kt = unit / nbh, bhk = unit % nbh;
   const int b = bhk / p.Hkv, hk = bhk % p.Hkv;
+  const int gsub = p.group / bp.hsplit;
+  const int hq0 = hk * p.group + hsi * gsub;
   const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
   const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
   const int coff = lk - lq;
@@ -457,15 +465,15 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   const int qt0 = ibeg / 64;
   const int nqt = k0 < lk ? (lq + 63) / 64 : 0;
   const int per_head = max(0, nqt - qt0);
-  const int ntiles = per_head * p.group;
+  const int ntiles = per_head * gsub;
 
   const uint32_t qoff = tile_lane_off<D, kDkvWaves>(wave, lane, p.qs[2], p.Dqk);
   const uint32_t dooff = tile_lane_off<D, kDkvWaves>(wave, lane, bp.dos[2], p.Dv);
   const uint32_t lds0 = lds_addr(smem);
-  // tile t = (query tile qt0 + t / G, query head hk * G + t % G)
+  // tile t = (query tile qt0 + t / gsub, query head hq0 + t % gsub)
   auto issue = [&](int t) {
-    const int hq = hk * p.group + t % p.group;
-    const int q0 = 64 * (qt0 + t / p.group);
+    const int hq = hq0 + t % gsub;
+    const int q0 = 64 * (qt0 + t / gsub);
     const uint32_t st = lds0 + (t & 1) * STAGE;
     const S* qb = (const S*)p.q + b * p.qs[0] + hq * p.qs[1];
     const S* db = (const S*)bp.dout + b * bp.dos[0] + hq * bp.dos[1];
@@ -497,7 +505,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
       // query tiles qt0 .. qs - 1 hold a row that sees at most 256 keys
       const int qs = CAUSAL ? (lk <= 256 ? nqt : min(nqt, max(qt0, (256 - coff) / 64 + 1))) : (lk <= 256 ? nqt : qt0);
       // a key block past this batch's keys has nqt = 0 < qt0: no tiles at all
-      n_split = max(0, qs - qt0) * p.group;
+      n_split = max(0, qs - qt0) * gsub;
     }
   }
   auto run = [&](int t_begin, int t_end, auto split_tag) {
@@ -506,8 +514,8 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
       wait_vmcnt<0>();
       lds_barrier();  // tile t landed for every wave; tile t-1 is no longer read
       if (t + 1 < ntiles) issue(t + 1);
-      const int hq = hk * p.group + t % p.group;
-      const int q0 = 64 * (qt0 + t / p.group);
+      const int hq = hq0 + t % gsub;
+      const int q0 = 64 * (qt0 + t / gsub);
       // nothing of this wave's keys is visible to the tile's rows
       if (kw0 >= lk || (CAUSAL && kw0 > q0 + 63 + coff)) continue;
       const bool edge = MASK || q0 + 64 > lq || kw0 + 32 > lk || (CAUSAL && kw0 + 31 > q0 + coff);
@@ -584,6 +592,23 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   if constexpr (std::is_same<T, TBF16>::value) run(0, n_split, std::true_type{});
   run(n_split, ntiles, std::false_type{});
 
+  if (bp.hsplit > 1) {
+    // this head group's share, in fp32, for bwd_dkv_reduce_kernel
+    if (my_j < p.Lk) {
+      float* pr = bp.ws_part + ((((int64_t)hsi * p.B + b) * p.Hkv + hk) * p.Lk + my_j) * (2 * D);
+      const float sc = bp.scale;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * mb + 8 * q4 + 4 * g;
+          *(f32x4*)(pr + d0) = f32x4{dk[mb][4 * q4] * sc, dk[mb][4 * q4 + 1] * sc, dk[mb][4 * q4 + 2] * sc,
+                                     dk[mb][4 * q4 + 3] * sc};
+          *(f32x4*)(pr + D + d0) = f32x4{dv[mb][4 * q4], dv[mb][4 * q4 + 1], dv[mb][4 * q4 + 2], dv[mb][4 * q4 + 3]};
+        }
+    }
+    return;
+  }
   if (my_j < p.Lk) {
     S* kr = (S*)bp.dk + b * bp.dks[0] + hk * bp.dks[1] + (int64_t)my_j * bp.dks[2];
     S* vr = (S*)bp.dv + b * bp.dvs[0] + hk * bp.dvs[1] + (int64_t)my_j * bp.dvs[2];
@@ -599,6 +624,31 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
         if (32 * mb + 8 * q4 + 4 * g < p.Dqk) *(u32x2*)(kr + 32 * mb + 8 * q4 + 4 * g) = wk;
         if (32 * mb + 8 * q4 + 4 * g < p.Dv) *(u32x2*)(vr + 32 * mb + 8 * q4 + 4 * g) = wv;
       }
+  }
+}
+
+// ---- head groups of a split dK / dV: sum the hsplit fp32 shares of each key
+// row and write dK, dV in the input type.  Thread = 4 consecutive elements of
+// one row's [dK | dV] (2 D floats).
+template <class T, int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_dkv_reduce_kernel(BwdParams bp) {
+  using S = uint16_t;
+  const AttnParams& p = bp.f;
+  constexpr int TPR = 2 * D / 4;               // threads per row
+  constexpr int RPB = kBwdThreads / TPR;       // rows per workgroup
+  const int64_t nrows = (int64_t)p.B * p.Hkv * p.Lk;
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  if (row >= nrows) return;
+  const int c = (threadIdx.x % TPR) * 4;       // element within [dK | dV]
+  f32x4 acc = f32x4{};
+  for (int h = 0; h < bp.hsplit; ++h) acc += *(const f32x4*)(bp.ws_part + ((int64_t)h * nrows + row) * (2 * D) + c);
+  const int j = (int)(row % p.Lk);
+  const int bh = (int)(row / p.Lk), b = bh / p.Hkv, hk = bh % p.Hkv;
+  const u32x2 w = {cvt_pk(T{}, acc[0], acc[1]), cvt_pk(T{}, acc[2], acc[3])};
+  if (c < D) {
+    if (c < p.Dqk) *(u32x2*)((S*)bp.dk + b * bp.dks[0] + hk * bp.dks[1] + (int64_t)j * bp.dks[2] + c) = w;
+  } else if (c - D < p.Dv) {
+    *(u32x2*)((S*)bp.dv + b * bp.dvs[0] + hk * bp.dvs[1] + (int64_t)j * bp.dvs[2] + (c - D)) = w;
   }
 }
 
@@ -923,7 +973,13 @@ hipError_t launch_main(const BwdParams& bp, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkv_kernel<T, D, CAUSAL, MASK>),
-                       dim3((unsigned)((p.Lk + kDkvKeys - 1) / kDkvKeys * p.B * p.Hkv)), dim3(kDkvThreads), 0, s, bp);
+                       dim3((unsigned)((p.Lk + kDkvKeys - 1) / kDkvKeys * p.B * p.Hkv * bp.hsplit)), dim3(kDkvThreads),
+                       0, s, bp);
+    e = hipGetLastError();
+    if (e != hipSuccess || bp.hsplit == 1) return e;
+    constexpr int RPB = kBwdThreads / (2 * D / 4);
+    const int64_t nrows = (int64_t)p.B * p.Hkv * p.Lk;
+    hipLaunchKernelGGL((bwd_dkv_reduce_kernel<T, D>), dim3((unsigned)((nrows + RPB - 1) / RPB)), block, 0, s, bp);
     return hipGetLastError();
   }
 }
@@ -955,7 +1011,7 @@ hipError_t launch_t(const BwdParams& bp, bool causal, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float scale, float* ws, int dtype,
-                           bool causal, hipStream_t s) {
+                           bool causal, int head_split, hipStream_t s) {
   BwdParams bp{};
   bp.f = p;
   bp.scale = scale;
@@ -973,6 +1029,9 @@ hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float sc
   const size_t nrows = (size_t)p.B * p.Hq * p.Lq;
   bp.ws_d = ws;
   bp.ws_l = ws + nrows;
+  // (fp32 keeps one workgroup per key block and KV head)
+  bp.hsplit = dtype == SDPA_F32 ? 1 : head_split;
+  bp.ws_part = ws + (2 * nrows + 3) / 4 * 4;  // 16-byte aligned
   if (p.sinks == nullptr) bp.dsinks = nullptr;
   switch (dtype) {
     case SDPA_F32: return launch_t<TF32>(bp, causal, s);

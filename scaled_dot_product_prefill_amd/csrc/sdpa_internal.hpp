@@ -42,9 +42,14 @@ hipError_t launch_prefill(const AttnParams& p, int dtype, bool causal, hipStream
 hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s);
 // 16-bit prefill at kernel head dim 512 (sets its own column chunks), one pass
 hipError_t launch_prefill_wide(const AttnParams& p, int dtype, hipStream_t s);
-// Gradients: ws holds 2 * B * Hq * Lq floats (D_i, then the LSE in log2 units).
+// Gradients: ws holds 2 * B * Hq * Lq floats (D_i, then the LSE in log2
+// units) and, with head_split > 1, from the next 16-byte boundary on,
+// head_split * B * Hkv * Lk rows of 2 * kernel head dim floats (each head
+// group's fp32 dK, dV).
 hipError_t launch_backward(const AttnParams& p, const sdpa_bwd_args& g, float scale, float* ws, int dtype,
-                           bool causal, hipStream_t s);
+                           bool causal, int head_split, hipStream_t s);
+// The dK / dV kernel's keys per workgroup (16-bit).
+constexpr int kBwdKeyBlock = 256;
 
 // Decode tiling shared by the host heuristics and the kernels.  The Lq * G
 // (query row, head) columns of a KV head form 16-column blocks; in 16-bit up

@@ -297,7 +297,33 @@ def test_backward_validation(lib):
     assert _bwd(lib, ws=(1 << 45) + 8) == S.ERR_ALIGN
     assert _bwd(lib, ws=(1 << 41) + 64) == S.ERR_ARG                           # workspace inside dout
     a = _args()
-    assert lib.sdpa_prefill_backward_workspace_bytes(ctypes.byref(a)) == 2 * 8 * 64 * 2 * 4
+    # D_i and LSE rows (B * Hq * Lq * 2 floats), then -- GQA-4 over one
+    # 256-key block for 2 x 2 (batch, KV head) units -- the fp32 dK / dV shares
+    # of 4 head groups: 4 * B * Hkv * Lk rows of 2 * 128 floats
+    assert lib.sdpa_prefill_backward_workspace_bytes(ctypes.byref(a)) == 2 * 8 * 64 * 2 * 4 + 4 * 2 * 2 * 64 * 256 * 4
+
+
+def test_backward_head_split_plan(lib):
+    # The dK / dV key blocks (256 keys) of a GQA call are split over query-head
+    # groups: the largest divisor of Hq / Hkv keeping the grid within 512
+    # workgroups (two per compute unit).  MHA and fp32 never split.
+    def ws(**kw):
+        a = _args(**kw)
+        return lib.sdpa_prefill_backward_workspace_bytes(ctypes.byref(a))
+    base = lambda B, Hq, Lq: ((B * Hq * Lq * 2 * 4 + 15) // 16) * 16
+    part = lambda hs, B, Hkv, Lk, kd: hs * B * Hkv * Lk * 2 * kd * 4
+    # MHA: no shares
+    assert ws(Hkv=8) == base(2, 8, 64)
+    # fp32: one workgroup per key block and KV head
+    assert ws(dtype=sdpa.F32) == base(2, 8, 64)
+    # GQA-4, B1 Hkv8 L4096: 8 x 16 = 128 units -> 4 groups (512 workgroups)
+    assert ws(B=1, Hq=32, Hkv=8, Lq=4096, Lk=4096) == base(1, 32, 4096) + part(4, 1, 8, 4096, 128)
+    # GQA-4, B4 Hkv8 L4096: 512 units already -> no split
+    assert ws(B=4, Hq=32, Hkv=8, Lq=4096, Lk=4096) == base(4, 32, 4096)
+    # GQA-8, B1 Hkv4 L4096, D64: 64 units -> 8 groups
+    assert ws(B=1, Hq=32, Hkv=4, Lq=4096, Lk=4096, D=64) == base(1, 32, 4096) + part(8, 1, 4, 4096, 64)
+    # GQA-6, 3 units: the largest divisor of 6 within 512 workgroups is 6; odd row count rounds up
+    assert ws(B=1, Hq=6, Hkv=1, Lq=7, Lk=700) == base(1, 6, 7) + part(6, 1, 1, 700, 128)
 
 
 def test_noalloc_decode_rejects_partials_beyond_the_static_scratch(lib):

@@ -152,6 +152,23 @@ def test_backward_seqlens_keys_end_early(dtype):
     _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
 
 
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("G", [4, 8])
+def test_backward_gqa_head_groups(dtype, G):
+    """GQA with several 256-key dK / dV blocks and a ragged key tail: the
+    blocks are split over query-head groups (each group's dK, dV in fp32,
+    summed by a reduction pass), so every key row sums the groups of every
+    head of its KV head."""
+    B, Hkv, L, D = 1, 2, 1100, 128
+    Hq = G * Hkv
+    x = random_case(5250 + G, B, Hq, Hkv, L, L, D, dtype, sinks=True, sink_scale=2.0)
+    dout = _dout(5250 + G, x["q"].shape, dtype)
+    (dq, dk, dv, ds), sc = _run(x, dout, dtype, True, None, None, want_dsinks=True)
+    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+                                             sinks=x["sinks"])
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
+
+
 def test_autograd_wrapper_matches_entry_point():
     x = to_dev(random_case(5200, 2, 4, 2, 150, 150, 64, "bf16", sinks=True))
     q, k, v = (x[n].clone().requires_grad_(True) for n in ("q", "k", "v"))
