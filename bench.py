@@ -115,12 +115,38 @@ def file_sha256(path: str):
         return None
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and with runs of whitespace folded, so
+    that the hash below follows the code the compiler sees, not its prose."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                       # string or char literal, kept whole
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_hash() -> str:
+    """Hash of the kernel sources' code (comments and layout excluded)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "scaled_dot_product_prefill_amd", "csrc")
     for fn in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, fn), "rb") as f:
-            h.update(fn.encode() + f.read())
+        with open(os.path.join(csrc, fn), encoding="utf-8") as f:
+            h.update(fn.encode() + _code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -433,6 +433,8 @@ __device__ inline float row_sum2(TBF16, uint32_t pk, float acc) {
 // Per wave (32 queries) and tile (64 keys), software-pipelined:
 //   S(t+1) = K(t+1) . Q^T  on the matrix cores  ||  P(t) = exp2(S(t) c - m)  on the VALU
 //   O^T   += V(t)^T . P(t)^T on the matrix cores  ||  row max of S(t+1) on the VALU
+// (the pre-scaled form's fast pass drops the row max and checks each tile's
+// row sum instead, see kFastSumMax).
 // K and V tiles arrive by direct buffer -> LDS loads into two-stage rings, one
 // tile ahead, with one fence-free barrier per tile.  V^T is read with
 // ds_read_b64_tr_b16.  Interior tiles (every key visible to the whole
@@ -701,8 +703,10 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   //     the rest O^T += V(t)^T.P(t)^T in (kb, u) groups of NMB,
   //   - its share of the VALU work: "EC" items (two probabilities of P(t),
   //     exponentials, packing, row sum) before the P.V ops that consume them,
-  //     then "X" items (row max of S(t+1), two scores each) once it exists.
-  // Returns the row max of c S(t+1): relative to m for fp16, absolute for bf16.
+  //     then "X" items (row max of S(t+1), two scores each) once it exists
+  //     (none in the fast pass, whose slots there hold the row-sum check).
+  // Returns the row max of c S(t+1): relative to m for fp16, absolute for
+  // bf16; the fast pass moves the reference max itself and returns -inf.
   // A full scheduling fence closes every slot.  A wave whose matrix ops are
   // spaced by a few VALU ops lets both units run at once; a run of
   // back-to-back matrix ops stalls the VALU of the other wave on the SIMD.
