@@ -295,21 +295,28 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
       st = mma32(T{}, tile_rows<D>(Ks, 32 * kb, s, l32, g), qreg[s], st);
       dpt = mma32(T{}, tile_rows<D>(Vs, 32 * kb, s, l32, g), doreg[s], dpt);
     }
+    // the visibility test only on edge tiles, as separate code under a
+    // wave-uniform branch (one form with a runtime test issues the test's
+    // exec-masked code on every tile)
+    auto probs = [&](auto edge_tag) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = st[r] * c;
-      if (edge) {
-        const int j = 64 * t + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (MASK) {
-          const int ii = ok ? my_i : 0, jj = j < lk ? j : lk - 1;
-          x += kLog2e * mask_val(p.mask, p.mask_bool,
-                                 b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
+      for (int r = 0; r < 16; ++r) {
+        float x = st[r] * c;
+        if constexpr (decltype(edge_tag)::value) {
+          const int j = 64 * t + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (MASK) {
+            const int ii = ok ? my_i : 0, jj = j < lk ? j : lk - 1;
+            x += kLog2e * mask_val(p.mask, p.mask_bool,
+                                   b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
+          }
+          const bool vis = (j < lk) & (!CAUSAL | (j <= my_i + coff));
+          x = vis ? x : kNegInf;
         }
-        const bool vis = j < lk && (!CAUSAL || j <= my_i + coff);
-        x = vis ? x : kNegInf;
+        pr[r] = fast_exp2(x - lse2);
       }
-      pr[r] = fast_exp2(x - lse2);
-    }
+    };
+    if (edge) probs(std::true_type{});
+    else probs(std::false_type{});
   };
 
   // D_i.  Where every row of the workgroup sees more than 256 keys (and no
@@ -544,31 +551,39 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
           if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
         }
         f32x16 pr, ds;
+        // P and dS of the block; the visibility test only on edge tiles.  The
+        // two forms are separate code under a wave-uniform branch: written as
+        // one, the test's short-circuit on the lane's own key became per-score
+        // exec-masked code that every tile issued.
+        auto probs = [&](auto edge_tag) {
 #pragma unroll
-        for (int rh = 0; rh < 4; ++rh) {
-          // rows 32 qb + 8 rh + 4 g + (0..3) of the tile
-          const int ib = 32 * qb + 8 * rh + 4 * g;
-          const f32x4 l4 = *(const f32x4*)(Ls + ib);
-          const f32x4 d4 = *(const f32x4*)(Dv + ib);
+          for (int rh = 0; rh < 4; ++rh) {
+            // rows 32 qb + 8 rh + 4 g + (0..3) of the tile
+            const int ib = 32 * qb + 8 * rh + 4 * g;
+            const f32x4 l4 = *(const f32x4*)(Ls + ib);
+            const f32x4 d4 = *(const f32x4*)(Dv + ib);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * rh + e;
-            float x = s_[r] * c;
-            if (edge) {
-              const int i = q0 + ib + e;
-              if (MASK) {
-                const int ii = i < lq ? i : lq - 1, jj = kok ? my_j : lk - 1;
-                x += kLog2e * mask_val(p.mask, p.mask_bool,
-                                       b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * rh + e;
+              float x = s_[r] * c;
+              if constexpr (decltype(edge_tag)::value) {
+                const int i = q0 + ib + e;
+                if (MASK) {
+                  const int ii = i < lq ? i : lq - 1, jj = kok ? my_j : lk - 1;
+                  x += kLog2e * mask_val(p.mask, p.mask_bool,
+                                         b * p.ms[0] + hq * p.ms[1] + (int64_t)ii * p.ms[2] + (int64_t)jj * p.ms[3]);
+                }
+                const bool vis = kok & (i < lq) & (!CAUSAL | (my_j <= i + coff));
+                x = vis ? x : kNegInf;
               }
-              const bool vis = kok && i < lq && (!CAUSAL || my_j <= i + coff);
-              x = vis ? x : kNegInf;
+              const float pv = fast_exp2(x - l4[e]);
+              pr[r] = pv;
+              ds[r] = pv * (dp[r] - d4[e]);
             }
-            const float pv = fast_exp2(x - l4[e]);
-            pr[r] = pv;
-            ds[r] = pv * (dp[r] - d4[e]);
           }
-        }
+        };
+        if (edge) probs(std::true_type{});
+        else probs(std::false_type{});
         const int lane_b = D >= 128 ? fresh(lane) : lane;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {

@@ -529,8 +529,8 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // ---- direct buffer -> LDS loads.  Wave w fills lines w, w + NW, ... of a
   // tile; line i of a wave sits i * STEP_ROWS rows below line 0 and both
   // swizzles repeat every 16 rows: one per-lane offset plus a uniform step.
-  const S* kbase = (const S*)p.k + b * p.ks[0] + hk * p.ks[1];
-  const S* vbase = (const S*)p.v + b * p.vs[0] + hk * p.vs[1];
+  const S* kbase = uniform_ptr((const S*)p.k + b * p.ks[0] + hk * p.ks[1]);
+  const S* vbase = uniform_ptr((const S*)p.v + b * p.vs[0] + hk * p.vs[1]);
   // A lane whose chunk lies past the real head dim loads nothing (kNoLoad).
   uint32_t koff[C::KVAR], voff;
   {
@@ -545,8 +545,10 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     const int lch = pch ^ swz_v<C::NCH>(row);
     voff = lch * 8 < p.Dv ? (uint32_t)(row * p.vs[2] * 2 + lch * 16) : kNoLoad;
   }
-  const uint32_t krow = (uint32_t)(p.ks[2] * 2), vrow = (uint32_t)(p.vs[2] * 2);
-  const uint32_t kstep = C::STEP_ROWS * krow, vstep = C::STEP_ROWS * vrow;
+  const uint32_t krow = __builtin_amdgcn_readfirstlane((uint32_t)(p.ks[2] * 2));
+  const uint32_t vrow = __builtin_amdgcn_readfirstlane((uint32_t)(p.vs[2] * 2));
+  const uint32_t kstep = __builtin_amdgcn_readfirstlane(C::STEP_ROWS * krow);
+  const uint32_t vstep = __builtin_amdgcn_readfirstlane(C::STEP_ROWS * vrow);
   // bytes of a tile that hold real keys: rows from lk on (and, since the row
   // stride is at least the real row, everything past the last real row) read
   // as zero

@@ -210,6 +210,15 @@ __device__ inline void dma16(const void* base, uint32_t bytes, uint32_t lds_addr
       :
       : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr));
 }
+// A wave-uniform pointer pinned to scalar registers, so that addresses built
+// from it stay in scalar arithmetic.
+template <class P>
+__device__ inline P* uniform_ptr(P* ptr) {
+  const uint64_t a = (uint64_t)ptr;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return (P*)(lo | (hi << 32));
+}
 // LDS byte address of a pointer into shared memory
 __device__ inline uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)(p);
