@@ -173,7 +173,17 @@ template <int D, int NW = kBwdWaves>
 __device__ inline u32x4 tile_rows(const uint8_t* t, int rb, int s, int l32, int g) {
   using L = Tile64<D, NW>;
   const int row = rb + l32;
-  return lds_read16(t + row * L::RB + (((2 * s + g) ^ L::swz(row)) * 16));
+  if constexpr (L::PAD) {
+    // swz(row) = (l32 >> 2) & 3 = 2 h + w: chunk (2 s + g) ^ (2 h + w) is
+    // 2 (s ^ h) + (g ^ w), and s ^ h = s + h for even s, s - h for odd s, so
+    // the offset is a per-lane term (one for each parity of s) plus a
+    // constant that the read's immediate offset carries
+    const int h = (l32 >> 3) & 1, w = (l32 >> 2) & 1;
+    const int lane_off = l32 * L::RB + 16 * (g ^ w) + ((s & 1) ? -32 * h : 32 * h);
+    return lds_read16(t + lane_off + rb * L::RB + 32 * s);
+  } else {
+    return lds_read16(t + row * L::RB + (((2 * s + g) ^ L::swz(row)) * 16));
+  }
 }
 
 // Matrix-core A operand from a Tile64, transposed: A[m = column 32 mb + lane%32]
@@ -185,11 +195,22 @@ __device__ inline u32x4 tile_cols(const uint8_t* t, int rb, int mb, int lane) {
   using L = Tile64<D, NW>;
   const int r16 = lane & 15, g = lane >> 5, dh = (lane >> 4) & 1;
   const int vr = rb + 4 * g + (r16 >> 2);
-  const int ch = 4 * mb + 2 * dh + ((r16 >> 1) & 1);
-  const uint8_t* p0 = t + vr * L::RB + ((ch ^ L::swz(vr)) * 16) + (r16 & 1) * 8;
-  const uint8_t* p1 = t + (vr + 8) * L::RB + ((ch ^ L::swz(vr + 8)) * 16) + (r16 & 1) * 8;
-  const u32x2 a0 = lds_read_tr16(p0), a1 = lds_read_tr16(p1);
-  return u32x4{a0[0], a0[1], a1[0], a1[1]};
+  if constexpr (L::PAD) {
+    // rb is a multiple of 16, so swz(vr) = g and swz(vr + 8) = g ^ 2: both
+    // touch only the low two chunk bits, and 4 mb passes through the XOR
+    const int lo = 2 * dh + ((r16 >> 1) & 1);
+    const int base = (4 * g + (r16 >> 2)) * L::RB + (r16 & 1) * 8;
+    const int off0 = base + 16 * (lo ^ g), off1 = base + 8 * L::RB + 16 * (lo ^ g ^ 2);
+    const u32x2 a0 = lds_read_tr16(t + off0 + rb * L::RB + 64 * mb);
+    const u32x2 a1 = lds_read_tr16(t + off1 + rb * L::RB + 64 * mb);
+    return u32x4{a0[0], a0[1], a1[0], a1[1]};
+  } else {
+    const int ch = 4 * mb + 2 * dh + ((r16 >> 1) & 1);
+    const uint8_t* p0 = t + vr * L::RB + ((ch ^ L::swz(vr)) * 16) + (r16 & 1) * 8;
+    const uint8_t* p1 = t + (vr + 8) * L::RB + ((ch ^ L::swz(vr + 8)) * 16) + (r16 & 1) * 8;
+    const u32x2 a0 = lds_read_tr16(p0), a1 = lds_read_tr16(p1);
+    return u32x4{a0[0], a0[1], a1[0], a1[1]};
+  }
 }
 
 // registers 8u .. 8u+7 as bf16 hi + lo pairs (about 16 significant bits)
@@ -417,10 +438,13 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
   using L = Tile64<D, kDkvWaves>;
   constexpr int NQ = D / 16, NMB = D / 32;
   constexpr int STAGE = 2 * L::BYTES + 2048;  // Q, dO, LSE line, D line
-  // the workgroup's value rows: unpadded, chunks swizzled as in an unpadded
-  // tile (each lane reads back only its own row; 16 rows per pass)
-  constexpr int VRB = D * 2;
-  auto vswz = [](int row) { return D >= 128 ? (row & 15) : ((row >> 1) & 7); };
+  // the workgroup's value rows (each lane reads back only its own row; 16
+  // rows per pass).  D = 128: rows padded by one chunk (272 bytes, 68 dwords:
+  // 16 rows at one chunk fall on 16 distinct 4-bank groups), so a lane's
+  // reads are one base plus immediate offsets; D = 64: unpadded, chunks
+  // swizzled as in an unpadded tile.
+  constexpr int VRB = D >= 128 ? D * 2 + 16 : D * 2;
+  auto vswz = [](int row) { return D >= 128 ? 0 : ((row >> 1) & 7); };
   constexpr int VBYTES = kDkvKeys * VRB;
   using S = uint16_t;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE + VBYTES];
@@ -539,7 +563,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
         // and each reload's wait also waited for the next tile's loads in
         // flight (measured: causal bf16 8 % faster, GQA-4 15 %).  At D = 64
         // they fit, and recomputing them cost 4 %.
-        const int lane_a = D >= 128 ? fresh(lane) : lane, l32_a = lane_a & 31, g_a = lane_a >> 5;
+        const int lane_a = D >= 128 ? fresh_lane(lane) : lane, l32_a = lane_a & 31, g_a = lane_a >> 5;
         // operand reads run at most two k-steps ahead of the products (a
         // fence every second step), which keeps the wave inside half the
         // register file
@@ -584,7 +608,7 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
         };
         if (edge) probs(std::true_type{});
         else probs(std::false_type{});
-        const int lane_b = D >= 128 ? fresh(lane) : lane;
+        const int lane_b = D >= 128 ? fresh_lane(lane) : lane;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const u32x4 db = pack_b<T>(ds, u);

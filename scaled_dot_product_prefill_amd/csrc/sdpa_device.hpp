@@ -314,6 +314,10 @@ __device__ inline int fresh(int v) {
   asm volatile("" : "+v"(v));
   return v;
 }
+// A fresh copy of the lane index.  The mask restores what the compiler knew
+// of it (0..63), so that swizzled LDS offsets derived from it still fold into
+// per-lane bases plus immediate offsets.
+__device__ inline int fresh_lane(int lane) { return fresh(lane) & 63; }
 
 // exchange with lane l ^ 32 (the other half of the wave)
 __device__ inline float xor32(float v) { return __shfl_xor(v, 32, 64); }
