@@ -564,15 +564,27 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
         // flight (measured: causal bf16 8 % faster, GQA-4 15 %).  At D = 64
         // they fit, and recomputing them cost 4 %.
         const int lane_a = D >= 128 ? fresh_lane(lane) : lane, l32_a = lane_a & 31, g_a = lane_a >> 5;
-        // operand reads run at most two k-steps ahead of the products (a
-        // fence every second step), which keeps the wave inside half the
-        // register file
+        // the operands of k-step s + 1 are read before the products of step
+        // s are issued (one fence per step): each read has a step of this
+        // wave's products to land, in two sets of operand registers
+        auto vrow = [&](int s) { return lds_read16(Vw + l32_a * VRB + (((2 * s + g_a) ^ vswz(l32_a)) * 16)); };
+        u32x4 qo = tile_rows<D, kDkvWaves>(Qs, 32 * qb, 0, l32_a, g_a);
+        u32x4 doo = tile_rows<D, kDkvWaves>(Ds, 32 * qb, 0, l32_a, g_a);
+        u32x4 vo = vrow(0);
 #pragma unroll
         for (int s = 0; s < NQ; ++s) {
-          s_ = mma32(T{}, tile_rows<D, kDkvWaves>(Qs, 32 * qb, s, l32_a, g_a), kreg[s], s_);
-          dp = mma32(T{}, tile_rows<D, kDkvWaves>(Ds, 32 * qb, s, l32_a, g_a),
-                     lds_read16(Vw + l32_a * VRB + (((2 * s + g_a) ^ vswz(l32_a)) * 16)), dp);
-          if (s % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+          u32x4 qn = qo, dn = doo, vn = vo;
+          if (s + 1 < NQ) {
+            qn = tile_rows<D, kDkvWaves>(Qs, 32 * qb, s + 1, l32_a, g_a);
+            dn = tile_rows<D, kDkvWaves>(Ds, 32 * qb, s + 1, l32_a, g_a);
+            vn = vrow(s + 1);
+          }
+          s_ = mma32(T{}, qo, kreg[s], s_);
+          dp = mma32(T{}, doo, vo, dp);
+          __builtin_amdgcn_sched_barrier(0);
+          qo = qn;
+          doo = dn;
+          vo = vn;
         }
         f32x16 pr, ds;
         // P and dS of the block; the visibility test only on edge tiles.  The
@@ -609,20 +621,32 @@ __global__ __launch_bounds__(kDkvThreads, 1) void bwd_dkv_kernel(BwdParams bp) {
         if (edge) probs(std::true_type{});
         else probs(std::false_type{});
         const int lane_b = D >= 128 ? fresh_lane(lane) : lane;
+        u32x4 pb[2], pl[2], db[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const u32x4 db = pack_b<T>(ds, u);
-          u32x4 pb, pl;
-          if constexpr (SPLIT) pack_b_split(pr, u, pb, pl);
-          else pb = pack_b<T>(pr, u);
+          db[u] = pack_b<T>(ds, u);
+          if constexpr (SPLIT) pack_b_split(pr, u, pb[u], pl[u]);
+          else pb[u] = pack_b<T>(pr, u);
+        }
+        // step i = (u, mb): the transposed dO and Q columns of step i + 1 are
+        // read before the products of step i are issued
+        u32x4 da = tile_cols<D, kDkvWaves>(Ds, 32 * qb, 0, lane_b);
+        u32x4 qa = tile_cols<D, kDkvWaves>(Qs, 32 * qb, 0, lane_b);
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) {
-            const u32x4 da = tile_cols<D, kDkvWaves>(Ds, 32 * qb + 16 * u, mb, lane_b);
-            dv[mb] = mma32(T{}, da, pb, dv[mb]);
-            if constexpr (SPLIT) dv[mb] = mma32(T{}, da, pl, dv[mb]);
-            dk[mb] = mma32(T{}, tile_cols<D, kDkvWaves>(Qs, 32 * qb + 16 * u, mb, lane_b), db, dk[mb]);
-            if (mb % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 2 * NMB; ++i) {
+          const int u = i / NMB, mb = i % NMB;
+          u32x4 dn = da, qn = qa;
+          if (i + 1 < 2 * NMB) {
+            const int u1 = (i + 1) / NMB, mb1 = (i + 1) % NMB;
+            dn = tile_cols<D, kDkvWaves>(Ds, 32 * qb + 16 * u1, mb1, lane_b);
+            qn = tile_cols<D, kDkvWaves>(Qs, 32 * qb + 16 * u1, mb1, lane_b);
           }
+          dv[mb] = mma32(T{}, da, pb[u], dv[mb]);
+          if constexpr (SPLIT) dv[mb] = mma32(T{}, da, pl[u], dv[mb]);
+          dk[mb] = mma32(T{}, qa, db[u], dk[mb]);
+          __builtin_amdgcn_sched_barrier(0);
+          da = dn;
+          qa = qn;
         }
       }
     }
