@@ -644,14 +644,12 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       m_run = m_new;
     }
   };
-  // P = exp2(S cs - m) (interior) or exp2(S - m) (edge, already scaled), packed
-  // as the B operands of P.V: k-step u of block kb <-> accumulator rows 8u..8u+7.
-  // Without the split the row sum is row_sum2's (bf16: the rounded values
-  // P.V multiplies).
-  auto probs = [&](f32x16* sc, u32x4 (&hi)[C::NKB][2], u32x4 (&lo)[C::NKB][2], auto edge_tag,
-                   bool split) {
+  // P = exp2(S cs - m) (interior) or exp2(S - m) (edge, already scaled), left
+  // in sc and packed as the B operands of P.V: k-step u of block kb <->
+  // accumulator rows 8u..8u+7.  The row sum adds the packed values (bf16:
+  // the rounded values P.V multiplies).
+  auto probs = [&](f32x16* sc, u32x4 (&pk)[C::NKB][2], auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
-    constexpr bool BF = std::is_same<T, TBF16>::value;
     const float m_use = m_run == kNegInf ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb) {
@@ -662,22 +660,13 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
       for (int u = 0; u < 2; ++u)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = sc[kb][8 * u + 2 * e], p1 = sc[kb][8 * u + 2 * e + 1];
-          if (BF && split) {
-            uint32_t h, l;
-            TBF16::split2(p0, p1, h, l);
-            hi[kb][u][e] = h;
-            lo[kb][u][e] = l;
-            l_run += p0 + p1;
-          } else {
-            hi[kb][u][e] = cvt_pk(T{}, p0, p1);
-            l_run = row_sum2(T{}, hi[kb][u][e], l_run);
-          }
+          pk[kb][u][e] = cvt_pk(T{}, sc[kb][8 * u + 2 * e], sc[kb][8 * u + 2 * e + 1]);
+          l_run = row_sum2(T{}, pk[kb][u][e], l_run);
         }
     }
   };
-  auto pv = [&](const uint8_t* Vst, u32x4 (&hi)[C::NKB][2], u32x4 (&lo)[C::NKB][2], bool split) {
-    constexpr bool BF = std::is_same<T, TBF16>::value;
+  // O^T += V^T P^T for one packed P
+  auto pv = [&](const uint8_t* Vst, const u32x4 (&pk)[C::NKB][2]) {
     const uint8_t* Vs = Vst + v_lane;
 #pragma unroll
     for (int kb = 0; kb < C::NKB; ++kb)
@@ -690,8 +679,7 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
           const u32x2 a0 = lds_read_tr16(vb + ch);
           const u32x2 a1 = lds_read_tr16(vb + 8 * C::RB + ch);
           const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
-          acc[mb] = mma32(T{}, va, hi[kb][u], acc[mb]);
-          if (BF && split) acc[mb] = mma32(T{}, va, lo[kb][u], acc[mb]);
+          acc[mb] = mma32(T{}, va, pk[kb][u], acc[mb]);
         }
       }
   };
@@ -931,9 +919,33 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     lds_barrier();
     if (t + 1 < ntiles) issue_v(t + 1, Vring + (par ^ 1) * C::TILE);
     if (t + 2 < ntiles) issue_k(t + 2, Kring + par * C::TILE);
-    u32x4 hi[C::NKB][2], lo[C::NKB][2];
-    probs(sa, hi, lo, edge_tag, split_p);
-    pv(Vring + par * C::TILE, hi, lo, split_p);
+    // The bf16 hi + lo split is a branch per tile around its own products:
+    // a runtime choice inside probs / pv put a branch around every product,
+    // so each product was a block of its own and nothing was scheduled
+    // across them (bf16 at D = 256, whose tiles all take this path, ran 43 %
+    // slower than fp16).
+    u32x4 hi[C::NKB][2];
+    probs(sa, hi, edge_tag);
+    if constexpr (std::is_same<T, TBF16>::value) {
+      if (split_p) {
+        // P = hi + lo: lo is the rounding hi left, as a second set of
+        // products; the row sum adds it too
+        u32x4 lo[C::NKB][2];
+#pragma unroll
+        for (int kb = 0; kb < C::NKB; ++kb)
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t h = hi[kb][u][e];
+              lo[kb][u][e] = TBF16::pack2(sa[kb][8 * u + 2 * e] - TBF16::to_f32((uint16_t)(h & 0xffffu)),
+                                          sa[kb][8 * u + 2 * e + 1] - TBF16::to_f32((uint16_t)(h >> 16)));
+              l_run = row_sum2(T{}, lo[kb][u][e], l_run);
+            }
+        pv(Vring + par * C::TILE, lo);
+      }
+    }
+    pv(Vring + par * C::TILE, hi);
     if (t + 1 < ntiles) {
       qk(Kring + (par ^ 1) * C::TILE, sa);
       update_max(t + 1 < n_int ? tile_max(t + 1, sa, std::false_type{})
