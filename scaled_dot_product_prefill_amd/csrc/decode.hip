@@ -694,27 +694,58 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
         u32x4 hi, lo = u32x4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) hi[e] = cvt_pk(T{}, pr[2 * e], pr[2 * e + 1]);
-        if constexpr (std::is_same<T, TBF16>::value) {
-          if (split_p) {
+        const uint8_t* vb = Vs + 32 * bp * C::RB + vlane_t;
+        if constexpr (CPW >= 8) {
+          // Eight 16-column waves sit at the register limit: the two-loop
+          // form below spilled inside the loop here (causal GQA-8 D512 bf16
+          // 0.9 -> 4.4 ms), so the split choice stays beside each product.
+          if constexpr (std::is_same<T, TBF16>::value) {
+            if (split_p) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              uint32_t h, l;
-              T::split2(pr[2 * e], pr[2 * e + 1], h, l);
-              hi[e] = h;
-              lo[e] = l;
+              for (int e = 0; e < 4; ++e) {
+                uint32_t h, l;
+                T::split2(pr[2 * e], pr[2 * e + 1], h, l);
+                hi[e] = h;
+                lo[e] = l;
+              }
             }
           }
-        }
-        const uint8_t* vb = Vs + 32 * bp * C::RB + vlane_t;
 #pragma unroll
-        for (int i = 0; i < NOB; ++i) {
-          const int lch = 2 * (ob0 + i) + ((n_t >> 1) & 1);
-          const u32x2 v0 = lds_read_tr16(vb + ((lch ^ swv_t) * 16));
-          const u32x2 v1 = lds_read_tr16(vb + 16 * C::RB + ((lch ^ swv_t) * 16));
-          const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
-          acc[i] = mma16(T{}, va, hi, acc[i]);
-          if (split_p) acc[i] = mma16(T{}, va, lo, acc[i]);
-          if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+          for (int i = 0; i < NOB; ++i) {
+            const int lch = 2 * (ob0 + i) + ((n_t >> 1) & 1);
+            const u32x2 v0 = lds_read_tr16(vb + ((lch ^ swv_t) * 16));
+            const u32x2 v1 = lds_read_tr16(vb + 16 * C::RB + ((lch ^ swv_t) * 16));
+            const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+            acc[i] = mma16(T{}, va, hi, acc[i]);
+            if (split_p) acc[i] = mma16(T{}, va, lo, acc[i]);
+            if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+          // The split (P = hi + lo, lo the rounding hi left) and unsplit
+          // forms as separate loops under one branch: a runtime choice beside
+          // every product put a branch around each one, and nothing was
+          // scheduled across them (causal MHA-8 D512 bf16 484 -> 400 us).
+          auto pv_step = [&](auto split_tag) {
+#pragma unroll
+            for (int i = 0; i < NOB; ++i) {
+              const int lch = 2 * (ob0 + i) + ((n_t >> 1) & 1);
+              const u32x2 v0 = lds_read_tr16(vb + ((lch ^ swv_t) * 16));
+              const u32x2 v1 = lds_read_tr16(vb + 16 * C::RB + ((lch ^ swv_t) * 16));
+              const u32x4 va = {v0[0], v0[1], v1[0], v1[1]};
+              acc[i] = mma16(T{}, va, hi, acc[i]);
+              if constexpr (decltype(split_tag)::value) acc[i] = mma16(T{}, va, lo, acc[i]);
+              if (i % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+            }
+          };
+          if (std::is_same<T, TBF16>::value && split_p) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              lo[e] = T::pack2(pr[2 * e] - T::to_f32((uint16_t)(hi[e] & 0xffffu)),
+                               pr[2 * e + 1] - T::to_f32((uint16_t)(hi[e] >> 16)));
+            pv_step(std::true_type{});
+          } else {
+            pv_step(std::false_type{});
+          }
         }
       }
     } else {
