@@ -642,18 +642,38 @@ __global__ __launch_bounds__(64 * (CPW > kWaves ? CPW : kWaves), 1) void decode1
     const uint32_t vlane_t = vrow_t * C::RB + (n_t & 1) * 8;
     // ---- S^T = K . Q^T
     f32x4 sc[C::NBLK];
+    if constexpr (CPW > 1 && !(MASK && CPW >= 8)) {
+      // key operands read two products ahead (a ring of two), a fence on
+      // each side of every product: read just before its product, each
+      // operand's LDS latency was waited out in full (causal GQA-8 D512 bf16
+      // 772 -> 748 us, MHA-8 400 -> 382 us).  Not in the masked eight-block
+      // kernel, whose loop already spills.
+      auto kread = [&](int i) {  // i = blk * NQ + ss
+        const uint8_t* krow = Ks + (16 * (i / C::NQ) + n_t) * C::RB;
+        return lds_read16(krow + ((4 * (i % C::NQ) + g4_t) ^ swk_t) * 16);
+      };
+      constexpr int N = C::NBLK * C::NQ, LA = 2;
+      u32x4 kr[LA];
 #pragma unroll
-    for (int blk = 0; blk < C::NBLK; ++blk) {
-      f32x4 s = f32x4{};
-      const uint8_t* krow = Ks + (16 * blk + n_t) * C::RB;
+      for (int j = 0; j < LA; ++j) kr[j] = kread(j < N ? j : 0);
 #pragma unroll
-      for (int ss = 0; ss < C::NQ; ++ss) {
-        s = mma16(T{}, lds_read16(krow + ((4 * ss + g4_t) ^ swk_t) * 16), qreg[ss], s);
-        // two waves per SIMD hold half the register file: keep the operand
-        // reads from being hoisted all at once
-        if (CPW > 1 && ss % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < N; ++i) {
+        const int blk = i / C::NQ, ss = i % C::NQ;
+        const u32x4 ka = kr[i % LA];
+        if (i + LA < N) kr[i % LA] = kread(i + LA);
+        __builtin_amdgcn_sched_barrier(0);
+        sc[blk] = mma16(T{}, ka, qreg[ss], ss == 0 ? f32x4{} : sc[blk]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      sc[blk] = s;
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < C::NBLK; ++blk) {
+        f32x4 s = f32x4{};
+        const uint8_t* krow = Ks + (16 * blk + n_t) * C::RB;
+#pragma unroll
+        for (int ss = 0; ss < C::NQ; ++ss) s = mma16(T{}, lds_read16(krow + ((4 * ss + g4_t) ^ swk_t) * 16), qreg[ss], s);
+        sc[blk] = s;
+      }
     }
     // ---- scale, mask, key tail, running max
     float mx = kNegInf;
