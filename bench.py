@@ -611,6 +611,11 @@ def main():
                              "leaves 1 +- gate is repeated (at most 3)"}
     cfg = {}
     if P is not None:
+        # the query tiles past the last multiple of the compute units run as
+        # key pieces, merged by a second kernel (sdpa_prefill_ws), where that
+        # applies to the workload
+        tail_split = (not pre_w.grad) and sdpa.prefill_workspace_bytes(
+            P["q"], P["k"], P["v"], causal=pre_w.causal, mask=P["mask"]) > 0
         pm = tp.ms()
         avg = sum(pm) / len(pm)
         fl = backward_flops(pre_w) if pre_w.grad else prefill_flops(pre_w)
@@ -619,7 +624,8 @@ def main():
         res.update(value=round(tf, 2), unit="TFLOP/s", dtype=pre_w.dtype)
         res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                            "frac": round(tf / peak, 4), "traffic": load_traffic("prefill_" + pre_w.name),
-                           "kernel": ("bwd_prep + bwd_dq + bwd_dkv kernels" if pre_w.grad else "prefill_kernel"),
+                           "kernel": ("bwd_prep + bwd_dq + bwd_dkv kernels" if pre_w.grad else
+                                      "prefill_kernel + prefill_tail_merge_kernel" if tail_split else "prefill_kernel"),
                            "avg_ms": round(avg, 5),
                            "median_ms": round(median(pm), 5),
                            "median_frac": round(fl / (median(pm) * 1e-3) / 1e12 / peak, 4),

@@ -176,6 +176,31 @@ SDPA_API int sdpa_prefill(const sdpa_args *args, void *stream);
  * Returns what sdpa_prefill would return before launching. */
 SDPA_API int sdpa_prefill_check(const sdpa_args *args);
 
+/* Prefill with a workspace: the same results as sdpa_prefill (up to the
+ * rounding order of the merge), which it calls when
+ * sdpa_prefill_workspace_bytes() is 0.  Otherwise (F16 / BF16, not causal,
+ * no mask, no per-batch lengths, kernel head dim 64 or 128, and a 128-row
+ * tile count that is not a multiple of 256) the tiles past the last multiple
+ * of 256 (at most 128 of them) each run as two pieces of the key range, each
+ * piece writing its
+ * partial numerators, running max and row sum to the workspace, and a second
+ * kernel merges the pieces by the rescaling of the two-pass split-K vector
+ * kernel of the "Add D512 support to Metal vector attention" page (the same
+ * algebra as the rustytorch "flash_attention.metal" page's "Online softmax
+ * update"), sink and log-sum-exp included.  Two launches on `stream`.  The
+ * workspace is device memory of at least sdpa_prefill_workspace_bytes()
+ * bytes, 16-byte aligned, caller-owned; its contents need not be initialised
+ * and are overwritten.
+ * SDPA_ERR_WORKSPACE if it is needed and missing, too small or misaligned. */
+SDPA_API int sdpa_prefill_ws(const sdpa_args *args, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Workspace bytes sdpa_prefill_ws needs for these arguments (0: none, and
+ * sdpa_prefill_ws is sdpa_prefill).  Host-only; reads the sizes, dtype, the
+ * causal flag and whether mask / seqlens pointers are set (no other pointer
+ * or stride); 0 for invalid sizes. */
+SDPA_API size_t sdpa_prefill_workspace_bytes(const sdpa_args *args);
+
 /* Decode: single-query (Lq == 1) or multi-query (1 <= Lq <= 16) attention
  * whose keys stream once per KV head.  The Lq query rows and the Hq / Hkv
  * query heads sharing a KV head are processed together; causal is

@@ -29,7 +29,7 @@ from typing import Optional
 import torch
 
 __all__ = ["prefill", "decode", "decode_noalloc", "DECODE_SCRATCH_BYTES", "decode_num_splits",
-           "decode_workspace_bytes", "prefill_backward", "attention", "SdpaArgs", "SdpaBwdArgs", "library",
+           "decode_workspace_bytes", "prefill_workspace_bytes", "prefill_backward", "attention", "SdpaArgs", "SdpaBwdArgs", "library",
            "library_path", "Status", "SdpaError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -101,6 +101,10 @@ def library():
     lib.sdpa_prefill.restype = ctypes.c_int
     lib.sdpa_prefill_check.argtypes = [P]
     lib.sdpa_prefill_check.restype = ctypes.c_int
+    lib.sdpa_prefill_ws.argtypes = [P, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.sdpa_prefill_ws.restype = ctypes.c_int
+    lib.sdpa_prefill_workspace_bytes.argtypes = [P]
+    lib.sdpa_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.sdpa_decode.argtypes = [P, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.sdpa_decode.restype = ctypes.c_int
     lib.sdpa_decode_check.argtypes = [P, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t]
@@ -214,10 +218,14 @@ def _common(q, k, v, scale, mask, sinks, Lq_expected=None):
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional[float] = None,
             causal: bool = False, mask: Optional[torch.Tensor] = None,
             sinks: Optional[torch.Tensor] = None, return_lse: bool = False,
-            out: Optional[torch.Tensor] = None, seqlens_q=None, seqlens_k=None):
+            out: Optional[torch.Tensor] = None, seqlens_q=None, seqlens_k=None,
+            split_tail: bool = True, workspace: Optional[torch.Tensor] = None):
     """Fused attention forward over a whole query block (prefill / full
     self-attention).  seqlens_q / seqlens_k: real query rows / keys of each
-    batch (the rest is padding; padding rows come out as rows with no key)."""
+    batch (the rest is padding; padding rows come out as rows with no key).
+    split_tail: call sdpa_prefill_ws, which runs the query tiles past the last
+    multiple of the compute units as key pieces (with a workspace, allocated
+    here unless one is given) where that applies; False: sdpa_prefill."""
     lib = library()
     q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
@@ -227,10 +235,28 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
     a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    st = lib.sdpa_prefill(ctypes.byref(a), ctypes.c_void_p(stream))
+    need = int(lib.sdpa_prefill_workspace_bytes(ctypes.byref(a))) if split_tail else 0
+    if need > 0:
+        if workspace is None or workspace.numel() * workspace.element_size() < need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        st = lib.sdpa_prefill_ws(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
+                                 workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
+    else:
+        st = lib.sdpa_prefill(ctypes.byref(a), ctypes.c_void_p(stream))
     if st != 0:
         _raise(st)
     return (o, lse) if return_lse else o
+
+
+def prefill_workspace_bytes(q, k, v, *, causal: bool = False, mask=None, seqlens=False) -> int:
+    """Workspace bytes sdpa_prefill_ws needs (0: none) for these shapes; a
+    mask or per-batch lengths (seqlens=True) rule the tail split out."""
+    lib = library()
+    a = _size_args(q, k, v)
+    a.causal = int(bool(causal))
+    if mask is not None or seqlens:
+        return 0
+    return int(lib.sdpa_prefill_workspace_bytes(ctypes.byref(a)))
 
 
 def _decode_args(q, k, v, scale, mask, sinks):

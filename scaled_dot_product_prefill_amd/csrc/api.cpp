@@ -8,6 +8,7 @@
 // support to Metal vector attention" page.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -218,6 +219,50 @@ struct SplitPlan {
 // within a few percent of the best fixed split count for each.
 constexpr int64_t kDecodeCUs = 256;
 constexpr int64_t kDecodeMaxTilesPerSplit = 32;
+
+// Prefill tail split (16-bit, non-causal, no mask, no per-batch lengths,
+// kernel head dim <= 128).  The query tiles take about equal time, and the
+// kernel runs as long as the compute unit that gets the most of them:
+// ceil(tiles / 256) tiles' worth (a sweep of the head count at B2 L4250 D64
+// moves in those steps).  The r = tiles % 256 tiles past the last multiple of
+// 256 therefore run as two key pieces each (pieces of a whole number of
+// 64-key tiles; needs r <= 128), so that they spread over 2 r compute units
+// and add half a tile's time instead of a whole one; a merge kernel combines
+// the pieces.  More pieces per tile (up to 8) measured slower on the DiT
+// shape (B2 H38 L4250 D64, r = 24; same box, fp16 one pass 377 us: 2 pieces
+// 364 us, 4 pieces 368 us, 8 pieces 375 us): each piece pays the start of a
+// tile loop and writes a whole partial.  Not without a workspace
+// (sdpa_prefill).
+constexpr int64_t kTailPieces = 2;
+struct TailPlan {
+  int64_t tiles = 0;
+  int64_t tail = 0;
+  int k = 1;
+  int64_t chunk = 0;
+};
+TailPlan plan_tail(const sdpa_args* a) {
+  TailPlan t;
+  if (a->dtype == SDPA_F32 || a->causal || a->mask || a->seqlens_q || a->seqlens_k) return t;
+  if (prefill_narrow(a) || kernel_dim(a) > 128) return t;
+  const int64_t tiles = (a->Lq + 127) / 128 * a->B * a->Hq;
+  const int64_t r = tiles % kDecodeCUs;
+  if (tiles < kDecodeCUs || r == 0) return t;
+  const int64_t k0 = std::min<int64_t>(kTailPieces, kDecodeCUs / r);
+  if (k0 < 2) return t;
+  const int64_t chunk = ((a->Lk + k0 - 1) / k0 + 63) / 64 * 64;
+  const int64_t k = (a->Lk + chunk - 1) / chunk;
+  if (k < 2) return t;
+  t.tiles = tiles;
+  t.tail = r;
+  t.k = (int)k;
+  t.chunk = chunk;
+  return t;
+}
+// partial numerators [piece][128][kernel head dim] and (max, sum) [piece][128][2]
+size_t tail_workspace(const sdpa_args* a, const TailPlan& t) {
+  if (t.tail == 0) return 0;
+  return (size_t)t.tail * t.k * 128 * (size_t)(kernel_dim(a) + 2) * sizeof(float);
+}
 
 SplitPlan plan_splits(const sdpa_args* a, int num_splits) {
   SplitPlan sp;
@@ -450,6 +495,10 @@ AttnParams make_params(const sdpa_args& a) {
   p.nsplit = 1;
   p.nchunk = 1;
   p.split_len = (int)a.Lk;
+  p.tiles = 0;
+  p.tail_tiles = 0;
+  p.tail_k = 1;
+  p.tail_chunk = (int)a.Lk;
   return p;
 }
 
@@ -475,6 +524,31 @@ int sdpa_prefill(const sdpa_args* args, void* stream) {
     return sdpa::launch_status(sdpa::launch_decode(p, args->dtype, (hipStream_t)stream));
   }
   return sdpa::launch_status(sdpa::launch_prefill(p, args->dtype, args->causal != 0, (hipStream_t)stream));
+}
+
+size_t sdpa_prefill_workspace_bytes(const sdpa_args* args) {
+  // sizes only (like the decode query): pointers and strides are not needed
+  if (sdpa::check_sizes(args) != SDPA_OK || sdpa::kernel_dim(args) == 0) return 0;
+  return sdpa::tail_workspace(args, sdpa::plan_tail(args));
+}
+
+int sdpa_prefill_ws(const sdpa_args* args, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = sdpa::check_prefill(args);
+  if (st != SDPA_OK) return st;
+  const sdpa::TailPlan t = sdpa::plan_tail(args);
+  const size_t need = sdpa::tail_workspace(args, t);
+  if (need == 0) return sdpa_prefill(args, stream);
+  if (workspace == nullptr || workspace_bytes < need)
+    return sdpa::fail(SDPA_ERR_WORKSPACE, "prefill workspace: need %zu bytes, got %zu%s", need, workspace_bytes,
+                      workspace ? "" : " (null)");
+  if (((uintptr_t)workspace & 15) != 0) return sdpa::fail(SDPA_ERR_WORKSPACE, "prefill workspace not 16-byte aligned");
+  sdpa::AttnParams p = sdpa::make_params(*args);
+  p.tail_tiles = (int)t.tail;
+  p.tail_k = t.k;
+  p.tail_chunk = (int)t.chunk;
+  p.part_o = (float*)workspace;
+  p.part_ml = p.part_o + (size_t)t.tail * t.k * 128 * sdpa::kernel_dim(args);
+  return sdpa::launch_status(sdpa::launch_prefill(p, args->dtype, false, (hipStream_t)stream));
 }
 
 int sdpa_decode_check(const sdpa_args* args, int num_splits, const void* workspace, size_t workspace_bytes) {

@@ -458,8 +458,21 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   const int g = lane >> 5;
 
   const int nqt = (p.Lq + BM - 1) / BM;
+  // Work item: a query tile of the work list, or (non-causal, no mask) one
+  // key piece of a tail tile.  The tiles' count per compute unit sets the
+  // kernel's time (each runs about as long as the others), so the tiles past
+  // the last multiple of the compute units run as pieces spread over several
+  // units, and a merge kernel combines their partials.
+  int item = (int)blockIdx.x, piece = -1;
+  if constexpr (!CAUSAL && !MASK) {
+    const int first = p.tiles - p.tail_tiles;
+    if (item >= first) {
+      piece = (item - first) % p.tail_k;
+      item = first + (item - first) / p.tail_k;
+    }
+  }
   int qt, bh;
-  prefill_tile((int)blockIdx.x, (int)gridDim.x, nqt, p.B * p.Hq, CAUSAL, qt, bh);
+  prefill_tile(item, p.tiles, nqt, p.B * p.Hq, CAUSAL, qt, bh);
   const int b = bh / p.Hq;
   const int hq = bh % p.Hq;
   const int hk = hq / p.group;
@@ -467,9 +480,12 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   const int i0 = qt * BM;
   const int iw = i0 + 32 * wave;
   const int my_i = iw + l32;
-  // real query rows and keys of this batch; bottom-right causal offset
+  // real query rows and keys of this batch (a piece: its own key range, from
+  // key kbeg on); bottom-right causal offset
   const int lq = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_q, b, p.Lq));
-  const int lk = __builtin_amdgcn_readfirstlane(batch_len(p.seqlens_k, b, p.Lk));
+  const int kbeg = piece >= 0 ? piece * p.tail_chunk : 0;
+  const int lk = __builtin_amdgcn_readfirstlane(
+      piece >= 0 ? min(p.Lk - kbeg, p.tail_chunk) : batch_len(p.seqlens_k, b, p.Lk));
   const int coff = lk - lq;
 
   // exponent scale c = |scale| log2(e); a negative scale is moved into Q.
@@ -529,8 +545,8 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
   // ---- direct buffer -> LDS loads.  Wave w fills lines w, w + NW, ... of a
   // tile; line i of a wave sits i * STEP_ROWS rows below line 0 and both
   // swizzles repeat every 16 rows: one per-lane offset plus a uniform step.
-  const S* kbase = uniform_ptr((const S*)p.k + b * p.ks[0] + hk * p.ks[1]);
-  const S* vbase = uniform_ptr((const S*)p.v + b * p.vs[0] + hk * p.vs[1]);
+  const S* kbase = uniform_ptr((const S*)p.k + b * p.ks[0] + hk * p.ks[1] + (int64_t)kbeg * p.ks[2]);
+  const S* vbase = uniform_ptr((const S*)p.v + b * p.vs[0] + hk * p.vs[1] + (int64_t)kbeg * p.vs[2]);
   // A lane whose chunk lies past the real head dim loads nothing (kNoLoad).
   uint32_t koff[C::KVAR], voff;
   {
@@ -1067,6 +1083,23 @@ __device__ __forceinline__ void prefill16_body(const AttnParams& p) {
     m_run = kNegInf;
     l_tot = 0.f;
   }
+  if constexpr (!CAUSAL && !MASK) {
+    if (piece >= 0) {
+      // a piece's partial: the unnormalised numerators, the reference max
+      // (log2 units) and the row sum; the sink enters at the merge
+      const int part = (int)blockIdx.x - (p.tiles - p.tail_tiles);
+      const int row = 32 * wave + l32;
+      float* po = p.part_o + ((int64_t)part * BM + row) * D;
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *(f32x4*)(po + 32 * mb + 8 * q4 + 4 * g) =
+              f32x4{acc[mb][4 * q4], acc[mb][4 * q4 + 1], acc[mb][4 * q4 + 2], acc[mb][4 * q4 + 3]};
+      if (g == 0) *(f32x2*)(p.part_ml + ((int64_t)part * BM + row) * 2) = f32x2{m_run, l_tot};
+      return;
+    }
+  }
   float M = m_run, Ltot = l_tot;
   if (p.sinks) {
     const float sk = p.sinks[hq] * kLog2e;
@@ -1107,6 +1140,55 @@ __global__ __launch_bounds__(kThreads, 1) void prefill16_mask_kernel(AttnParams 
   prefill16_body<T, D, CAUSAL, true, kWaves, false>(p);
 }
 
+// The tail tiles' pieces, merged: workgroup = (tail tile, quarter of its 128
+// rows), 8 threads per row, each over D/8 columns.  Per row: M = the largest
+// piece max (and the sink), each piece weighted by 2^(m - M), the sink added
+// to the denominator, as the one-pass epilogue does; the pieces are summed in
+// piece order, so the result does not depend on which finished first.
+constexpr int kMergeRowsThreads = 256;
+template <class T, int D>
+__global__ __launch_bounds__(kMergeRowsThreads) void prefill_tail_merge_kernel(AttnParams p) {
+  using S = uint16_t;
+  constexpr int BM = kBM, ROWS = BM / 4, TPR = kMergeRowsThreads / ROWS, CPT = D / TPR;
+  static_assert(CPT % 4 == 0, "merge columns");
+  const int tile = (int)blockIdx.x / 4, quarter = (int)blockIdx.x % 4;
+  const int item = p.tiles - p.tail_tiles + tile;
+  int qt, bh;
+  prefill_tile(item, p.tiles, (p.Lq + BM - 1) / BM, p.B * p.Hq, false, qt, bh);
+  const int b = bh / p.Hq, hq = bh % p.Hq;
+  const int row = quarter * ROWS + (int)threadIdx.x / TPR, c0 = ((int)threadIdx.x % TPR) * CPT;
+  const int i = qt * BM + row;
+  if (i >= p.Lq) return;
+  const int k = p.tail_k;
+  const int64_t base = (int64_t)tile * k;
+  float M = p.sinks ? p.sinks[hq] * kLog2e : kNegInf;
+  for (int j = 0; j < k; ++j) M = fmaxf(M, p.part_ml[((base + j) * BM + row) * 2]);
+  float L = 0.f;
+  if (M != kNegInf) {
+    for (int j = 0; j < k; ++j) {
+      const f32x2 ml = *(const f32x2*)(p.part_ml + ((base + j) * BM + row) * 2);
+      if (ml[0] != kNegInf) L += ml[1] * fast_exp2(ml[0] - M);
+    }
+    if (p.sinks) L += fast_exp2(p.sinks[hq] * kLog2e - M);
+  }
+  const float inv = (M != kNegInf && L > 0.f) ? 1.f / L : 0.f;
+  S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)i * p.os[2];
+#pragma unroll
+  for (int c = c0; c < c0 + CPT; c += 4) {
+    f32x4 o = f32x4{};
+    for (int j = 0; j < k; ++j) {
+      const float m = p.part_ml[((base + j) * BM + row) * 2];
+      if (m == kNegInf) continue;
+      const float w = fast_exp2(m - M) * inv;
+      const f32x4 v = *(const f32x4*)(p.part_o + ((base + j) * BM + row) * D + c);
+      o += v * w;
+    }
+    if (c < p.Dv) *(u32x2*)(orow + c) = u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
+  }
+  if (p.lse && c0 == 0)
+    p.lse[((int64_t)b * p.Hq + hq) * p.Lq + i] = (M != kNegInf && L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
+}
+
 template <class T, int D>
 hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
   const bool mask = p.mask != nullptr;
@@ -1125,21 +1207,29 @@ hipError_t launch_t(const AttnParams& p, bool causal, hipStream_t s) {
     // 4-wave workgroups of 128 query rows.  (2-wave workgroups for D = 64 shrink
     // the idle tail of the last round but double the K/V tile traffic into
     // LDS, and measure slower.)
-    const dim3 grid((unsigned)((p.Lq + kBM - 1) / kBM * p.B * p.Hq));
+    AttnParams q = p;
+    q.tiles = (p.Lq + kBM - 1) / kBM * p.B * p.Hq;
+    const dim3 grid((unsigned)(q.tiles + q.tail_tiles * (q.tail_k - 1)));
     const dim3 block(kThreads);
     // pre-scaled Q: fp16, exponent scale at most 1, no log-sum-exp output
     const bool rel = std::is_same<T, TF16>::value && fabsf(p.scale_log2) <= 1.f && p.lse == nullptr;
     if (mask) {
-      if (causal) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, true>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((prefill16_mask_kernel<T, D, false>), grid, block, 0, s, p);
+      if (causal) hipLaunchKernelGGL((prefill16_mask_kernel<T, D, true>), grid, block, 0, s, q);
+      else hipLaunchKernelGGL((prefill16_mask_kernel<T, D, false>), grid, block, 0, s, q);
     } else if (rel) {
       if constexpr (std::is_same<T, TF16>::value) {
-        if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves, true>), grid, block, 0, s, p);
-        else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves, true>), grid, block, 0, s, p);
+        if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves, true>), grid, block, 0, s, q);
+        else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves, true>), grid, block, 0, s, q);
       }
     } else {
-      if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves, false>), grid, block, 0, s, p);
-      else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves, false>), grid, block, 0, s, p);
+      if (causal) hipLaunchKernelGGL((prefill16_kernel<T, D, true, kWaves, false>), grid, block, 0, s, q);
+      else hipLaunchKernelGGL((prefill16_kernel<T, D, false, kWaves, false>), grid, block, 0, s, q);
+    }
+    if (q.tail_tiles > 0) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL((prefill_tail_merge_kernel<T, D>), dim3((unsigned)(q.tail_tiles * 4)), dim3(kMergeRowsThreads),
+                         0, s, q);
     }
   }
   return hipGetLastError();

@@ -33,11 +33,21 @@ struct AttnParams {
   int split_len;     // keys per split
   float* part_o;     // [B*Hq*Lq, nsplit, D]  fp32 partial numerators
   float* part_ml;    // [B*Hq*Lq, nsplit, 2]  fp32 (running max in log2 units, sum)
+  // 16-bit prefill work list: `tiles` query tiles (128 rows x one (b, hq));
+  // the last tail_tiles of them run as tail_k pieces of tail_chunk keys each,
+  // whose partials (part_o: [piece][128 rows][D], part_ml: [piece][128][2])
+  // a merge kernel combines (0 tail tiles: one pass per tile)
+  int tiles;
+  int tail_tiles;
+  int tail_k;
+  int tail_chunk;
 };
 
 AttnParams make_params(const sdpa_args& a);
 
-// Kernel launchers: return hipSuccess or the launch error.
+// Kernel launchers: return hipSuccess or the launch error.  launch_prefill
+// sets p.tiles itself; a tail split (p.tail_tiles > 0, non-causal 16-bit
+// without a mask, kernel head dim <= 128) also enqueues the merge.
 hipError_t launch_prefill(const AttnParams& p, int dtype, bool causal, hipStream_t s);
 hipError_t launch_decode(const AttnParams& p, int dtype, hipStream_t s);
 // 16-bit prefill at kernel head dim 512 (sets its own column chunks), one pass

@@ -326,6 +326,36 @@ def test_backward_head_split_plan(lib):
     assert ws(B=1, Hq=6, Hkv=1, Lq=7, Lk=700) == base(1, 6, 7) + part(6, 1, 1, 700, 128)
 
 
+def test_prefill_tail_plan(lib):
+    # The workspace form of prefill runs the r 128-row tiles past the last
+    # multiple of 256 (r <= 128) as two key pieces of whole 64-key tiles each;
+    # 16-bit, non-causal, no mask or per-batch lengths, kernel head dim <= 128.
+    # Workspace: per piece 128 rows of kernel-dim numerators plus (max, sum),
+    # fp32.
+    def ws(**kw):
+        a = _args(**kw)
+        return lib.sdpa_prefill_workspace_bytes(ctypes.byref(a))
+    part = lambda r, kd: r * 2 * 128 * (kd + 2) * 4
+    dit = dict(B=2, Hq=38, Hkv=38, Lq=4250, Lk=4250, D=64, dtype=sdpa.F16)
+    assert ws(**dit) == part(24, 64)  # 2584 tiles: 24 past 2560
+    assert ws(**{**dit, "dtype": sdpa.BF16}) == part(24, 64)
+    assert ws(**{**dit, "Hq": 42, "Hkv": 42}) == part(40, 64)  # 2856 tiles: 40 past 2816
+    assert ws(**{**dit, "causal": 1}) == 0
+    assert ws(**{**dit, "dtype": sdpa.F32}) == 0
+    assert ws(**{**dit, "D": 256}) == 0
+    assert ws(**{**dit, "mask": 1 << 41}) == 0
+    assert ws(**{**dit, "seqlens_k": 1 << 41}) == 0
+    assert ws(**{**dit, "Hq": 36, "Hkv": 36}) == 0  # 2448 tiles: 144 past 2304, more than 128
+    assert ws(B=1, Hq=32, Hkv=32, Lq=4096, Lk=4096, D=128) == 0  # 1024 tiles
+    assert ws(B=1, Hq=2, Hkv=2, Lq=128, Lk=128, D=64) == 0  # fewer tiles than compute units
+    assert ws(B=1, Hq=257, Hkv=257, Lq=128, Lk=64, D=64) == 0  # one key tile: nothing to split
+    # the GPU test cases
+    assert ws(B=1, Hq=65, Hkv=65, Lq=512, Lk=512, D=64, dtype=sdpa.F16) == part(4, 64)
+    assert ws(B=2, Hq=33, Hkv=33, Lq=512, Lk=300, D=64, dtype=sdpa.F16) == part(8, 64)
+    assert ws(B=1, Hq=65, Hkv=13, Lq=500, Lk=700, D=128, dtype=sdpa.F16) == part(4, 128)
+    assert ws(B=1, Hq=130, Hkv=130, Lq=256, Lk=4250, D=64, dtype=sdpa.F16) == part(4, 64)
+
+
 def test_noalloc_decode_rejects_partials_beyond_the_static_scratch(lib):
     # long-context decode shape at 128 splits: 8*32*1*128*(128+2)*4 bytes of
     # partials > 16 MiB; rejected by validation before any HIP call

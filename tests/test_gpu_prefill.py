@@ -39,6 +39,43 @@ def test_tiny_fp32_full():
     compare_full(out, l, x, sc, w.dtype, w.name)
 
 
+# (B, Hq, Hkv, Lq, Lk, D, sinks): 128-row tile counts just past a multiple of
+# 256, so that the workspace form runs the last tiles as two key pieces each
+# and merges them (4 or 8 tail tiles, ragged last pieces and rows)
+TAIL = [
+    (1, 65, 65, 512, 512, 64, False),     # 260 tiles, pieces of 256 keys
+    (1, 65, 13, 500, 700, 128, True),     # GQA-5, sinks, pieces of 384 and 316 keys
+    (2, 33, 33, 512, 300, 64, True),      # 264 tiles, pieces of 192 and 108 keys
+    (1, 130, 130, 256, 4250, 64, False),  # pieces of 2176 and 2074 keys
+]
+
+
+@pytest.mark.parametrize("dtype,lse", [("fp16", False), ("fp16", True), ("bf16", True)])
+@pytest.mark.parametrize("case", range(len(TAIL)))
+def test_prefill_tail_pieces(dtype, lse, case):
+    B, Hq, Hkv, Lq, Lk, D, sinks = TAIL[case]
+    say(f"prefill tail pieces {dtype} lse={lse} case={TAIL[case]}")
+    x = random_case(5000 + 10 * case, B, Hq, Hkv, Lq, Lk, D, dtype, sinks=sinks, sink_scale=2.0)
+    d = to_dev(x)
+    sc = 1.0 / math.sqrt(D)
+    assert sdpa.prefill_workspace_bytes(d["q"], d["k"], d["v"]) > 0  # the split applies
+    runs = []
+    for split in (True, True, False):
+        r = sdpa.prefill(d["q"], d["k"], d["v"], scale=sc, sinks=d["sinks"], return_lse=lse, split_tail=split)
+        runs.append(r if lse else (r, None))
+    torch.cuda.synchronize()
+    out, l = runs[0]
+    compare_full(out, l, x, sc, dtype, f"tail{case}-{dtype}-lse{int(lse)}")
+    # no atomics: the same call gives the same bits
+    assert torch.equal(runs[0][0], runs[1][0])
+    # and the one-pass form agrees within the gates: each piece rounds its
+    # probabilities against its own running max (bf16: 8 bits), so the row
+    # sums, and the LSE, differ in their last bits
+    torch.testing.assert_close(out.float(), runs[2][0].float(), atol=2e-3, rtol=1e-2)
+    if lse:
+        torch.testing.assert_close(l, runs[2][1], atol=1e-3, rtol=0)
+
+
 # (B, Hq, Hkv, Lq, Lk, causal, mask, sinks)
 GRID = [
     (1, 2, 2, 200, 333, False, False, False),   # ragged non-causal
