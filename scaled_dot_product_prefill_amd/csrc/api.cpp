@@ -251,7 +251,7 @@ TailPlan plan_tail(const sdpa_args* a) {
   if (k0 < 2) return t;
   const int64_t chunk = ((a->Lk + k0 - 1) / k0 + 63) / 64 * 64;
   const int64_t k = (a->Lk + chunk - 1) / chunk;
-  if (k < 2) return t;
+  if (k != kTailPieces) return t;  // the merge kernel takes exactly two pieces
   t.tiles = tiles;
   t.tail = r;
   t.k = (int)k;

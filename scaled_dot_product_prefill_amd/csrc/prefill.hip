@@ -1141,15 +1141,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill16_mask_kernel(AttnParams 
 }
 
 // The tail tiles' pieces, merged: workgroup = (tail tile, quarter of its 128
-// rows), 8 threads per row, each over D/8 columns.  Per row: M = the largest
+// rows), 8 threads per row, each over D/8 columns.  Per row: M = the larger
 // piece max (and the sink), each piece weighted by 2^(m - M), the sink added
 // to the denominator, as the one-pass epilogue does; the pieces are summed in
-// piece order, so the result does not depend on which finished first.
+// piece order, so the result does not depend on which finished first.  Two
+// pieces per tile (the host's plan): every load is issued before the first
+// use, the kernel being a few dependent memory round trips long.
 constexpr int kMergeRowsThreads = 256;
+constexpr int kTailPiecesK = 2;
 template <class T, int D>
 __global__ __launch_bounds__(kMergeRowsThreads) void prefill_tail_merge_kernel(AttnParams p) {
   using S = uint16_t;
-  constexpr int BM = kBM, ROWS = BM / 4, TPR = kMergeRowsThreads / ROWS, CPT = D / TPR;
+  constexpr int BM = kBM, ROWS = BM / 4, TPR = kMergeRowsThreads / ROWS, CPT = D / TPR, K = kTailPiecesK;
   static_assert(CPT % 4 == 0, "merge columns");
   const int tile = (int)blockIdx.x / 4, quarter = (int)blockIdx.x % 4;
   const int item = p.tiles - p.tail_tiles + tile;
@@ -1159,31 +1162,35 @@ __global__ __launch_bounds__(kMergeRowsThreads) void prefill_tail_merge_kernel(A
   const int row = quarter * ROWS + (int)threadIdx.x / TPR, c0 = ((int)threadIdx.x % TPR) * CPT;
   const int i = qt * BM + row;
   if (i >= p.Lq) return;
-  const int k = p.tail_k;
-  const int64_t base = (int64_t)tile * k;
-  float M = p.sinks ? p.sinks[hq] * kLog2e : kNegInf;
-  for (int j = 0; j < k; ++j) M = fmaxf(M, p.part_ml[((base + j) * BM + row) * 2]);
-  float L = 0.f;
-  if (M != kNegInf) {
-    for (int j = 0; j < k; ++j) {
-      const f32x2 ml = *(const f32x2*)(p.part_ml + ((base + j) * BM + row) * 2);
-      if (ml[0] != kNegInf) L += ml[1] * fast_exp2(ml[0] - M);
-    }
-    if (p.sinks) L += fast_exp2(p.sinks[hq] * kLog2e - M);
+  const int64_t base = (int64_t)tile * K;
+  f32x2 ml[K];
+  f32x4 v[K][CPT / 4];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    ml[j] = *(const f32x2*)(p.part_ml + ((base + j) * BM + row) * 2);
+#pragma unroll
+    for (int c = 0; c < CPT / 4; ++c) v[j][c] = *(const f32x4*)(p.part_o + ((base + j) * BM + row) * D + c0 + 4 * c);
   }
+  const float sk = p.sinks ? p.sinks[hq] * kLog2e : kNegInf;
+  float M = sk;
+#pragma unroll
+  for (int j = 0; j < K; ++j) M = fmaxf(M, ml[j][0]);
+  float w[K], L = 0.f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    w[j] = (M != kNegInf && ml[j][0] != kNegInf) ? fast_exp2(ml[j][0] - M) : 0.f;
+    L += ml[j][1] * w[j];
+  }
+  if (p.sinks && M != kNegInf) L += fast_exp2(sk - M);
   const float inv = (M != kNegInf && L > 0.f) ? 1.f / L : 0.f;
   S* orow = (S*)p.o + b * p.os[0] + hq * p.os[1] + (int64_t)i * p.os[2];
 #pragma unroll
-  for (int c = c0; c < c0 + CPT; c += 4) {
+  for (int c = 0; c < CPT / 4; ++c) {
     f32x4 o = f32x4{};
-    for (int j = 0; j < k; ++j) {
-      const float m = p.part_ml[((base + j) * BM + row) * 2];
-      if (m == kNegInf) continue;
-      const float w = fast_exp2(m - M) * inv;
-      const f32x4 v = *(const f32x4*)(p.part_o + ((base + j) * BM + row) * D + c);
-      o += v * w;
-    }
-    if (c < p.Dv) *(u32x2*)(orow + c) = u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
+#pragma unroll
+    for (int j = 0; j < K; ++j) o += v[j][c] * (w[j] * inv);
+    const int col = c0 + 4 * c;
+    if (col < p.Dv) *(u32x2*)(orow + col) = u32x2{cvt_pk(T{}, o[0], o[1]), cvt_pk(T{}, o[2], o[3])};
   }
   if (p.lse && c0 == 0)
     p.lse[((int64_t)b * p.Hq + hq) * p.Lq + i] = (M != kNegInf && L > 0.f) ? (M + fast_log2(L)) * kLn2 : kNegInf;
