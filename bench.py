@@ -624,7 +624,7 @@ def main():
         res.update(value=round(tf, 2), unit="TFLOP/s", dtype=pre_w.dtype)
         res["roofline"] = {"bound": "mfma", "achieved": round(tf, 2), "peak": peak, "unit": "TFLOP/s",
                            "frac": round(tf / peak, 4), "traffic": load_traffic("prefill_" + pre_w.name),
-                           "kernel": ("bwd_prep + bwd_dq + bwd_dkv kernels" if pre_w.grad else
+                           "kernel": ("bwd_dq + bwd_dkv kernels" if pre_w.grad else
                                       "prefill_kernel + prefill_tail_merge_kernel" if tail_split else "prefill_kernel"),
                            "avg_ms": round(avg, 5),
                            "median_ms": round(median(pm), 5),

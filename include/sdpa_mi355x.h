@@ -281,9 +281,9 @@ SDPA_API size_t sdpa_decode_workspace_bytes(const sdpa_args *args, int num_split
  * 256-key dK / dV blocks are split over hs query-head groups (hs the largest
  * divisor of Hq / Hkv with B * Hkv * ceil(Lk / 256) * hs <= 512),
  * hs * B * Hkv * Lk * 2 * (64 or 128, the kernel head dim) * 4 bytes of
- * fp32 dK / dV shares.  Four or five kernels are enqueued on `stream`
- * (a reduction of the shares when split); nothing is allocated or
- * synchronised.
+ * fp32 dK / dV shares.  Two to four kernels are enqueued on `stream` (dQ,
+ * dK/dV, a reduction of the shares when split, the sink gradient when
+ * asked for); nothing is allocated or synchronised.
  * The outputs must not overlap each other, the inputs or the workspace. */
 typedef struct sdpa_bwd_args {
   const void *dout; int64_t dout_stride[3];  /* [B, Hq,  Lq, Dv] upstream gradient */

@@ -24,8 +24,6 @@
 // fewer in the dQ kernel).
 //
 // Kernels, in launch order:
-//   bwd_prep_kernel   LSE_i in log2 units (+inf for rows without a key or
-//                     past the batch's length) into the workspace;
 //   bwd_dq_kernel     workgroup = 128 query rows of one (batch, query head);
 //                     each wave owns 32 rows, key tiles stream through LDS:
 //                     for rows that see few keys twice, S^T = K Q^T and
@@ -232,15 +230,17 @@ __device__ inline u32x4 pack_b(const f32x16& x, int u) {
 }
 
 // ---- the LSE in log2 units ------------------------------------------------
-__global__ __launch_bounds__(kBwdThreads) void bwd_prep_kernel(BwdParams bp) {
+// Row my_i of (b, hq): LSE_i * log2(e), +inf for a row without a key or past
+// the batch's length (ok false).  The dQ kernels, which run first and cover
+// every row once, also store it (lanes of the first half) in the workspace
+// for the dK/dV and sink-gradient kernels.
+__device__ inline float lse_log2(const BwdParams& bp, int b, int hq, int my_i, bool ok) {
   const AttnParams& p = bp.f;
-  const int64_t nrows = (int64_t)p.B * p.Hq * p.Lq;
-  const int64_t row = (int64_t)blockIdx.x * kBwdThreads + threadIdx.x;
-  if (row >= nrows) return;
-  const int i = (int)(row % p.Lq);
-  const int b = (int)(row / p.Lq / p.Hq);
-  const float lse = i < batch_len(p.seqlens_q, b, p.Lq) ? p.lse[row] : kNegInf;
-  bp.ws_l[row] = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+  const int64_t row = ((int64_t)b * p.Hq + hq) * p.Lq + my_i;
+  const float lse = ok ? p.lse[row] : kNegInf;
+  const float l2 = lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+  if (my_i < p.Lq && (threadIdx.x & 32) == 0) bp.ws_l[row] = l2;
+  return l2;
 }
 
 // ---- dQ ---------------------------------------------------------------------
@@ -283,8 +283,7 @@ __global__ __launch_bounds__(kBwdThreads, MASK ? 1 : 2) void bwd_dq_kernel(BwdPa
       doreg[s] = ok && ch < nd ? d : u32x4{0, 0, 0, 0};
     }
   }
-  const int64_t wrow = ((int64_t)b * p.Hq + hq) * p.Lq + (ok ? my_i : 0);
-  const float lse2 = ok ? bp.ws_l[wrow] : __builtin_inff();
+  const float lse2 = lse_log2(bp, b, hq, my_i, ok);
 
   int kend = i0 < lq ? lk : 0;
   if (CAUSAL) kend = min(kend, min(i0 + 128, lq) + coff);
@@ -827,8 +826,7 @@ __global__ __launch_bounds__(kBwdThreads, 1) void bwd_dq_f32_kernel(BwdParams bp
     }
   }
   const float dval = ok ? sum_xor32(dsum) : 0.f;
-  const int64_t wrow = ((int64_t)b * p.Hq + hq) * p.Lq + (ok ? my_i : 0);
-  const float lse2 = ok ? bp.ws_l[wrow] : __builtin_inff();
+  const float lse2 = lse_log2(bp, b, hq, my_i, ok);
   if (my_i < p.Lq && g == 0) bp.ws_d[((int64_t)b * p.Hq + hq) * p.Lq + my_i] = dval;
 
   int kend = i0 < lq ? lk : 0;
@@ -1050,11 +1048,7 @@ hipError_t launch_main(const BwdParams& bp, hipStream_t s) {
 template <class T, int D>
 hipError_t launch_td(const BwdParams& bp, bool causal, hipStream_t s) {
   const AttnParams& p = bp.f;
-  const int64_t nrows = (int64_t)p.B * p.Hq * p.Lq;
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((nrows + kBwdThreads - 1) / kBwdThreads)), dim3(kBwdThreads),
-                     0, s, bp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   const bool mask = p.mask != nullptr;
   if (causal) e = mask ? launch_main<T, D, true, true>(bp, s) : launch_main<T, D, true, false>(bp, s);
   else e = mask ? launch_main<T, D, false, true>(bp, s) : launch_main<T, D, false, false>(bp, s);
