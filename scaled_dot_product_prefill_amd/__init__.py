@@ -140,15 +140,62 @@ def _raise(status: int):
     raise SdpaError(status, msg)
 
 
+def _aligned(x: torch.Tensor) -> bool:
+    """Unit last-dim stride and 16-byte aligned pointer and strides (the rule
+    of prepare_sdpa_input on the mlx 0.30.7 page)."""
+    es = x.element_size()
+    return (x.stride(-1) == 1 and x.data_ptr() % 16 == 0
+            and all((s * es) % 16 == 0 for s in x.stride()[:3]))
+
+
 def _prep(x: torch.Tensor, name: str) -> torch.Tensor:
-    """Unit last-dim stride and 16-byte aligned pointer and strides, else a
-    contiguous copy (the rule of prepare_sdpa_input on the mlx 0.30.7 page)."""
+    """x itself if it meets the layout rule of _aligned, else a contiguous copy."""
     if x.dim() != 4:
         raise ValueError(f"{name} must be 4-D [B, H, L, D], got {tuple(x.shape)}")
-    es = x.element_size()
-    ok = (x.stride(-1) == 1 and x.data_ptr() % 16 == 0
-          and all((s * es) % 16 == 0 for s in x.stride()[:3]))
-    return x if ok else x.contiguous()
+    return x if _aligned(x) else x.contiguous()
+
+
+def _on_device(t: torch.Tensor, name: str, device) -> None:
+    """The kernels dereference every pointer on the GPU: a tensor elsewhere is
+    an error here, before any launch."""
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+def _out_tensor(out: Optional[torch.Tensor], shape, dtype, device, name: str) -> torch.Tensor:
+    """A new output, or the caller's: on the device, of this dtype and shape,
+    and (being written in place) already in the layout of _aligned."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _on_device(out, name, device)
+    if out.dtype != dtype or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {out.dtype} {tuple(out.shape)}")
+    if not _aligned(out):
+        raise ValueError(f"{name} needs a unit last-dim stride and 16-byte aligned pointer and strides")
+    return out
+
+
+def _lse_tensor(lse: Optional[torch.Tensor], shape, device) -> torch.Tensor:
+    """A new LSE output, or the caller's: written as a dense float32 [B, Hq, Lq]
+    array, so it must be one on the device."""
+    if lse is None:
+        return torch.empty(shape, dtype=torch.float32, device=device)
+    _on_device(lse, "lse", device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(shape) or not lse.is_contiguous():
+        raise ValueError(f"lse must be a contiguous float32 {tuple(shape)} tensor")
+    return lse
+
+
+def _workspace(ws: Optional[torch.Tensor], need: int, device, min_bytes: int = 0) -> torch.Tensor:
+    """The caller's workspace if it holds `need` bytes, else a new one.  A
+    given workspace must be a contiguous tensor on the device."""
+    if ws is not None:
+        _on_device(ws, "workspace", device)
+        if not ws.is_contiguous():
+            raise ValueError("workspace must be contiguous")
+        if ws.numel() * ws.element_size() >= need:
+            return ws
+    return torch.empty(max(need, min_bytes), dtype=torch.uint8, device=device)
 
 
 def _fill(a: SdpaArgs, name: str, t: Optional[torch.Tensor]):
@@ -199,6 +246,8 @@ def _common(q, k, v, scale, mask, sinks, Lq_expected=None):
         raise ValueError("q, k and v must share a dtype")
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise ValueError("q, k and v must be GPU tensors (there is no CPU path)")
+    if k.device != q.device or v.device != q.device:
+        raise ValueError(f"q, k and v must be on one device, got {q.device}, {k.device}, {v.device}")
     q, k, v = _prep(q, "q"), _prep(k, "k"), _prep(v, "v")
     B, Hq, Lq, D = q.shape
     if k.shape[:3] != v.shape[:3] or k.shape[0] != B or k.shape[3] != D:
@@ -229,16 +278,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optiona
     lib = library()
     q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
-    o = torch.empty((B, Hq, Lq, v.shape[3]), dtype=q.dtype, device=q.device) if out is None else out
-    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    o = _out_tensor(out, (B, Hq, Lq, v.shape[3]), q.dtype, q.device, "out")
+    lse = _lse_tensor(None, (B, Hq, Lq), q.device) if return_lse else None
     sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
     sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
     a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     need = int(lib.sdpa_prefill_workspace_bytes(ctypes.byref(a))) if split_tail else 0
     if need > 0:
-        if workspace is None or workspace.numel() * workspace.element_size() < need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _workspace(workspace, need, q.device)
         st = lib.sdpa_prefill_ws(ctypes.byref(a), ctypes.c_void_p(workspace.data_ptr()),
                                  workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))
     else:
@@ -299,15 +347,14 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: Optional
     lib = library()
     q, k, v, scale, mask, sinks = _decode_args(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
-    o = torch.empty((B, Hq, Lq, v.shape[3]), dtype=q.dtype, device=q.device) if out is None else out
-    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    o = _out_tensor(out, (B, Hq, Lq, v.shape[3]), q.dtype, q.device, "out")
+    lse = _lse_tensor(None, (B, Hq, Lq), q.device) if return_lse else None
     sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
     sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
     a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
     need = int(lib.sdpa_decode_workspace_bytes(ctypes.byref(a), int(num_splits)))
-    if need > 0 and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if (workspace is not None and need > 0) else None
+    workspace = _workspace(workspace, need, q.device) if need > 0 else None
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if ws_ptr else 0
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib.sdpa_decode(ctypes.byref(a), int(num_splits), ws_ptr, ws_bytes, ctypes.c_void_p(stream))
@@ -332,11 +379,8 @@ def decode_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, scale: 
     lib = library()
     q, k, v, scale, mask, sinks = _decode_args(q, k, v, scale, mask, sinks)
     B, Hq, Lq, D = q.shape
-    o = torch.empty((B, Hq, Lq, v.shape[3]), dtype=q.dtype, device=q.device) if out is None else out
-    if return_lse and lse is None:
-        lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device)
-    if not return_lse:
-        lse = None
+    o = _out_tensor(out, (B, Hq, Lq, v.shape[3]), q.dtype, q.device, "out")
+    lse = _lse_tensor(lse, (B, Hq, Lq), q.device) if return_lse else None
     sq = _lengths(seqlens_q, B, q.device, "seqlens_q")
     sk = _lengths(seqlens_k, B, q.device, "seqlens_k")
     a = _make_args(q, k, v, o, scale, causal, mask, sinks, lse, sq, sk)
@@ -358,6 +402,8 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
     multiples of 8 up to 128."""
     lib = library()
     q, k, v, scale, mask, sinks = _common(q, k, v, scale, mask, sinks)
+    for t, n in ((o, "o"), (dout, "dout"), (lse, "lse")):
+        _on_device(t, n, q.device)
     o, dout = _prep(o, "o"), _prep(dout, "dout")
     B, Hq, Lq, D = q.shape
     oshape = (B, Hq, Lq, v.shape[3])
@@ -381,8 +427,7 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch
             st[i] = t.stride(i)
     g.dsinks = ds.data_ptr() if ds is not None else None
     need = int(lib.sdpa_prefill_backward_workspace_bytes(ctypes.byref(a)))
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device, min_bytes=16)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     st = lib.sdpa_prefill_backward(ctypes.byref(a), ctypes.byref(g), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream))

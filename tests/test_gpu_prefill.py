@@ -367,3 +367,38 @@ def test_d512_eight_wave_workgroups_sampled(dtype, mask):
     out, l, sc = _run(x, dtype, causal=True)
     compare_sampled(out, l, x, sc, dtype, f"d512 w8 {dtype} mask={mask}",
                     [(0, 0), (3, 9), (7, 15)], [0, 1, 127, 128, 500, 1023], causal=True)
+
+
+def test_binding_rejects_bad_buffers():
+    # caller-supplied outputs, LSE and workspaces that the kernels could not
+    # write safely are refused in the binding, before any launch
+    say("binding: bad out / lse / workspace buffers")
+    dev = torch.device("cuda")
+    B, H, L, D = 1, 2, 64, 64
+    q, k, v = (torch.randn(B, H, L, D, device=dev).half() for _ in range(3))
+    bad_outs = [torch.empty(B, H, L, D, dtype=torch.float16),                     # host memory
+                torch.empty(B, H, L, D, dtype=torch.bfloat16, device=dev),        # dtype
+                torch.empty(B, H, L + 1, D, dtype=torch.float16, device=dev),     # shape
+                torch.empty(B, H, L, D + 1, dtype=torch.float16, device=dev)[..., :D]]  # 130-byte rows
+    for o in bad_outs:
+        with pytest.raises(ValueError):
+            sdpa.prefill(q, k, v, out=o)
+        with pytest.raises(ValueError):
+            sdpa.decode(q[:, :, :1], k, v, out=o[:, :, :1] if o.shape[2] == L else o)
+    qd = q[:, :, :1].contiguous()
+    with pytest.raises(ValueError):
+        sdpa.decode(qd, k, v, num_splits=4, workspace=torch.empty(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        sdpa.decode(qd, k, v, num_splits=4,
+                    workspace=torch.empty(2, 1 << 20, dtype=torch.uint8, device=dev)[:, ::2])
+    with pytest.raises(ValueError):
+        sdpa.decode_noalloc(qd, k, v, return_lse=True,
+                            lse=torch.empty(B, 2 * H, 1, device=dev)[:, ::2])
+    with pytest.raises(ValueError):
+        sdpa.prefill(q, k.cpu().cuda(), v.cpu(), causal=True)
+    o, lse = sdpa.prefill(q, k, v, causal=True, return_lse=True)
+    with pytest.raises(ValueError):
+        sdpa.prefill_backward(q, k, v, o, lse.cpu(), torch.randn_like(o), causal=True)
+    with pytest.raises(ValueError):
+        sdpa.prefill_backward(q, k, v, o.cpu(), lse, torch.randn_like(o), causal=True)
+    torch.cuda.synchronize()
