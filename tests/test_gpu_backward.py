@@ -22,25 +22,69 @@ import torch
 import scaled_dot_product_prefill_amd as sdpa
 from oracle import allclose_report, sdpa_backward_reference
 from tests.gpu_util import say, to_dev
+from tests.grad_bound import grad_magnitudes
 from workloads import DTYPES, random_case
 
 pytestmark = pytest.mark.gpu
 
 
-def _report(got, ref, what, dtype="bf16"):
+# unit roundoff of the input type; the elementwise gate's multiple of it
+# (measured worst over these tests: bf16 0.66, fp16 0.72, fp32 19.6); the
+# absolute rounding step of a result stored below fp16's normal range (2^-14
+# and down: step 2^-24, error at most 2^-25)
+UNIT = {"fp32": 2.0 ** -24, "fp16": 2.0 ** -11, "bf16": 2.0 ** -8}
+C_ELEM = {"fp32": 64.0, "fp16": 4.0, "bf16": 2.0}
+OUT_FLOOR = {"fp32": 0.0, "fp16": 2.0 ** -25, "bf16": 0.0}
+
+
+def _report(got, ref, what, dtype="bf16", mag=None):
+    """Three gates: |got - ref| <= atol max(1, max|ref|) + rtol |ref|; the
+    normwise relative error; and, with the magnitude companion `mag` of each
+    element's sum, |got - ref| <= C u mag + u |ref| + (fp16: 2^-25) element
+    by element (a small element of a tensor with a large maximum gets its
+    own scale; the last two terms are the rounding of the stored result)."""
     ref = np.asarray(ref, dtype=np.float64)
     s = max(1.0, float(np.abs(ref).max()) if ref.size else 1.0)
     atol, rtol, nrel = (1e-5, 0.0, 1e-5) if dtype == "fp32" else (2e-3, 1e-2, 1e-2)
-    rep = allclose_report(got.float().cpu().numpy(), ref, atol * s, rtol)
+    g = got.float().cpu().numpy().astype(np.float64)
+    rep = allclose_report(g, ref, atol * s, rtol)
     ok = rep["ok"] and rep["norm_rel"] <= nrel
-    say(f"  {what}: max_abs={rep['max_abs']:.3e} (scale {s:.3g}) norm_rel={rep['norm_rel']:.3e} ok={ok}")
+    elem = ""
+    if mag is not None:
+        mag = np.asarray(mag, dtype=np.float64)
+        assert np.all(np.abs(ref) <= mag * (1 + 1e-9) + 1e-300), f"{what}: companion below its reference"
+        u = UNIT[dtype]
+        excess = np.abs(g - ref) - u * np.abs(ref) - OUT_FLOOR[dtype]
+        zero = mag == 0
+        ratio = float(np.max(excess[~zero] / (u * mag[~zero]))) if np.any(~zero) else 0.0
+        ok_zero = bool(np.all(excess[zero] <= 0)) if np.any(zero) else True
+        ok = ok and ratio <= C_ELEM[dtype] and ok_zero
+        rep["elem_ratio"], rep["elem_zero_ok"] = ratio, ok_zero
+        elem = f" elem_ratio={ratio:.3g} (gate {C_ELEM[dtype]:g}) zero_ok={ok_zero}"
+        if ratio > C_ELEM[dtype] or not ok_zero:
+            rr = np.where(zero, 0.0, excess / np.maximum(u * mag, 1e-300))
+            idx = np.unravel_index(np.argmax(rr), rr.shape)
+            sl = tuple(idx[:3])
+            say(f"    worst {idx}: got={g[idx]:.6e} ref={ref[idx]:.6e} mag={mag[idx]:.3e} "
+                f"row |ref| max={np.abs(ref[sl]).max():.3e} row mag max={mag[sl].max():.3e} "
+                f"over the gate: {int(np.sum(rr > C_ELEM[dtype]))}")
+    say(f"  {what}: max_abs={rep['max_abs']:.3e} (scale {s:.3g}) norm_rel={rep['norm_rel']:.3e}{elem} ok={ok}")
     return None if ok else f"{what}: {rep}"
 
 
-def _check_all(pairs, dtype="bf16"):
-    """Report every gradient, then fail on the first mismatch."""
-    bad = [m for m in (_report(g, r, w, dtype) for g, r, w in pairs) if m]
+def _check_all(pairs, dtype="bf16", mags=None):
+    """Report every gradient, then fail on the first mismatch.  mags: the
+    magnitude companions of the first three pairs (dq, dk, dv)."""
+    bad = [m for m in (_report(g, r, w, dtype, mags[i] if mags is not None and i < 3 else None)
+                       for i, (g, r, w) in enumerate(pairs)) if m]
     assert not bad, bad
+
+
+def _reference(q, k, v, dout, **kw):
+    """The oracle's gradients and their magnitude companions (with fp16's
+    absolute rounding floor below its normal range)."""
+    floor = 2.0 ** -14 if q.dtype == torch.float16 else 0.0
+    return sdpa_backward_reference(q, k, v, dout, **kw), grad_magnitudes(q, k, v, dout, floor=floor, **kw)
 
 
 def _dout(seed, shape, dtype):
@@ -82,14 +126,14 @@ def test_backward_grid(dtype, D, case):
                     sink_scale=2.0, mask_neg_inf_frac=0.1)
     dout = _dout(5000 + case, x["q"].shape, dtype)
     (dq, dk, dv, ds), sc = _run(x, dout, dtype, causal, want_dsinks=True)
-    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=causal,
+    (rq, rk, rv, rs), mags = _reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=causal,
                                              mask=x["mask"], sinks=x["sinks"])
     pairs = [(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")]
     if sinks:
         pairs.append((ds, rs, "dsinks"))
     else:
         assert ds is None
-    _check_all(pairs, dtype)
+    _check_all(pairs, dtype, mags)
 
 
 # (D, Dv): head dims that are multiples of 8 up to 128, run at kernel dim 64
@@ -108,12 +152,12 @@ def test_backward_head_dims(dtype, dims, causal):
     dout = _dout(5300 + D, (B, Hq, Lq, Dv), dtype)
     (dq, dk, dv, ds), sc = _run(x, dout, dtype, causal, want_dsinks=True)
     assert dq.shape == x["q"].shape and dk.shape == x["k"].shape and dv.shape == x["v"].shape
-    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=causal,
+    (rq, rk, rv, rs), mags = _reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=causal,
                                              sinks=x["sinks"])
     pairs = [(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")]
     if causal:
         pairs.append((ds, rs, "dsinks"))
-    _check_all(pairs, dtype)
+    _check_all(pairs, dtype, mags)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
@@ -131,9 +175,9 @@ def test_backward_seqlens(dtype):
         y["k"][b, :, sk[b]:] = float("nan")
         y["v"][b, :, sk[b]:] = float("nan")
     (dq, dk, dv, ds), sc = _run(y, dpad, dtype, True, sq, sk, want_dsinks=True)
-    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+    (rq, rk, rv, rs), mags = _reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
                                              sinks=x["sinks"], seqlens_q=np.array(sq), seqlens_k=np.array(sk))
-    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype, mags)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -147,9 +191,9 @@ def test_backward_seqlens_keys_end_early(dtype):
     x = random_case(5150, B, Hq, Hkv, Lq, Lk, D, dtype, sinks=True, sink_scale=2.0)
     dout = _dout(5150, x["q"].shape, dtype)
     (dq, dk, dv, ds), sc = _run(x, dout, dtype, True, sq, sk, want_dsinks=True)
-    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+    (rq, rk, rv, rs), mags = _reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
                                              sinks=x["sinks"], seqlens_q=np.array(sq), seqlens_k=np.array(sk))
-    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype, mags)
 
 
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
@@ -164,9 +208,9 @@ def test_backward_gqa_head_groups(dtype, G):
     x = random_case(5250 + G, B, Hq, Hkv, L, L, D, dtype, sinks=True, sink_scale=2.0)
     dout = _dout(5250 + G, x["q"].shape, dtype)
     (dq, dk, dv, ds), sc = _run(x, dout, dtype, True, None, None, want_dsinks=True)
-    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+    (rq, rk, rv, rs), mags = _reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
                                              sinks=x["sinks"])
-    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype, mags)
 
 
 def test_autograd_wrapper_matches_entry_point():
@@ -208,10 +252,10 @@ def test_causal_full_size_sampled_heads():
     torch.cuda.synchronize()
     for h in (0, 31):
         sl = slice(h, h + 1)
-        rq, rk, rv, _ = sdpa_backward_reference(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], x["dout"][:, sl],
+        (rq, rk, rv, _), mags = _reference(x["q"][:, sl], x["k"][:, sl], x["v"][:, sl], x["dout"][:, sl],
                                                 scale=w.scale, causal=True)
         _check_all([(dq[:, sl], rq, f"dq head {h}"), (dk[:, sl], rk, f"dk head {h}"),
-                    (dv[:, sl], rv, f"dv head {h}")])
+                    (dv[:, sl], rv, f"dv head {h}")], "bf16", mags)
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "fp16", "bf16"])
@@ -223,6 +267,6 @@ def test_backward_bool_mask(dtype):
     x["mask"] = torch.from_numpy(keep)
     dout = _dout(5400, x["q"].shape, dtype)
     (dq, dk, dv, ds), sc = _run(x, dout, dtype, True, want_dsinks=True)
-    rq, rk, rv, rs = sdpa_backward_reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
+    (rq, rk, rv, rs), mags = _reference(x["q"], x["k"], x["v"], dout, scale=sc, causal=True,
                                              mask=x["mask"], sinks=x["sinks"])
-    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype)
+    _check_all([(dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv"), (ds, rs, "dsinks")], dtype, mags)
