@@ -1,10 +1,12 @@
-"""The parity gates can fail: on the long-context decode shape (B=8, Hq=32,
+"""The parity gates can fail.  On the long-context decode shape (B=8, Hq=32,
 Hkv=8, D=128, Lk=131072, trailing tenth of the keys masked, bf16), an output
 that lost one 2048-key split of the 64 the decode kernel uses, or six, is
 rejected, although the elementwise allclose bound alone accepts it (|O| is
 about sqrt(e / Lk) = 0.0046 there, half of it below atol).  The "wrong"
 outputs come from the oracle itself with those keys hidden, i.e. what a merge
-that skipped a split would produce.  CPU only."""
+that skipped a split would produce.  And the magnitude-companion gate rejects
+a head of small values that lost keys, which the other two gates accept.
+CPU only."""
 import functools
 
 import numpy as np
@@ -69,3 +71,27 @@ def test_six_dropped_splits_fail_the_lse_gate():
     assert allclose_report(Lb, L, atol, rtol)["ok"]             # LSE within rtol * |LSE| alone
     ok, rep = gate(Lb, L, "bf16", lse=True)
     assert not ok and not rep["lse_ok"], rep
+
+
+
+def test_companion_gate_scales_small_heads():
+    """The magnitude-companion gate (|gpu - ref| <= C u A + u |ref|, A_i =
+    sum_j P_ij |V_j|) gives each element its own scale: in a tensor whose
+    second head has values 1000 times smaller, that head losing four of its
+    64 keys passes the allclose bound and the normwise bound, and fails it."""
+    g = torch.Generator().manual_seed(71)
+    q, k, v = (torch.randn(1, 2, 64, 32, generator=g).to(torch.bfloat16) for _ in range(3))
+    v[:, 1] = (v[:, 1].float() * 1e-3).to(torch.bfloat16)
+    sc = 32 ** -0.5
+    O, _ = sdpa_reference(q, k, v, scale=sc)
+    A, _ = sdpa_reference(q, k, v.abs(), scale=sc)
+    assert np.all(np.abs(O) <= A * (1 + 1e-12))
+    ok, rep = gate(_bf16(O), O, "bf16", mag=A)
+    assert ok and rep["mag_ok"], rep
+    m = torch.zeros(1, 2, 64, 64)
+    m[0, 1, :, 10:14] = -np.inf
+    Ob, _ = sdpa_reference(q, k, v, scale=sc, mask=m)
+    ok, rep = gate(_bf16(Ob), O, "bf16")
+    assert ok, rep                                     # allclose and normwise accept it
+    ok, rep = gate(_bf16(Ob), O, "bf16", mag=A)
+    assert not ok and not rep["mag_ok"] and rep["elem_ratio"] > 5, rep
