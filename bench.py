@@ -406,7 +406,8 @@ def config_cells(torch, sdpa, workloads, dev, preroll_s: float):
              "drift": drift(ms), "preroll": pre, "samples_us": [round(t * 1e3, 2) for t in ms],
              "value": round(tf, 3), "unit": "TFLOP/s",
              "roofline": {"bound": "mfma", "peak": PEAK_TFLOPS[w.dtype], "unit": "TFLOP/s",
-                          "frac": round(tf / PEAK_TFLOPS[w.dtype], 4), "flops_per_launch": fl}}
+                          "frac": round(tf / PEAK_TFLOPS[w.dtype], 4), "flops_per_launch": fl,
+                          "traffic": load_traffic("prefill_" + w.name)}}
         if chain:
             ch = time_chain(torch, lambda y: sdpa.prefill(y, x["k"], x["v"], scale=w.scale), x["q"],
                             spin_cycles=spin)
@@ -446,7 +447,8 @@ def config_cells(torch, sdpa, workloads, dev, preroll_s: float):
         "drift": drift(ms), "preroll": pre, "samples_us": [round(t * 1e3, 2) for t in ms],
         "value": round(gbs, 1), "unit": "GB/s",
         "roofline": {"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                     "bytes_per_launch": nb, "kernel": "decode_kernel + merge_kernel"}}
+                     "bytes_per_launch": nb, "kernel": "decode_kernel + merge_kernel",
+                     "traffic": load_traffic("decode_" + w.name)}}
     del x, sets, ws, out
     torch.cuda.empty_cache()
     return cells
